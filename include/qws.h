@@ -1,0 +1,203 @@
+/*
+ * qws.h -- C ABI of libqws: the batch-size-1 decode step of a sparse MoE model on one MI355X
+ * (gfx950). Two weight streams dominate that step: the routed experts and the vocabulary LM head
+ * (runbyai.xyz/posts/593 paragraph 2; Netics Labs, "Three MoE Inference Optimizations NVIDIA
+ * Measured on DGX Spark", section "Decoding was memory-bound on a 124-billion-parameter model at
+ * batch size 1"). This library streams both.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Buffers are DEVICE pointers the caller owns (allocated by the caller, for example as torch
+ *    tensors). Descriptors are non-owning views; they must stay valid until the enqueued work ends.
+ *  - Every call checks its arguments on the host first. On any error it returns a negative status
+ *    and enqueues nothing. On success it enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    default stream) and returns QWS_OK without synchronising, except qws_selfcheck.
+ *  - Weight and activation base pointers must be 16-byte aligned (QWS_ERR_ALIGN otherwise).
+ *  - bf16 is passed as 16-bit patterns; float32 logits and outputs are IEEE binary32.
+ *  - Calls are re-entrant and thread-safe; calls that share a workspace must not overlap in time.
+ *  - No call allocates or frees memory.
+ */
+#ifndef QWS_H
+#define QWS_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QWS_ABI_VERSION 1
+
+typedef void* qws_stream_t; /* hipStream_t */
+
+enum qws_status {
+  QWS_OK = 0,
+  QWS_ERR_ARG = -1,       /* NULL pointer where one is required, bad enum value, both outputs NULL */
+  QWS_ERR_SHAPE = -2,     /* a size outside the supported range (see each call) */
+  QWS_ERR_ALIGN = -3,     /* a base pointer that is not 16-byte aligned */
+  QWS_ERR_FORMAT = -4,    /* a descriptor whose format tag does not match the entry point */
+  QWS_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  QWS_ERR_DEVICE = -6,    /* the HIP runtime refused a launch; qws_strerror appends its message */
+  QWS_ERR_SELFCHECK = -7  /* the device decoded a format differently from the host tables */
+};
+
+/* Format tags carried by descriptors. A descriptor tagged with one format is refused by an entry
+ * point that expects another, so quantised bytes are never read as a different type: the pages
+ * report that exact silent failure, FP8 head weights read as BF16 by a draft model, and advise
+ * asserting the configuration at startup (posts/593 paragraph 9; Netics, section "One missing
+ * interface makes the stack slower than baseline"). */
+enum qws_format {
+  QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634, /* e2m1 nibbles + one E8M0 scale per 32 elements */
+  QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes + one fp32 scale per row */
+  QWS_FMT_BF16 = 0x42463136                 /* plain bf16 */
+};
+
+/* Text for a status code. For QWS_ERR_DEVICE the text of the calling thread's last HIP error is
+ * appended. The returned pointer stays valid until the next call on the same thread. */
+const char* qws_strerror(int status);
+
+/* QWS_ABI_VERSION of the loaded library. */
+int qws_abi_version(void);
+
+/* Startup validation (Netics, "One missing interface ...": validate at startup that each
+ * optimisation is active rather than infer it from throughput). Decodes every e2m1 code under
+ * several E8M0 scales through both device dequantisation routines, every E4M3 code, and encodes a
+ * fixed set of float32 values to E4M3 on the device, then compares with tables built on the host.
+ * Synchronises `stream`. Returns QWS_OK or QWS_ERR_SELFCHECK (or QWS_ERR_DEVICE). */
+int qws_selfcheck(qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * MoE router: logits, top-k, renormalised softmax gate weights.
+ *   logits[m, e] = sum_k x[m, k] * w_router[e, k] + bias[m, e]
+ *   topk_idx[m, :] = the K largest logits, ordered by (logit descending, expert index
+ *                    ascending): ties go to the lower index; -0.0 equals +0.0; NaN ranks lowest.
+ *   topk_w[m, i]   = exp(l_i - l_max) / sum_j exp(l_j - l_max) over the K selected logits.
+ * Each MoE layer routes a token to eight of 512 routed experts plus one shared expert
+ * (posts/593 paragraph 2); the score function is not stated on the pages, softmax over the
+ * selected logits is this library's reading.
+ *
+ *   x_bf16          [M, H] bf16, rows contiguous.            1 <= M <= 4, H % 8 == 0, 8 <= H <= 2560
+ *   w_router_bf16   [E, H] bf16, row-major.                  1 <= E <= 1024
+ *   bias            NULL, [E] (bias_row_stride 0) or [M, E] (bias_row_stride E), fp32.
+ *   K               1 <= K <= min(8, E).
+ *   topk_idx        [M, K] int32 out.  topk_w [M, K] fp32 out.
+ *   logits_out      NULL or [M, E] fp32 out (the logits including bias).
+ *   workspace       device memory of moe_route_workspace_bytes(M, E) bytes, ZERO-FILLED before
+ *                   its first use; every call leaves it zero-filled again.
+ * -------------------------------------------------------------------------------------------*/
+size_t moe_route_workspace_bytes(int M, int E);
+int moe_route_topk(const void* x_bf16, int M, int H, const void* w_router_bf16, int E,
+                   const float* bias, long long bias_row_stride, int K, int* topk_idx,
+                   float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes,
+                   qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * MXFP4 expert bank (non-owning view). Expert e < n_routed is a routed expert; if has_shared,
+ * the shared expert is stored at index n_routed. Per expert, canonical row-major layout:
+ *   gate_up_q [2I, H/2] bytes: byte j of a row holds element 2j in bits 3:0, 2j+1 in bits 7:4
+ *   gate_up_s [2I, H/32] E8M0 bytes: scale of elements 32b .. 32b+31 of the row is 2^(s-127)
+ *   down_q    [H, I/2],  down_s [H, I/32], same encoding.
+ * gate_up rows [0, I) are the gate projection, rows [I, 2I) the up projection. Consecutive
+ * experts are contiguous (expert e starts at e * rows * row_bytes). Scale bytes must be in 1..254.
+ * MXFP4 is the experts' format on the pages (posts/593 paragraph 4; Netics, "Humming MXFP4
+ * kernels compile at run time ..."); element and scale encodings are OCP MX v1.0.
+ * -------------------------------------------------------------------------------------------*/
+typedef struct {
+  unsigned format; /* must be QWS_FMT_MXFP4_E2M1_E8M0_B32 */
+  int n_routed;    /* 1 .. 1024 */
+  int has_shared;  /* 0 or 1 */
+  int hidden;      /* H: multiple of 32, 32 .. 2560 */
+  int inter;       /* I: multiple of 32, 32 .. 1024 */
+  const unsigned char* gate_up_q;
+  const unsigned char* gate_up_s;
+  const unsigned char* down_q;
+  const unsigned char* down_s;
+} qws_mxfp4_experts;
+
+/* ------------------------------------------------------------------------------------------
+ * Routed-expert FFN with the expert union of a verification window (posts/593 paragraph 5:
+ * verifying four positions can touch up to 32 experts; each expert is read once for all of
+ * them):
+ *   y[m] = shared(x[m]) + sum_i topk_w[m, i] * expert_{topk_idx[m, i]}(x[m])
+ *   expert(x) = W_down . (silu(W_gate . x) * (W_up . x)),  silu(g) = g / (1 + e^-g)
+ * float32 accumulation throughout; the SwiGLU activation stays float32.
+ *
+ *   x_bf16       [M, H] bf16.  1 <= M <= 4.
+ *   topk_idx     [M, K] int32, topk_w [M, K] fp32 (device-resident, e.g. from moe_route_topk).
+ *                1 <= K <= 8. A token holding an id outside [0, n_routed) gets a NaN row.
+ *                A token listing an expert twice adds both weights.
+ *   y_bf16       NULL or [M, H] bf16 out: round-to-nearest-even of y_f32.
+ *   y_f32        NULL or [M, H] fp32 out. At least one of y_bf16, y_f32 must be given.
+ *   workspace    moe_expert_workspace_bytes(M, K, H, I) bytes, ZERO-FILLED before first use;
+ *                every call leaves its counters zero again.
+ * -------------------------------------------------------------------------------------------*/
+size_t moe_expert_workspace_bytes(int M, int K, int hidden, int inter);
+int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
+                          const int* topk_idx, const float* topk_w, int K, void* y_bf16,
+                          float* y_f32, void* workspace, size_t workspace_bytes,
+                          qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Vocabulary LM head (non-owning view). The head projects H = 2,560 onto 157,184 tokens and
+ * every generated token reads all of it: ~805 MB per token in bf16, half in FP8 (posts/593
+ * paragraph 3).
+ *   format QWS_FMT_BF16:                w = bf16 [rows, cols], row_scale NULL.
+ *   format QWS_FMT_FP8_E4M3FN_ROWSCALE: w = E4M3 codes u8 [rows, cols], row_scale fp32 [rows];
+ *                                       weight[r, k] = e4m3(w[r, k]) * row_scale[r].
+ * rows >= 1; cols multiple of 32, 32 .. 2560.
+ * -------------------------------------------------------------------------------------------*/
+typedef struct {
+  unsigned format;
+  long long rows;
+  long long cols;
+  const void* w;
+  const float* row_scale;
+} qws_lmhead;
+
+/* Fill a bf16 head descriptor (no device work). */
+int lmhead_bf16_desc(const void* w_bf16, long long rows, long long cols, qws_lmhead* desc_out);
+
+/* Online FP8 quantisation of a bf16 head, done once when the head is constructed (Netics,
+ * "Online FP8 quantization halves the LM head weight reads"):
+ *   s_r = fl32(max_k |W[r, k]| / 448)  (s_r = 1 for an all-zero row)
+ *   q[r, k] = E4M3(fl32(W[r, k] / s_r)), round to nearest even, saturating at +-448
+ * Both divisions are IEEE float32 round-to-nearest-even.
+ *   w_bf16 [rows, cols] in; codes_out u8 [rows, cols] and row_scale_out fp32 [rows] out.
+ *   desc_out (host memory) is filled with an FP8-tagged descriptor of the outputs.         */
+int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long cols,
+                        unsigned char* codes_out, float* row_scale_out, qws_lmhead* desc_out,
+                        qws_stream_t stream);
+
+/* logits[m, r] = row_scale[r] * sum_k e4m3(q[r, k]) * x[m, k]   (head must be FP8-tagged)
+ *   x_bf16 [M, cols], 1 <= M <= 4; logits_out fp32 [M, rows].                              */
+int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
+                    qws_stream_t stream);
+
+/* logits[m, r] = sum_k W[r, k] * x[m, k]   (head must be BF16-tagged; an FP8 head is refused
+ * with QWS_ERR_FORMAT instead of being read as bf16). Same shapes as lmhead_gemv_fp8.       */
+int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
+                     qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Diagnostics (not on the hot path)
+ * -------------------------------------------------------------------------------------------*/
+/* Dequantise an MXFP4 matrix [rows, cols] (canonical layout above) into fp32 out [rows, cols]
+ * with the device routine of the down projection (path 0: e2m1 -> fp32 with the block scale)
+ * or of the gate/up projection (path 1: e2m1 -> bf16 with the block scale, widened to fp32).
+ * cols multiple of 32, 32 .. 65536. Exact for scale bytes 2 .. 252.                        */
+int qws_debug_dequant_mxfp4(const unsigned char* q, const unsigned char* s, long long rows,
+                            int cols, int path, float* out, qws_stream_t stream);
+
+/* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for an FP8-tagged head, fp32 [rows, cols].  */
+int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t stream);
+
+/* Streaming-read probe: reads `bytes` (multiple of 16, 16-byte aligned) with 128-bit loads and
+ * writes one checksum word per workgroup into sink[0 .. blocks) (blocks <= 65536). Measures the
+ * device's practical read bandwidth.                                                        */
+int qws_probe_read(const void* buf, size_t bytes, unsigned* sink, int blocks, qws_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWS_H */

@@ -1,0 +1,225 @@
+"""Batch-size-1 MoE decode-step weight streaming on MI355X (gfx950).
+
+Python binding of libqws (include/qws.h): the same entry points, taking torch device tensors and
+the current HIP stream. Argument marshalling only -- every step runs in the library's HIP kernels;
+if libqws.so is missing, the first call raises (there is no CPU fallback).
+
+    route  = moe_route_topk(x, w_router, K)               # router GEMV + top-K + softmax
+    y      = moe_expert_gemv_mxfp4(bank, x, idx, w)       # union of experts, SwiGLU, combine
+    head   = lmhead_quantize_fp8(w_head_bf16)             # online FP8 head, once
+    logits = lmhead_gemv_fp8(head, x)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32, LMHeadDesc,  # noqa: F401
+                   MxFp4Experts, QwsError, check)
+
+__all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "LMHead", "lmhead_bf16",
+           "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "debug_dequant_mxfp4", "debug_dequant_fp8",
+           "probe_read", "route_workspace", "expert_workspace", "QwsError", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def selfcheck(device=None) -> None:
+    """Device format self-check against host tables; raises QwsError on any mismatch."""
+    check("qws_selfcheck", lib().qws_selfcheck(_stream(device)))
+
+
+# ----------------------------------------------------------------------------------- router
+def route_workspace(M: int, E: int, device) -> torch.Tensor:
+    n = lib().moe_route_workspace_bytes(M, E)
+    if n == 0:
+        raise ValueError(f"unsupported router shape M={M} E={E}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_route_topk(x: torch.Tensor, w_router: torch.Tensor, K: int, bias: torch.Tensor | None = None,
+                   topk_idx=None, topk_w=None, logits_out=None, workspace=None):
+    """(topk_idx int32 [M, K], topk_w fp32 [M, K]); logits_out (fp32 [M, E]) is filled if given."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.bfloat16, 2)
+    M, H = x.shape
+    E = w_router.shape[0]
+    stride = 0
+    if bias is not None:
+        _need(bias, "bias", torch.float32)
+        stride = 0 if bias.dim() == 1 else bias.shape[-1]
+    if topk_idx is None:
+        topk_idx = torch.empty((M, K), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = route_workspace(M, E, x.device)
+    st = lib().moe_route_topk(_p(x), M, H, _p(w_router), E, _p(bias), stride, K, _p(topk_idx), _p(topk_w),
+                              _p(logits_out), _p(workspace), workspace.numel(), _stream(x.device))
+    check("moe_route_topk", st)
+    return topk_idx, topk_w
+
+
+# ----------------------------------------------------------------------------------- experts
+@dataclass
+class ExpertBank:
+    """MXFP4 experts in the canonical layout (uint8 tensors [n_experts, rows, bytes]); the shared
+    expert, if any, is the last one."""
+    gate_up_q: torch.Tensor
+    gate_up_s: torch.Tensor
+    down_q: torch.Tensor
+    down_s: torch.Tensor
+    n_routed: int
+    has_shared: bool = True
+
+    def __post_init__(self):
+        n = self.n_routed + int(self.has_shared)
+        two_i, hb = self.gate_up_q.shape[1:]
+        for name, t, shape in (("gate_up_q", self.gate_up_q, (n, two_i, hb)),
+                               ("gate_up_s", self.gate_up_s, (n, two_i, hb * 2 // 32)),
+                               ("down_q", self.down_q, (n, hb * 2, two_i // 4)),
+                               ("down_s", self.down_s, (n, hb * 2, two_i // 2 // 32))):
+            _need(t, name, torch.uint8, 3)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        self.hidden = hb * 2
+        self.inter = two_i // 2
+        self.desc = MxFp4Experts(QWS_FMT_MXFP4_E2M1_E8M0_B32, self.n_routed, int(self.has_shared), self.hidden,
+                                 self.inter, self.gate_up_q.data_ptr(), self.gate_up_s.data_ptr(),
+                                 self.down_q.data_ptr(), self.down_s.data_ptr())
+
+    @classmethod
+    def from_dict(cls, d: dict, n_routed: int, has_shared: bool = True):
+        return cls(d["gate_up_q"], d["gate_up_s"], d["down_q"], d["down_s"], n_routed, has_shared)
+
+
+def expert_workspace(M: int, K: int, hidden: int, inter: int, device) -> torch.Tensor:
+    n = lib().moe_expert_workspace_bytes(M, K, hidden, inter)
+    if n == 0:
+        raise ValueError("unsupported expert shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_expert_gemv_mxfp4(bank: ExpertBank, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                          y_bf16=None, y_f32=None, workspace=None, want_bf16=True, want_f32=True):
+    """(y_bf16, y_f32) for the window x [M, H]; either output may be skipped."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    M, H = x.shape
+    K = topk_idx.shape[1]
+    if H != bank.hidden or tuple(topk_w.shape) != (M, K) or topk_idx.shape[0] != M:
+        raise ValueError("x / routing shapes do not match the bank")
+    if y_bf16 is None and want_bf16:
+        y_bf16 = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if y_f32 is None and want_f32:
+        y_f32 = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = expert_workspace(M, K, bank.hidden, bank.inter, x.device)
+    st = lib().moe_expert_gemv_mxfp4(C.byref(bank.desc), _p(x), M, _p(topk_idx), _p(topk_w), K, _p(y_bf16),
+                                     _p(y_f32), _p(workspace), workspace.numel(), _stream(x.device))
+    check("moe_expert_gemv_mxfp4", st)
+    return y_bf16, y_f32
+
+
+# ----------------------------------------------------------------------------------- LM head
+@dataclass
+class LMHead:
+    """A vocabulary head and its descriptor: bf16 weights, or E4M3 codes with fp32 row scales."""
+    w: torch.Tensor
+    row_scale: torch.Tensor | None
+    desc: LMHeadDesc
+
+    @property
+    def format(self) -> int:
+        return self.desc.format
+
+    @property
+    def rows(self) -> int:
+        return self.desc.rows
+
+
+def lmhead_bf16(w: torch.Tensor) -> LMHead:
+    _need(w, "w", torch.bfloat16, 2)
+    d = LMHeadDesc()
+    check("lmhead_bf16_desc", lib().lmhead_bf16_desc(_p(w), w.shape[0], w.shape[1], C.byref(d)))
+    return LMHead(w, None, d)
+
+
+def lmhead_quantize_fp8(w: torch.Tensor, codes=None, row_scale=None) -> LMHead:
+    """Online per-row FP8 quantisation of a bf16 head (done once, at construction)."""
+    _need(w, "w", torch.bfloat16, 2)
+    rows, cols = w.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    if row_scale is None:
+        row_scale = torch.empty(rows, dtype=torch.float32, device=w.device)
+    d = LMHeadDesc()
+    st = lib().lmhead_quantize_fp8(_p(w), rows, cols, _p(codes), _p(row_scale), C.byref(d), _stream(w.device))
+    check("lmhead_quantize_fp8", st)
+    return LMHead(codes, row_scale, d)
+
+
+def _gemv(fn: str, head: LMHead, x: torch.Tensor, out):
+    _need(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, head.rows), dtype=torch.float32, device=x.device)
+    st = getattr(lib(), fn)(C.byref(head.desc), _p(x), M, _p(out), _stream(x.device))
+    check(fn, st)
+    return out
+
+
+def lmhead_gemv_fp8(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
+    return _gemv("lmhead_gemv_fp8", head, x, out)
+
+
+def lmhead_gemv_bf16(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
+    return _gemv("lmhead_gemv_bf16", head, x, out)
+
+
+# ----------------------------------------------------------------------------------- diagnostics
+def debug_dequant_mxfp4(q: torch.Tensor, s: torch.Tensor, path: int = 0) -> torch.Tensor:
+    _need(q, "q", torch.uint8, 2)
+    _need(s, "s", torch.uint8, 2)
+    rows, cols = q.shape[0], q.shape[1] * 2
+    out = torch.empty((rows, cols), dtype=torch.float32, device=q.device)
+    check("qws_debug_dequant_mxfp4", lib().qws_debug_dequant_mxfp4(_p(q), _p(s), rows, cols, path, _p(out),
+                                                                    _stream(q.device)))
+    return out
+
+
+def debug_dequant_fp8(head: LMHead) -> torch.Tensor:
+    out = torch.empty((head.desc.rows, head.desc.cols), dtype=torch.float32, device=head.w.device)
+    check("qws_debug_dequant_fp8", lib().qws_debug_dequant_fp8(C.byref(head.desc), _p(out), _stream(head.w.device)))
+    return out
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    check("qws_probe_read", lib().qws_probe_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), blocks,
+                                                 _stream(buf.device)))

@@ -1,0 +1,86 @@
+"""ctypes view of libqws.so (the C ABI declared in include/qws.h). Loading fails loudly."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqws.so")
+
+QWS_OK = 0
+QWS_ERR_ARG = -1
+QWS_ERR_SHAPE = -2
+QWS_ERR_ALIGN = -3
+QWS_ERR_FORMAT = -4
+QWS_ERR_WORKSPACE = -5
+QWS_ERR_DEVICE = -6
+QWS_ERR_SELFCHECK = -7
+
+QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634
+QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845
+QWS_FMT_BF16 = 0x42463136
+
+
+class MxFp4Experts(C.Structure):
+    _fields_ = [("format", C.c_uint), ("n_routed", C.c_int), ("has_shared", C.c_int), ("hidden", C.c_int),
+                ("inter", C.c_int), ("gate_up_q", C.c_void_p), ("gate_up_s", C.c_void_p), ("down_q", C.c_void_p),
+                ("down_s", C.c_void_p)]
+
+
+class LMHeadDesc(C.Structure):
+    _fields_ = [("format", C.c_uint), ("rows", C.c_longlong), ("cols", C.c_longlong), ("w", C.c_void_p),
+                ("row_scale", C.c_void_p)]
+
+
+_P = C.c_void_p
+_I = C.c_int
+_LL = C.c_longlong
+_SZ = C.c_size_t
+
+# name -> (restype, argtypes); every entry point of include/qws.h
+SIGNATURES = {
+    "qws_strerror": (C.c_char_p, [_I]),
+    "qws_abi_version": (_I, []),
+    "qws_selfcheck": (_I, [_P]),
+    "moe_route_workspace_bytes": (_SZ, [_I, _I]),
+    "moe_route_topk": (_I, [_P, _I, _I, _P, _I, _P, _LL, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_expert_gemv_mxfp4": (_I, [C.POINTER(MxFp4Experts), _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "lmhead_bf16_desc": (_I, [_P, _LL, _LL, C.POINTER(LMHeadDesc)]),
+    "lmhead_quantize_fp8": (_I, [_P, _LL, _LL, _P, _P, C.POINTER(LMHeadDesc), _P]),
+    "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
+    "lmhead_gemv_bf16": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
+    "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),
+    "qws_debug_dequant_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _P]),
+    "qws_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load libqws.so once. Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"libqws.so not built at {path}; run quantized_weight_streaming_amd/build.py "
+                               "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
+        lib = C.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class QwsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load().qws_strerror(status).decode(errors="replace")
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != QWS_OK:
+        raise QwsError(fn, status)

@@ -1,0 +1,116 @@
+// Shared device helpers and host-side plumbing of libqws (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qws.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace qws {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------------------ loads
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// ------------------------------------------------------------------------------ formats
+// E8M0 byte -> the float32 scale 2^(s-127). Bytes 1..254 are normal float32 exponents; byte 0 is
+// 2^-127 (a float32 subnormal); byte 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : (s << 23));
+  return __uint_as_float(bits);
+}
+
+// Two e2m1 nibbles of byte `B` of `w`, times `scale`, as bf16x2 / float2 (element order: low
+// nibble first). gfx950 converts in one VALU op.
+template <int B>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, B);
+}
+template <int B>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, B);
+}
+// Two E4M3 codes of 16-bit half `H` of `w` as bf16x2 (exact: E4M3 values are bf16 values).
+template <bool H>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, H);
+}
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+// Two floats -> two E4M3 codes, round to nearest even and saturating at +-448, written into 16-bit
+// half H of `old` (element a in the lower byte). Clamping first makes the result independent of
+// how the conversion treats overflow; RNE(clamp(v)) equals saturating RNE because 448 is a code.
+template <bool H>
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b, uint32_t old) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, H);
+}
+
+// acc + a.x*b.x + a.y*b.y with bf16 inputs (products exact in fp32).
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------------------------ reductions
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane gets its group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ------------------------------------------------------------------------------ sync
+// Arrive on a counter shared by `expected` workgroups; returns true in the last one to arrive
+// (in every thread of it) after making the others' global writes visible to it. The last one
+// resets the counter to zero. All threads of the workgroup must call it.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, bool* lds_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned prev = atomicAdd(counter, 1u);
+    bool last = prev + 1 == expected;
+    if (last) *counter = 0u;
+    *lds_flag = last;
+  }
+  __syncthreads();
+  bool last = *lds_flag;
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace qws
+
+// ------------------------------------------------------------------------------ host side
+namespace qws_host {
+
+int set_device_error(hipError_t e);  // records the message, returns QWS_ERR_DEVICE
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QWS_OK : set_device_error(e);
+}
+
+}  // namespace qws_host

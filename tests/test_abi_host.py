@@ -1,0 +1,160 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point include/qws.h declares,
+and its host-side validation returns the documented status before anything is enqueued. All
+pointers here are fake; every call below is refused by validation, so none reaches HIP."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from quantized_weight_streaming_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qws.h")
+
+A = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqws.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert lib.qws_abi_version() == 1
+    for st in range(0, -8, -1):
+        assert lib.qws_strerror(st)
+    assert b"format" in lib.qws_strerror(_lib.QWS_ERR_FORMAT)
+
+
+def test_workspace_sizes(lib):
+    assert lib.moe_route_workspace_bytes(1, 512) >= 512 * 4
+    assert lib.moe_route_workspace_bytes(0, 512) == 0
+    assert lib.moe_route_workspace_bytes(5, 512) == 0
+    assert lib.moe_route_workspace_bytes(1, 1025) == 0
+    w1 = lib.moe_expert_workspace_bytes(1, 8, 2560, 768)
+    w4 = lib.moe_expert_workspace_bytes(4, 8, 2560, 768)
+    assert 0 < w1 < w4
+    assert w4 >= 33 * 4 * (2560 + 768) * 4
+    assert lib.moe_expert_workspace_bytes(1, 9, 2560, 768) == 0
+    assert lib.moe_expert_workspace_bytes(1, 8, 4096, 768) == 0
+
+
+def _route(lib, **kw):
+    a = dict(x=A, M=1, H=2560, w=A, E=512, bias=None, stride=0, K=8, idx=A, tw=A, logits=None, ws=A,
+             wsb=lib.moe_route_workspace_bytes(1, 512), stream=None)
+    a.update(kw)
+    return lib.moe_route_topk(a["x"], a["M"], a["H"], a["w"], a["E"], a["bias"], a["stride"], a["K"], a["idx"],
+                              a["tw"], a["logits"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.QWS_ERR_ARG), (dict(idx=None), _lib.QWS_ERR_ARG),
+    (dict(M=0), _lib.QWS_ERR_SHAPE), (dict(M=5), _lib.QWS_ERR_SHAPE), (dict(H=2568), _lib.QWS_ERR_SHAPE),
+    (dict(H=100), _lib.QWS_ERR_SHAPE), (dict(E=0), _lib.QWS_ERR_SHAPE), (dict(E=1025), _lib.QWS_ERR_SHAPE),
+    (dict(K=0), _lib.QWS_ERR_SHAPE), (dict(K=9), _lib.QWS_ERR_SHAPE), (dict(E=4, K=5), _lib.QWS_ERR_SHAPE),
+    (dict(bias=A, stride=7), _lib.QWS_ERR_SHAPE), (dict(x=MIS), _lib.QWS_ERR_ALIGN),
+    (dict(w=MIS), _lib.QWS_ERR_ALIGN), (dict(ws=None), _lib.QWS_ERR_WORKSPACE), (dict(wsb=16), _lib.QWS_ERR_WORKSPACE),
+])
+def test_route_validation(lib, kw, status):
+    assert _route(lib, **kw) == status
+
+
+def _bank(**kw):
+    d = dict(format=_lib.QWS_FMT_MXFP4_E2M1_E8M0_B32, n_routed=512, has_shared=1, hidden=2560, inter=768,
+             gate_up_q=A, gate_up_s=A, down_q=A, down_s=A)
+    d.update(kw)
+    return _lib.MxFp4Experts(**d)
+
+
+def _experts(lib, bank=None, **kw):
+    a = dict(x=A, M=1, idx=A, tw=A, K=8, y16=A, y32=A, ws=A, wsb=lib.moe_expert_workspace_bytes(1, 8, 2560, 768))
+    a.update(kw)
+    b = bank if bank is not None else _bank()
+    return lib.moe_expert_gemv_mxfp4(C.byref(b), a["x"], a["M"], a["idx"], a["tw"], a["K"], a["y16"], a["y32"],
+                                     a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("bank_kw,kw,status", [
+    (dict(format=_lib.QWS_FMT_BF16), {}, _lib.QWS_ERR_FORMAT),
+    (dict(format=_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE), {}, _lib.QWS_ERR_FORMAT),
+    (dict(down_s=None), {}, _lib.QWS_ERR_ARG), (dict(has_shared=2), {}, _lib.QWS_ERR_ARG),
+    ({}, dict(y16=None, y32=None), _lib.QWS_ERR_ARG), ({}, dict(idx=None), _lib.QWS_ERR_ARG),
+    (dict(hidden=2592), {}, _lib.QWS_ERR_SHAPE), (dict(hidden=48), {}, _lib.QWS_ERR_SHAPE),
+    (dict(inter=1056), {}, _lib.QWS_ERR_SHAPE), (dict(n_routed=0), {}, _lib.QWS_ERR_SHAPE),
+    ({}, dict(M=5), _lib.QWS_ERR_SHAPE), ({}, dict(K=9), _lib.QWS_ERR_SHAPE),
+    (dict(gate_up_q=MIS), {}, _lib.QWS_ERR_ALIGN), ({}, dict(x=MIS), _lib.QWS_ERR_ALIGN),
+    ({}, dict(wsb=1024), _lib.QWS_ERR_WORKSPACE), ({}, dict(ws=None), _lib.QWS_ERR_WORKSPACE),
+])
+def test_expert_validation(lib, bank_kw, kw, status):
+    assert _experts(lib, _bank(**bank_kw), **kw) == status
+
+
+def test_expert_workspace_for_larger_window_is_required(lib):
+    # a workspace sized for M = 1 is refused for M = 4
+    assert _experts(lib, M=4) == _lib.QWS_ERR_WORKSPACE
+
+
+def test_lmhead_format_tags_refuse_mismatched_heads(lib):
+    fp8 = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 157184, 2560, A, A)
+    bf16 = _lib.LMHeadDesc(_lib.QWS_FMT_BF16, 157184, 2560, A, None)
+    # an FP8 head handed to the bf16 GEMV is refused instead of being read as bf16, and vice versa
+    assert lib.lmhead_gemv_bf16(C.byref(fp8), A, 1, A, None) == _lib.QWS_ERR_FORMAT
+    assert lib.lmhead_gemv_fp8(C.byref(bf16), A, 1, A, None) == _lib.QWS_ERR_FORMAT
+    assert lib.qws_debug_dequant_fp8(C.byref(bf16), A, None) == _lib.QWS_ERR_FORMAT
+    nos = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 157184, 2560, A, None)
+    assert lib.lmhead_gemv_fp8(C.byref(nos), A, 1, A, None) == _lib.QWS_ERR_ARG
+
+
+@pytest.mark.parametrize("rows,cols,x,M,status", [
+    (0, 2560, A, 1, _lib.QWS_ERR_SHAPE), (10, 2592, A, 1, _lib.QWS_ERR_SHAPE), (10, 48, A, 1, _lib.QWS_ERR_SHAPE),
+    (10, 2560, A, 0, _lib.QWS_ERR_SHAPE), (10, 2560, A, 5, _lib.QWS_ERR_SHAPE), (10, 2560, MIS, 1, _lib.QWS_ERR_ALIGN),
+    (10, 2560, None, 1, _lib.QWS_ERR_ARG),
+])
+def test_lmhead_gemv_validation(lib, rows, cols, x, M, status):
+    d = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, A, A)
+    assert lib.lmhead_gemv_fp8(C.byref(d), x, M, A, None) == status
+
+
+def test_lmhead_desc_and_quantize_validation(lib):
+    d = _lib.LMHeadDesc()
+    assert lib.lmhead_bf16_desc(A, 157184, 2560, C.byref(d)) == _lib.QWS_OK
+    assert d.format == _lib.QWS_FMT_BF16 and d.rows == 157184 and d.cols == 2560
+    assert lib.lmhead_bf16_desc(MIS, 10, 64, C.byref(d)) == _lib.QWS_ERR_ALIGN
+    assert lib.lmhead_bf16_desc(A, 10, 63, C.byref(d)) == _lib.QWS_ERR_SHAPE
+    assert lib.lmhead_quantize_fp8(A, 10, 64, A, A, None, None) == _lib.QWS_ERR_ARG
+    assert lib.lmhead_quantize_fp8(A, 10, 2600, A, A, C.byref(d), None) == _lib.QWS_ERR_SHAPE
+    assert lib.lmhead_quantize_fp8(A, 10, 64, MIS, A, C.byref(d), None) == _lib.QWS_ERR_ALIGN
+
+
+def test_diagnostics_validation(lib):
+    assert lib.qws_debug_dequant_mxfp4(A, A, 4, 64, 2, A, None) == _lib.QWS_ERR_ARG
+    assert lib.qws_debug_dequant_mxfp4(A, A, 4, 48, 0, A, None) == _lib.QWS_ERR_SHAPE
+    assert lib.qws_debug_dequant_mxfp4(MIS, A, 4, 64, 0, A, None) == _lib.QWS_ERR_ALIGN
+    assert lib.qws_probe_read(A, 100, A, 4, None) == _lib.QWS_ERR_SHAPE
+    assert lib.qws_probe_read(A, 1024, A, 0, None) == _lib.QWS_ERR_SHAPE
+    assert lib.qws_probe_read(None, 1024, A, 4, None) == _lib.QWS_ERR_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,144 @@
+"""GPU parity of moe_expert_gemv_mxfp4 and of the whole MoE layer (router + experts) against the
+oracle: tiny ragged shapes for every M, the 64- and 512-expert layers at M = 1 (natural and
+Zipf-concentrated routing), the three M = 4 verification regimes, invalid ids, duplicated ids, no
+shared expert, bitwise determinism and per-token == single-token results."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_weight_streaming_amd as qws
+import synth
+from oracle import moe as OM
+
+from .helpers import Layer, assert_close, bf16, check_topk, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bank(layer: Layer):
+    return qws.ExpertBank.from_dict(layer.bank_t, layer.shape.n_routed, layer.shape.has_shared)
+
+
+def _experts_with_routing(layer: Layer, idx: np.ndarray, w: np.ndarray):
+    it = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    wt = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
+    y16, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, it, wt)
+    y32n = y32.cpu().numpy()
+    # the bf16 output is the round-to-nearest-even of the fp32 output, bit for bit
+    assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+    return y32n
+
+
+def _layer_case(layer: Layer):
+    """Route on the GPU, check the routing, then the layer output against the oracle's layer."""
+    logits = torch.empty((layer.M, layer.shape.n_routed), dtype=torch.float32, device="cuda")
+    idx_t, w_t = qws.moe_route_topk(layer.x_t, layer.wr_t, layer.shape.topk, layer.bias_t, logits_out=logits)
+    y16, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, idx_t, w_t)
+    ridx, rw, rlg = layer.oracle_route()
+    near = check_topk(idx_t.cpu().numpy(), logits.cpu().numpy(), rlg, layer.shape.topk)
+    assert near == 0, "near-tie in a seeded layer case: pick another seed"
+    ref = layer.oracle_y(ridx, rw)
+    e = assert_close(y32.cpu().numpy(), ref, what=f"layer seed={layer.seed} M={layer.M}")
+    assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+    return e, idx_t.cpu().numpy()
+
+
+TINY = [synth.LayerShape(hidden=64, inter=32, n_routed=6, topk=2),
+        synth.LayerShape(hidden=96, inter=64, n_routed=9, topk=3),
+        synth.LayerShape(hidden=2560, inter=768, n_routed=5, topk=4),
+        synth.LayerShape(hidden=544, inter=1024, n_routed=12, topk=8),
+        synth.LayerShape(hidden=2560, inter=96, n_routed=3, topk=1, has_shared=False)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("si", range(len(TINY)))
+def test_small_layers(M, si):
+    shape = TINY[si]
+    say("experts small", M, shape)
+    layer = Layer(10 + si, M, shape, M)
+    _layer_case(layer)
+
+
+def test_64_expert_layer_m1():
+    say("layer E=64 M=1")
+    _layer_case(Layer(0, 0, synth.LayerShape(n_routed=64), 1))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_512_expert_layer_m1(seed):
+    say("layer E=512 M=1 seed", seed)
+    bias = synth.zipf_bias(seed, 0, 512) if seed == 1 else None
+    _layer_case(Layer(seed, 0, synth.LayerShape(), 1, bias=bias))
+
+
+@pytest.mark.parametrize("regime,union", [("same", 8), ("half", 20), ("disjoint", 32)])
+def test_verification_regimes_m4(regime, union):
+    say("layer M=4 regime", regime)
+    sets = synth.regime_sets(0, 0, regime, 4, 512)
+    layer = Layer(0, 0, synth.LayerShape(), 4, bias=synth.regime_bias(sets, 512))
+    _, idx = _layer_case(layer)
+    assert len(set(idx.reshape(-1).tolist())) == union
+
+
+def test_natural_routing_m4():
+    say("layer M=4 natural")
+    _layer_case(Layer(0, 3, synth.LayerShape(), 4))
+
+
+def test_window_tokens_equal_single_tokens_bitwise():
+    say("M=4 per-token == M=1")
+    layer = Layer(2, 0, synth.LayerShape(), 4)
+    ridx, rw, _ = layer.oracle_route()
+    y4 = _experts_with_routing(layer, ridx, rw)
+    for m in range(4):
+        single = Layer.__new__(Layer)
+        single.__dict__.update(layer.__dict__)
+        single.x_t = layer.x_t[m:m + 1].contiguous()
+        y1 = _experts_with_routing(single, ridx[m:m + 1], rw[m:m + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y4[m].view(np.uint32)), f"token {m}"
+
+
+def test_deterministic_and_workspace_reuse():
+    say("experts determinism")
+    layer = Layer(3, 0, synth.LayerShape(), 4)
+    ridx, rw, _ = layer.oracle_route()
+    it = torch.from_numpy(ridx.astype(np.int32)).cuda()
+    wt = torch.from_numpy(rw.astype(np.float32)).cuda()
+    ws = qws.expert_workspace(4, 8, 2560, 768, "cuda")
+    a = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, it, wt, workspace=ws)[1].cpu().numpy()
+    b = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, it, wt, workspace=ws)[1].cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # the arrival counters at the end of the workspace are back to zero
+    slots = 4 * 8 + 1
+    off = ((slots * 4 * 768 * 4 + 255) // 256) * 256 + ((slots * 4 * 2560 * 4 + 255) // 256) * 256
+    cnt = ws[off:off + 4 * 40].cpu().view(torch.int32).numpy()
+    assert np.all(cnt == 0)
+
+
+def test_invalid_ids_give_nan_rows_only():
+    say("experts invalid ids")
+    layer = Layer(4, 0, synth.LayerShape(), 3)
+    ridx, rw, _ = layer.oracle_route()
+    idx = ridx.copy()
+    idx[1, 3] = 512          # out of range
+    idx[2, 0] = -1
+    y = _experts_with_routing(layer, idx, rw)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+    assert_close(y[0], layer.oracle_y(ridx[:1], rw[:1])[0], what="valid token next to invalid ones")
+
+
+def test_duplicate_ids_add_weights():
+    say("experts duplicate ids")
+    layer = Layer(5, 0, synth.LayerShape(), 1)
+    idx = np.array([[7, 7, 100, 3]])
+    w = np.array([[0.25, 0.25, 0.3, 0.2]])
+    y = _experts_with_routing(layer, idx, w)
+    assert_close(y, layer.oracle_y(idx, w), what="duplicate ids")
+
+
+def test_all_invalid_without_shared_expert():
+    say("experts all invalid, no shared")
+    shape = synth.LayerShape(hidden=128, inter=64, n_routed=4, topk=2, has_shared=False)
+    layer = Layer(6, 0, shape, 2)
+    y = _experts_with_routing(layer, np.array([[9, -3], [4, 5]]), np.full((2, 2), 0.5))
+    assert np.all(np.isnan(y))

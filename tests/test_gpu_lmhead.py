@@ -1,0 +1,93 @@
+"""GPU parity of the LM-head GEMVs (FP8 and bf16) against the oracle: small ragged shapes for every
+M, and the full 157,184 x 2,560 head (quantised on the device, compared with the oracle's codes
+and logits, argmax with the top-2 gap rule)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_weight_streaming_amd as qws
+import synth
+from oracle import lmhead as OL
+
+from .helpers import assert_close, bf16, check_argmax, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (999, 96), (2049, 2560), (5000, 544)])
+def test_gemv_small(M, rows, cols):
+    say("lmhead small", M, rows, cols)
+    w = synth.bf16_normal(1, 0, synth.HEAD, rows + cols, (rows, cols), 0.02)
+    x = synth.token_vectors(1, 0, M, cols)
+    wt, xt = bf16(w), bf16(x)
+    h8 = qws.lmhead_quantize_fp8(wt)
+    hb = qws.lmhead_bf16(wt)
+    l8 = qws.lmhead_gemv_fp8(h8, xt).cpu().numpy()
+    lb = qws.lmhead_gemv_bf16(hb, xt).cpu().numpy()
+    codes, scales = OL.fp8_rowquant(w)
+    assert_close(l8, OL.lmhead_fp8(codes, scales, x), what="fp8 head")
+    assert_close(lb, OL.lmhead_bf16(w, x), what="bf16 head")
+
+
+def test_gemv_one_hot_columns():
+    say("lmhead one-hot")
+    w = synth.bf16_normal(2, 0, synth.HEAD, 0, (300, 2560), 0.02)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    x = np.zeros((4, 2560), dtype=np.uint16)
+    cols = [0, 1, 1279, 2559]
+    for m, k in enumerate(cols):
+        x[m, k] = 0x3F80
+    got = qws.lmhead_gemv_fp8(h8, bf16(x)).cpu().numpy()
+    deq = qws.debug_dequant_fp8(h8).cpu().numpy()
+    for m, k in enumerate(cols):
+        assert np.array_equal(got[m], deq[:, k])  # exactly one nonzero product per row
+
+
+def test_gemv_deterministic():
+    say("lmhead determinism")
+    w = synth.bf16_normal(3, 0, synth.HEAD, 0, (7001, 2560), 0.02)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    x = bf16(synth.token_vectors(3, 0, 4))
+    a = qws.lmhead_gemv_fp8(h8, x).cpu().numpy()
+    b = qws.lmhead_gemv_fp8(h8, x).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # each token of a window equals the same token alone, bit for bit
+    for m in range(4):
+        s = qws.lmhead_gemv_fp8(h8, x[m:m + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(s[0].view(np.uint32), a[m].view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def full_head():
+    say("full head: generate + quantize 157184x2560")
+    w = synth.head_weights(0)
+    wt = bf16(w)
+    h8 = qws.lmhead_quantize_fp8(wt)
+    torch.cuda.synchronize()
+    codes, scales = OL.fp8_rowquant(w)
+    return w, wt, h8, codes, scales
+
+
+def test_full_head_quantize_bit_exact(full_head):
+    w, wt, h8, codes, scales = full_head
+    say("full head codes/scales")
+    assert np.array_equal(h8.row_scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(h8.w.cpu().numpy(), codes)
+
+
+def test_full_head_gemv(full_head):
+    w, wt, h8, codes, scales = full_head
+    hb = qws.lmhead_bf16(wt)
+    for M in (1, 4):
+        say("full head gemv M", M)
+        x = synth.token_vectors(0, 7, M)
+        xt = bf16(x)
+        l8 = qws.lmhead_gemv_fp8(h8, xt).cpu().numpy()
+        lb = qws.lmhead_gemv_bf16(hb, xt).cpu().numpy()
+        r8 = OL.lmhead_fp8(codes, scales, x)
+        rb = OL.lmhead_bf16(w, x)
+        assert_close(l8, r8, what=f"fp8 head M={M}")
+        assert_close(lb, rb, what=f"bf16 head M={M}")
+        check_argmax(l8, r8)
+        check_argmax(lb, rb)
