@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void down_combine_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float v = group_sum<8>(acc[r][m]);
-      if (j == 0 && row < H && ((mask >> m) & 1u)) partial[((size_t)slot * M + m) * H + row] = wt[m] * v;
+      if (j == 0 && row < H && ((mask >> m) & 1u)) st_coherent(partial + ((size_t)slot * M + m) * H + row, wt[m] * v);
     }
   }
 
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void down_combine_kernel(
     if (row >= H) continue;
     float s = 0.0f;
     for (int u = 0; u < un.n; ++u)
-      if ((un.mask[u] >> m) & 1u) s += partial[((size_t)u * M + m) * H + row];
+      if ((un.mask[u] >> m) & 1u) s += ld_coherent(partial + ((size_t)u * M + m) * H + row);
     if ((un.bad >> m) & 1u) s = __uint_as_float(0x7fc00000u);
     if (y32) y32[(size_t)m * H + row] = s;
     if (y16) y16[(size_t)m * H + row] = f32_to_bf16_rne(s);

@@ -80,22 +80,68 @@ __device__ __forceinline__ float group_sum(float v) {
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------------------ sync
-// Arrive on a counter shared by `expected` workgroups; returns true in the last one to arrive
-// (in every thread of it) after making the others' global writes visible to it. The last one
-// resets the counter to zero. All threads of the workgroup must call it.
+// Cross-workgroup hand-off inside one kernel, without an agent-scope fence. On gfx950 such a
+// fence writes back the whole L2 of the XCD and invalidates it, and every wave that executes one
+// serialises device-wide (~14 ns each), so a grid of hundreds of workgroups pays tens of
+// microseconds. Instead, data that another workgroup reads in the same kernel is written with a
+// device-coherent store (global_store ... sc1: written through to the coherence point that all
+// XCDs share) and read with a device-coherent load (global_load ... sc1: never served by a stale
+// L2/L1 copy). A writer waits for its stores to be acknowledged (s_waitcnt) before it signals on
+// a counter, and a reader only issues its loads after it has observed the signal.
+template <typename T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Arrive on `counter`, shared by `expected` workgroups that each call this once per launch;
+// returns true (in every thread) in the last one to arrive, which also resets the counter to zero
+// for the next launch. Every thread must have finished its st_coherent() stores beforehand and
+// every thread of the workgroup must call this.
 __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, bool* lds_flag) {
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned prev = atomicAdd(counter, 1u);
-    bool last = prev + 1 == expected;
-    if (last) *counter = 0u;
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1 == expected;
+    if (last) st_coherent(counter, 0u);
     *lds_flag = last;
   }
   __syncthreads();
-  bool last = *lds_flag;
-  if (last) __threadfence();
-  return last;
+  return *lds_flag;
+}
+
+// Two-level arrival for large grids: same-address atomics serialise (~10 ns each), so workgroups
+// first arrive on one of kArriveGroups counters (blockIdx % kArriveGroups) and the last of each
+// group arrives on counters[kArriveGroups]. Returns true in the single last workgroup of the grid.
+// Needs kArriveGroups + 1 counters, each on its own 128-byte line (stride kCounterStride).
+constexpr int kArriveGroups = 16;
+constexpr int kCounterStride = 32;  // unsigned words: 128 bytes
+__device__ __forceinline__ bool arrive_last_grid(unsigned* counters, bool* lds_flag) {
+  const unsigned g = blockIdx.x % kArriveGroups;
+  const unsigned groups = gridDim.x < (unsigned)kArriveGroups ? gridDim.x : (unsigned)kArriveGroups;
+  const unsigned in_group = (gridDim.x - g + kArriveGroups - 1) / kArriveGroups;
+  wait_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool last = false;
+    unsigned prev = __hip_atomic_fetch_add(counters + g * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1 == in_group) {
+      st_coherent(counters + g * kCounterStride, 0u);
+      prev = __hip_atomic_fetch_add(counters + kArriveGroups * kCounterStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      last = prev + 1 == groups;
+      if (last) st_coherent(counters + kArriveGroups * kCounterStride, 0u);
+    }
+    *lds_flag = last;
+  }
+  __syncthreads();
+  return *lds_flag;
 }
 
 }  // namespace qws

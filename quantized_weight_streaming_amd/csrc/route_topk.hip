@@ -44,7 +44,7 @@ __device__ void select_topk(const float* __restrict__ lg, int E, int K, int* __r
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     int e = lane + i * kWave;
-    key[i] = e < E ? ((unsigned long long)ordered_key(lg[e]) << 32) | (0xffffffffu - (unsigned)e) : 0ull;
+    key[i] = e < E ? ((unsigned long long)ordered_key(ld_coherent(lg + e)) << 32) | (0xffffffffu - (unsigned)e) : 0ull;
   }
   float sel_v[8];
   int sel_i[8];
@@ -120,21 +120,23 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_topk_kernel(
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float b = bias ? bias[(size_t)m * bias_stride + e] : 0.0f;
-        logits[(size_t)m * E + e] = acc[m] + b;
+        st_coherent(logits + (size_t)m * E + e, acc[m] + b);
       }
     }
   }
 
-  if (!arrive_last(counter, gridDim.x, &last_flag)) return;
+  if (!arrive_last_grid(counter, &last_flag)) return;
   for (int m = wave; m < M; m += kRouteWaves)
     select_topk(logits + (size_t)m * E, E, K, topk_idx + m * K, topk_w + m * K);
 }
 
 }  // namespace
 
+constexpr size_t kCounterBytes = (kArriveGroups + 1) * kCounterStride * sizeof(unsigned);
+
 extern "C" size_t moe_route_workspace_bytes(int M, int E) {
   if (M < 1 || M > 4 || E < 1 || E > kMaxE) return 0;
-  return qws_host::align256((size_t)M * E * sizeof(float)) + 256;
+  return qws_host::align256((size_t)M * E * sizeof(float)) + kCounterBytes;
 }
 
 extern "C" int moe_route_topk(const void* x_bf16, int M, int H, const void* w_router_bf16, int E,

@@ -15,6 +15,14 @@ from .helpers import Layer, assert_close, bf16, check_topk, say
 pytestmark = pytest.mark.gpu
 
 
+def _assert_bf16_is_rne_of_f32(y16: torch.Tensor, y32: torch.Tensor):
+    """y_bf16 is the round-to-nearest-even of y_f32 bit for bit; any NaN stays a NaN."""
+    a, b = y16.cpu(), y32.cpu()
+    nan = torch.isnan(b)
+    assert torch.equal(torch.isnan(a.float()), nan)
+    assert torch.equal(a.view(torch.int16)[~nan], b.to(torch.bfloat16).view(torch.int16)[~nan])
+
+
 def _bank(layer: Layer):
     return qws.ExpertBank.from_dict(layer.bank_t, layer.shape.n_routed, layer.shape.has_shared)
 
@@ -24,8 +32,7 @@ def _experts_with_routing(layer: Layer, idx: np.ndarray, w: np.ndarray):
     wt = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
     y16, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, it, wt)
     y32n = y32.cpu().numpy()
-    # the bf16 output is the round-to-nearest-even of the fp32 output, bit for bit
-    assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+    _assert_bf16_is_rne_of_f32(y16, y32)
     return y32n
 
 
@@ -39,7 +46,7 @@ def _layer_case(layer: Layer):
     assert near == 0, "near-tie in a seeded layer case: pick another seed"
     ref = layer.oracle_y(ridx, rw)
     e = assert_close(y32.cpu().numpy(), ref, what=f"layer seed={layer.seed} M={layer.M}")
-    assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+    _assert_bf16_is_rne_of_f32(y16, y32)
     return e, idx_t.cpu().numpy()
 
 
@@ -124,7 +131,7 @@ def test_invalid_ids_give_nan_rows_only():
     idx[2, 0] = -1
     y = _experts_with_routing(layer, idx, rw)
     assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
-    assert_close(y[0], layer.oracle_y(ridx[:1], rw[:1])[0], what="valid token next to invalid ones")
+    assert_close(y[0], layer.oracle_y(ridx, rw)[0], what="valid token next to invalid ones")
 
 
 def test_duplicate_ids_add_weights():
@@ -142,3 +149,47 @@ def test_all_invalid_without_shared_expert():
     layer = Layer(6, 0, shape, 2)
     y = _experts_with_routing(layer, np.array([[9, -3], [4, 5]]), np.full((2, 2), 0.5))
     assert np.all(np.isnan(y))
+
+
+def test_graph_replay_matches_eager():
+    """A captured layer + head replays correctly several times, with eager work in between
+    (the arrival counters reset themselves; nothing in the path records a memset)."""
+    say("graph replay layer + head")
+    layer = Layer(7, 0, synth.LayerShape(), 1)
+    bank = _bank(layer)
+    ws_r = qws.route_workspace(1, 512, "cuda")
+    ws_e = qws.expert_workspace(1, 8, 2560, 768, "cuda")
+    idx = torch.empty((1, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, 8), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, 2560), dtype=torch.bfloat16, device="cuda")
+    head = qws.lmhead_quantize_fp8(bf16(synth.head_chunk(7, 0, 4096)))
+    logits = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+
+    def run():
+        qws.moe_route_topk(layer.x_t, layer.wr_t, 8, topk_idx=idx, topk_w=w, workspace=ws_r)
+        qws.moe_expert_gemv_mxfp4(bank, layer.x_t, idx, w, y_bf16=y, workspace=ws_e, want_f32=False)
+        qws.lmhead_gemv_fp8(head, layer.x_t, out=logits)
+
+    run()
+    torch.cuda.synchronize()
+    ref_y, ref_l = y.clone(), logits.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(5):
+        y.zero_()
+        logits.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), f"replay {i}: layer output"
+        assert torch.equal(logits.view(torch.int32), ref_l.view(torch.int32)), f"replay {i}: logits"
+        run()                                                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16))
