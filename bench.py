@@ -6,9 +6,10 @@ MXFP4 gate_up/down with SwiGLU, hidden 2560, intermediate 768; each layer with i
 weights and token vector) followed by the FP8 LM head (157,184 x 2,560), at M = 1 token. Inputs are
 resident in HBM before timing starts. The value is whole-step algorithmic bytes / step time.
 
-The 42 layers of a step replay as one captured HIP graph (the launches are dependent and short);
-the FP8 head runs between two HIP events on the same stream in every timed step, which gives the
-live per-launch duration of the step's largest kernel for the roofline entry.
+The 42 layers of a step run as ONE persistent launch (moe_layers_mxfp4: each layer's router,
+top-K, experts and combine inside one grid, layer l+1 starting after layer l's output is written);
+the FP8 head follows on the same stream. HIP events bracket both launches in every timed step,
+which gives the live per-launch duration of the head for the roofline entry.
 
 Also reported (in "breakdown"): one layer cold-cache at M = 1 (natural and Zipf-concentrated
 routing), the three M = 4 verification regimes and their cost ratio over M = 1, the FP8 and bf16
@@ -73,16 +74,18 @@ def _bf16(bits, dev):
 
 
 class Flusher:
-    """Evicts L2 and the Infinity Cache by writing 1 GiB between timed iterations."""
+    """Evicts L2 and the Infinity Cache between timed iterations by streaming a 1 GiB buffer
+    through the read probe (a read flush leaves no dirty lines to write back during the next
+    measured launch)."""
 
-    def __init__(self, dev):
+    def __init__(self, qws, dev):
         import torch
-        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        self.k = 0
+        self.qws = qws
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        self.sink = torch.empty(4096, dtype=torch.int32, device=dev)
 
     def __call__(self):
-        self.k += 1
-        self.buf.fill_(self.k & 0xFF)
+        self.qws.probe_read(self.buf, self.sink, 4096)
 
 
 def time_cold(fn, dev, iters=50, warm=5, flush=None):
@@ -104,7 +107,8 @@ def time_cold(fn, dev, iters=50, warm=5, flush=None):
 
 
 class MoeLayer:
-    """Device-resident inputs, routing buffers and workspaces of one MoE layer."""
+    """Device-resident inputs and outputs of one MoE layer, runnable through the fused one-launch
+    entry point or through the two-call path (router kernel, then the expert kernels)."""
 
     def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None):
         import torch
@@ -115,13 +119,15 @@ class MoeLayer:
         self.wr = _bf16(synth.router_weights(seed, layer, shape.n_routed), dev)
         self.x = _bf16(synth.token_vectors(seed, layer, M), dev)
         self.bias = None if bias is None else torch.from_numpy(bias).to(dev)
-        self.idx = torch.empty((M, K_TOP), dtype=torch.int32, device=dev)
-        self.w = torch.empty((M, K_TOP), dtype=torch.float32, device=dev)
-        self.y = torch.empty((M, shape.hidden), dtype=torch.bfloat16, device=dev)
+        self.fused = qws.MoeLayer(self.x, self.wr, self.bank, K_TOP, bias=self.bias, want_f32=False)
+        self.idx, self.w, self.y = self.fused.topk_idx, self.fused.topk_w, self.fused.y_bf16
         self.M = M
         self.qws = qws
 
-    def run(self, ws_route, ws_exp):
+    def run(self, ws):
+        self.qws.moe_layer_mxfp4(self.fused, workspace=ws)
+
+    def run_two_call(self, ws_route, ws_exp):
         q = self.qws
         q.moe_route_topk(self.x, self.wr, K_TOP, self.bias, topk_idx=self.idx, topk_w=self.w, workspace=ws_route)
         q.moe_expert_gemv_mxfp4(self.bank, self.x, self.idx, self.w, y_bf16=self.y, workspace=ws_exp, want_f32=False)
@@ -146,62 +152,52 @@ def probe_ceiling(qws, dev):
 
 # ------------------------------------------------------------------------------------ decode step
 class DecodeStep:
+    """42 MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head."""
+
     def __init__(self, qws, M, dev, n_layers, head, banks=None):
         import torch
+        import synth
         self.qws, self.M, self.dev = qws, M, dev
         log(f"building {n_layers} layers (M={M})")
         self.layers = [MoeLayer(qws, 0, l, M, dev, bank=None if banks is None else banks[l]) for l in range(n_layers)]
-        self.ws_route = qws.route_workspace(M, 512, dev)
-        self.ws_exp = qws.expert_workspace(M, K_TOP, 2560, 768, dev)
-        import synth
+        self.seq = qws.MoeLayers([L.fused for L in self.layers])
+        self.ws = qws.moe_layer_workspace(M, K_TOP, 512, 2560, 768, dev)
         self.xh = _bf16(synth.token_vectors(0, 1000, M), dev)
         self.head = head
         self.logits = torch.empty((M, head.rows), dtype=torch.float32, device=dev)
-        self.graph = None
 
-    def layers_eager(self):
-        for L in self.layers:
-            L.run(self.ws_route, self.ws_exp)
+    def layers_call(self):
+        self.seq.run(self.ws)
 
     def head_call(self):
         self.qws.lmhead_gemv_fp8(self.head, self.xh, out=self.logits)
 
-    def capture(self):
-        import torch
-        s = torch.cuda.Stream(self.dev)
-        s.wait_stream(torch.cuda.current_stream(self.dev))
-        with torch.cuda.stream(s):
-            self.layers_eager()          # warm the path on the capture stream
-        torch.cuda.current_stream(self.dev).wait_stream(s)
-        torch.cuda.synchronize(self.dev)
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            self.layers_eager()
-        torch.cuda.synchronize(self.dev)
-
     def bytes(self):
         return sum(layer_bytes(L.union(), self.M) for L in self.layers) + head_bytes(self.M)
+
+    def errors(self):
+        return self.qws.moe_workspace_errors(self.ws, self.M, K_TOP, 512, 768)
 
     def timed(self, steps, warmup):
         import torch
         for _ in range(warmup):
-            self.graph.replay()
+            self.layers_call()
             self.head_call()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize(self.dev)
         t0 = time.perf_counter()
-        g0.record()
-        for a, b in ev:
-            self.graph.replay()
+        for a, b, c in ev:
             a.record()
-            self.head_call()
+            self.layers_call()
             b.record()
-        g1.record()
+            self.head_call()
+            c.record()
         torch.cuda.synchronize(self.dev)
         wall = (time.perf_counter() - t0) / steps
-        head_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-        return {"wall_ms": wall * 1e3, "gpu_ms": g0.elapsed_time(g1) / steps,
+        moe_us = sorted(a.elapsed_time(b) * 1e3 for a, b, _ in ev)
+        head_us = sorted(b.elapsed_time(c) * 1e3 for _, b, c in ev)
+        gpu_ms = sum(a.elapsed_time(c) for a, _, c in ev) / steps
+        return {"wall_ms": wall * 1e3, "gpu_ms": gpu_ms, "moe_us_mean": sum(moe_us) / len(moe_us),
                 "head_us_mean": sum(head_us) / len(head_us), "head_us_median": head_us[len(head_us) // 2]}
 
 
@@ -292,14 +288,13 @@ def main():
     log(f"head generated in {time.perf_counter() - t0:.1f}s")
     head_bf16 = qws.lmhead_bf16(wh_t)
     head8 = qws.lmhead_quantize_fp8(wh_t)
-    flush = Flusher(dev)
+    flush = Flusher(qws, dev)
     quant_us = time_cold(lambda: qws.lmhead_quantize_fp8(wh_t, codes=head8.w, row_scale=head8.row_scale), dev,
                          iters=5, warm=1, flush=flush)["median_us"]
 
     step = DecodeStep(qws, 1, dev, args.layers, head8)
-    step.layers_eager()
+    step.layers_call()
     torch.cuda.synchronize(dev)
-    step.capture()
     sb = step.bytes()
     log(f"decode step M=1: {args.layers} layers, {sb / 1e9:.3f} GB per step; timing {args.steps} steps")
     r = step.timed(args.steps, args.warmup)
@@ -312,38 +307,43 @@ def main():
                 "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": head_launch_bytes, "launch_us_mean": round(r["head_us_mean"], 2)}
 
+    moe_bytes = sb - head_bytes(1)
     breakdown = {"decode_step_m1": {"ms_wall": round(r["wall_ms"], 4), "ms_gpu_events": round(r["gpu_ms"], 4),
                                     "bytes": sb, "GBps": round(value, 1),
+                                    "moe_layers_us": round(r["moe_us_mean"], 2),
+                                    "moe_us_per_layer": round(r["moe_us_mean"] / args.layers, 3),
+                                    "moe_layers_GBps": round(moe_bytes / (r["moe_us_mean"] * 1e-6) / 1e9, 1),
                                     "head_us_median": round(r["head_us_median"], 2),
-                                    "moe_us_per_layer": round((r["gpu_ms"] * 1e3 - r["head_us_mean"]) / args.layers, 3),
-                                    "unions": [L.union() for L in step.layers[:4]]},
+                                    "unions": [L.union() for L in step.layers[:4]],
+                                    "in_kernel_wait_timeouts": step.errors()},
                  "lmhead_quantize_fp8_us": round(quant_us, 1)}
 
     if not args.no_breakdown:
         breakdown["probe_read_ceiling"] = probe_ceiling(qws, dev)
         log("probe", breakdown["probe_read_ceiling"])
+        wsf = {1: qws.moe_layer_workspace(1, K_TOP, 512, 2560, 768, dev),
+               4: qws.moe_layer_workspace(4, K_TOP, 512, 2560, 768, dev)}
         wsr1 = qws.route_workspace(1, 512, dev)
         wse1 = qws.expert_workspace(1, K_TOP, 2560, 768, dev)
-        wsr4 = qws.route_workspace(4, 512, dev)
-        wse4 = qws.expert_workspace(4, K_TOP, 2560, 768, dev)
         lay = {}
         L0 = step.layers[0]
-        lay["moe_layer_m1_seed0"] = (MoeLayer(qws, 0, 0, 1, dev, bank=L0.bank_t), wsr1, wse1)
+        lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, bank=L0.bank_t)
         bank1 = synth.expert_bank_torch(1, 0, synth.LayerShape(), device=dev)
-        lay["moe_layer_m1_seed1_zipf"] = (MoeLayer(qws, 1, 0, 1, dev, bias=synth.zipf_bias(1, 0, 512), bank=bank1),
-                                          wsr1, wse1)
+        lay["moe_layer_m1_seed1_zipf"] = MoeLayer(qws, 1, 0, 1, dev, bias=synth.zipf_bias(1, 0, 512), bank=bank1)
         for reg in synth.REGIMES:
             sets = synth.regime_sets(0, 0, reg, 4, 512)
-            lay[f"moe_layer_m4_{reg}"] = (MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512),
-                                                   bank=L0.bank_t), wsr4, wse4)
-        for name, (Lr, wr_, we_) in lay.items():
-            t = time_cold(lambda: Lr.run(wr_, we_), dev, flush=flush)
+            lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), bank=L0.bank_t)
+        for name, Lr in lay.items():
+            t = time_cold(lambda: Lr.run(wsf[Lr.M]), dev, flush=flush)
             u = Lr.union()
             b = layer_bytes(u, Lr.M)
             t.update({"union": u, "bytes": b, "GBps": round(b / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
             breakdown[name] = t
             log(name, t)
+        L2 = lay["moe_layer_m1_seed0"]
+        t = time_cold(lambda: L2.run_two_call(wsr1, wse1), dev, flush=flush)
+        breakdown["moe_layer_m1_seed0_two_call_path"] = {"median_us": t["median_us"]}
         t1 = breakdown["moe_layer_m1_seed0"]["median_us"]
         breakdown["verify_cost_ratio"] = {reg: round(breakdown[f"moe_layer_m4_{reg}"]["median_us"] / t1, 3)
                                           for reg in synth.REGIMES}
@@ -361,12 +361,12 @@ def main():
             log(name, t)
         # decode step at M = 4 (natural routing), sharing the M = 1 step's expert banks
         step4 = DecodeStep(qws, 4, dev, args.layers, head8, banks=[L.bank_t for L in step.layers])
-        step4.layers_eager()
+        step4.layers_call()
         torch.cuda.synchronize(dev)
-        step4.capture()
         r4 = step4.timed(max(5, args.steps // 2), 2)
         b4 = step4.bytes()
         breakdown["decode_step_m4"] = {"ms_wall": round(r4["wall_ms"], 4), "bytes": b4,
+                                       "moe_us_per_layer": round(r4["moe_us_mean"] / args.layers, 3),
                                        "GBps": round(b4 / (r4["wall_ms"] * 1e-3) / 1e9, 1),
                                        "mean_union": round(float(np.mean([L.union() for L in step4.layers])), 2)}
         log("decode_step_m4", breakdown["decode_step_m4"])

@@ -138,6 +138,49 @@ int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
                           qws_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * One MoE layer in ONE launch: router GEMV, top-K, softmax, expert union, MXFP4 gate_up + SwiGLU,
+ * MXFP4 down + gate-weighted combine with the shared expert -- the same arithmetic as
+ * moe_route_topk followed by moe_expert_gemv_mxfp4, without the kernel boundaries between them
+ * (each costs ~1.7 us on MI355X, a third of a layer's streaming time at M = 1). The grid is one
+ * persistent workgroup per compute unit; its three internal hand-offs use device-coherent stores
+ * and arrival counters in the workspace.
+ * -------------------------------------------------------------------------------------------*/
+typedef struct {
+  const void* x_bf16;         /* [M, H] bf16, ready before the launch                               */
+  const void* w_router_bf16;  /* [E, H] bf16, E = experts.n_routed                                  */
+  const float* bias;          /* NULL, [E] (bias_row_stride 0) or [M, E] (bias_row_stride E)         */
+  long long bias_row_stride;
+  qws_mxfp4_experts experts;  /* the layer's bank; shapes must be equal across the layers of a call */
+  int* topk_idx;              /* NULL or [M, K] int32 out                                            */
+  float* topk_w;              /* NULL or [M, K] fp32 out                                             */
+  float* logits_out;          /* NULL or [M, E] fp32 out                                             */
+  void* y_bf16;               /* NULL or [M, H] bf16 out (RNE of y_f32)                              */
+  float* y_f32;               /* NULL or [M, H] fp32 out; at least one of y_bf16, y_f32             */
+} qws_moe_layer;
+
+/* Workspace for moe_layer_mxfp4 / moe_layers_mxfp4: ZERO-FILLED before its first use and then
+ * reused as is (its arrival counters only increase; nothing needs resetting, so a launch may be
+ * captured in a HIP graph and replayed). One workspace per device and stream; calls sharing it
+ * must not overlap in time. E <= 1024, H <= 2560, I <= 1024, K <= 8, M <= 4. */
+size_t moe_layer_workspace_bytes(int M, int K, int E, int hidden, int inter);
+
+/* One layer; `layer` is host memory. Same contract as the two-call path above. */
+int moe_layer_mxfp4(const qws_moe_layer* layer, int M, int K, void* workspace, size_t workspace_bytes,
+                    qws_stream_t stream);
+
+/* n_layers layers in stream order in one launch: layer l+1 starts its x-dependent work only
+ * after layer l's output is written. layers_host (host memory) is validated; layers_device must
+ * be an identical copy in device memory (read by the kernel for layers 1 .. n_layers-1). */
+int moe_layers_mxfp4(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
+                     int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream);
+
+/* Number of bounded in-kernel waits that timed out so far in this workspace (0 when healthy; a
+ * timeout means the grid was not co-resident, and that launch's outputs are not valid).
+ * Synchronises `stream`; errors_out is host memory. */
+int moe_workspace_errors(const void* workspace, int M, int K, int E, int inter, unsigned* errors_out,
+                         qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Vocabulary LM head (non-owning view). The head projects H = 2,560 onto 157,184 tokens and
  * every generated token reads all of it: ~805 MB per token in bf16, half in FP8 (posts/593
  * paragraph 3).
@@ -190,6 +233,15 @@ int qws_debug_dequant_mxfp4(const unsigned char* q, const unsigned char* s, long
 
 /* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for an FP8-tagged head, fp32 [rows, cols].  */
 int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t stream);
+
+/* Tracing of the fused MoE launches on the current device: while `buf` is registered (device
+ * memory, 16-byte aligned), every moe_layer_mxfp4 / moe_layers_mxfp4 launch whose trace fits in
+ * `bytes` writes, per layer and workgroup, 16 timestamps of the device wall clock (100 MHz,
+ * uint64): [0] layer start, [1] router/shared done, [2] after the first hand-off, [3] top-K and
+ * union done, [4] gate_up done, [5] after the second hand-off, [6] activations staged, [7] output
+ * written, [8]/[9] first hand-off drained/polled, [10]/[11] second, [12]/[13] layer boundary,
+ * [14] top-K done; layout [n_layers][grid][16]. NULL unregisters. Diagnostics only. */
+int qws_debug_trace_buffer(void* buf, size_t bytes);
 
 /* Streaming-read probe: reads `bytes` (multiple of 16, 16-byte aligned) with 128-bit loads and
  * writes one checksum word per workgroup into sink[0 .. blocks) (blocks <= 65536). Measures the

@@ -18,9 +18,10 @@ import torch
 
 from . import _lib
 from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32, LMHeadDesc,  # noqa: F401
-                   MxFp4Experts, QwsError, check)
+                   MoeLayerDesc, MxFp4Experts, QwsError, check)
 
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "LMHead", "lmhead_bf16",
+           "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
@@ -147,6 +148,83 @@ def moe_expert_gemv_mxfp4(bank: ExpertBank, x: torch.Tensor, topk_idx: torch.Ten
     return y_bf16, y_f32
 
 
+# ----------------------------------------------------------------------------------- fused layer(s)
+def moe_layer_workspace(M: int, K: int, E: int, hidden: int, inter: int, device) -> torch.Tensor:
+    n = lib().moe_layer_workspace_bytes(M, K, E, hidden, inter)
+    if n == 0:
+        raise ValueError("unsupported fused-layer shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+class MoeLayer:
+    """Tensors and the qws_moe_layer descriptor of one layer for the fused entry points."""
+
+    def __init__(self, x, w_router, bank: ExpertBank, K: int, bias=None, y_bf16=None, y_f32=None,
+                 topk_idx=None, topk_w=None, logits_out=None, want_bf16=True, want_f32=True):
+        _need(x, "x", torch.bfloat16, 2)
+        _need(w_router, "w_router", torch.bfloat16, 2)
+        M, H = x.shape
+        dev = x.device
+        if bias is not None:
+            _need(bias, "bias", torch.float32)
+        if y_bf16 is None and want_bf16:
+            y_bf16 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        if y_f32 is None and want_f32:
+            y_f32 = torch.empty((M, H), dtype=torch.float32, device=dev)
+        if topk_idx is None:
+            topk_idx = torch.empty((M, K), dtype=torch.int32, device=dev)
+        if topk_w is None:
+            topk_w = torch.empty((M, K), dtype=torch.float32, device=dev)
+        self.x, self.w_router, self.bank, self.bias = x, w_router, bank, bias
+        self.y_bf16, self.y_f32, self.topk_idx, self.topk_w, self.logits_out = y_bf16, y_f32, topk_idx, topk_w, logits_out
+        self.M, self.K = M, K
+        stride = 0 if bias is None or bias.dim() == 1 else bias.shape[-1]
+        self.desc = MoeLayerDesc(x.data_ptr(), w_router.data_ptr(), None if bias is None else bias.data_ptr(), stride,
+                                 bank.desc, topk_idx.data_ptr(), topk_w.data_ptr(),
+                                 None if logits_out is None else logits_out.data_ptr(),
+                                 None if y_bf16 is None else y_bf16.data_ptr(),
+                                 None if y_f32 is None else y_f32.data_ptr())
+
+
+def moe_layer_mxfp4(layer: MoeLayer, workspace=None) -> MoeLayer:
+    """Router + top-K + experts of one layer in one launch; fills the layer's output tensors."""
+    b = layer.bank
+    if workspace is None:
+        workspace = moe_layer_workspace(layer.M, layer.K, b.n_routed, b.hidden, b.inter, layer.x.device)
+    st = lib().moe_layer_mxfp4(C.byref(layer.desc), layer.M, layer.K, _p(workspace), workspace.numel(),
+                               _stream(layer.x.device))
+    check("moe_layer_mxfp4", st)
+    return layer
+
+
+class MoeLayers:
+    """A sequence of layers run by moe_layers_mxfp4 in one launch (descriptors copied to the device once)."""
+
+    def __init__(self, layers: list):
+        self.layers = layers
+        n = len(layers)
+        self.host = (MoeLayerDesc * n)(*[L.desc for L in layers])
+        raw = torch.frombuffer(bytearray(C.string_at(C.addressof(self.host), C.sizeof(self.host))), dtype=torch.uint8)
+        self.dev = raw.to(layers[0].x.device)
+
+    def run(self, workspace) -> None:
+        L0 = self.layers[0]
+        st = lib().moe_layers_mxfp4(self.host, _p(self.dev), len(self.layers), L0.M, L0.K, _p(workspace),
+                                    workspace.numel(), _stream(L0.x.device))
+        check("moe_layers_mxfp4", st)
+
+
+def moe_layers_mxfp4(layers: MoeLayers, workspace) -> None:
+    layers.run(workspace)
+
+
+def moe_workspace_errors(workspace: torch.Tensor, M: int, K: int, E: int, inter: int) -> int:
+    out = C.c_uint(0)
+    check("moe_workspace_errors", lib().moe_workspace_errors(_p(workspace), M, K, E, inter, C.byref(out),
+                                                             _stream(workspace.device)))
+    return int(out.value)
+
+
 # ----------------------------------------------------------------------------------- LM head
 @dataclass
 class LMHead:
@@ -218,6 +296,11 @@ def debug_dequant_fp8(head: LMHead) -> torch.Tensor:
     out = torch.empty((head.desc.rows, head.desc.cols), dtype=torch.float32, device=head.w.device)
     check("qws_debug_dequant_fp8", lib().qws_debug_dequant_fp8(C.byref(head.desc), _p(out), _stream(head.w.device)))
     return out
+
+
+def debug_trace_buffer(buf) -> None:
+    """Register (or, with None, unregister) a device buffer for fused-launch phase timestamps."""
+    check("qws_debug_trace_buffer", lib().qws_debug_trace_buffer(_p(buf), 0 if buf is None else buf.numel() * buf.element_size()))
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:

@@ -27,6 +27,12 @@ class MxFp4Experts(C.Structure):
                 ("down_s", C.c_void_p)]
 
 
+class MoeLayerDesc(C.Structure):
+    _fields_ = [("x_bf16", C.c_void_p), ("w_router_bf16", C.c_void_p), ("bias", C.c_void_p),
+                ("bias_row_stride", C.c_longlong), ("experts", MxFp4Experts), ("topk_idx", C.c_void_p),
+                ("topk_w", C.c_void_p), ("logits_out", C.c_void_p), ("y_bf16", C.c_void_p), ("y_f32", C.c_void_p)]
+
+
 class LMHeadDesc(C.Structure):
     _fields_ = [("format", C.c_uint), ("rows", C.c_longlong), ("cols", C.c_longlong), ("w", C.c_void_p),
                 ("row_scale", C.c_void_p)]
@@ -46,6 +52,10 @@ SIGNATURES = {
     "moe_route_topk": (_I, [_P, _I, _I, _P, _I, _P, _LL, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moe_expert_gemv_mxfp4": (_I, [C.POINTER(MxFp4Experts), _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "moe_layer_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_layer_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _I, _I, _P, _SZ, _P]),
+    "moe_layers_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _P, _I, _I, _I, _P, _SZ, _P]),
+    "moe_workspace_errors": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_uint), _P]),
     "lmhead_bf16_desc": (_I, [_P, _LL, _LL, C.POINTER(LMHeadDesc)]),
     "lmhead_quantize_fp8": (_I, [_P, _LL, _LL, _P, _P, C.POINTER(LMHeadDesc), _P]),
     "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
@@ -53,6 +63,7 @@ SIGNATURES = {
     "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),
     "qws_debug_dequant_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _P]),
     "qws_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
+    "qws_debug_trace_buffer": (_I, [_P, _SZ]),
 }
 
 _lib = None

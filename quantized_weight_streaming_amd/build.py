@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqws.so")
-SOURCES = ["route_topk.hip", "expert_gemv.hip", "lmhead.hip", "diag.hip"]
+SOURCES = ["route_topk.hip", "expert_gemv.hip", "moe_fused.hip", "lmhead.hip", "diag.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops keeps the compiler from forming v_pk_{add,mul,fma}_f32
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

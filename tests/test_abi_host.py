@@ -158,3 +158,42 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def _layer_desc(**kw):
+    d = dict(x_bf16=A, w_router_bf16=A, bias=None, bias_row_stride=0, experts=_bank(), topk_idx=A, topk_w=A,
+             logits_out=None, y_bf16=A, y_f32=A)
+    d.update(kw)
+    return _lib.MoeLayerDesc(**d)
+
+
+@pytest.mark.parametrize("kw,M,K,wsb,status", [
+    (dict(x_bf16=None), 1, 8, None, _lib.QWS_ERR_ARG),
+    (dict(y_bf16=None, y_f32=None), 1, 8, None, _lib.QWS_ERR_ARG),
+    (dict(experts=_bank(format=_lib.QWS_FMT_BF16)), 1, 8, None, _lib.QWS_ERR_FORMAT),
+    (dict(experts=_bank(down_q=None)), 1, 8, None, _lib.QWS_ERR_ARG),
+    ({}, 5, 8, None, _lib.QWS_ERR_SHAPE), ({}, 1, 9, None, _lib.QWS_ERR_SHAPE),
+    (dict(experts=_bank(hidden=2592)), 1, 8, None, _lib.QWS_ERR_SHAPE),
+    (dict(experts=_bank(n_routed=4)), 1, 8, None, _lib.QWS_ERR_SHAPE),       # E < K
+    (dict(bias=A, bias_row_stride=3), 1, 8, None, _lib.QWS_ERR_SHAPE),
+    (dict(x_bf16=MIS), 1, 8, None, _lib.QWS_ERR_ALIGN),
+    (dict(experts=_bank(gate_up_q=MIS)), 1, 8, None, _lib.QWS_ERR_ALIGN),
+    ({}, 1, 8, 64, _lib.QWS_ERR_WORKSPACE),
+])
+def test_fused_layer_validation(lib, kw, M, K, wsb, status):
+    d = _layer_desc(**kw)
+    n = lib.moe_layer_workspace_bytes(M, K, 512, 2560, 768) if wsb is None else wsb
+    assert lib.moe_layer_mxfp4(C.byref(d), M, K, A, n if n else 1 << 20, None) == status
+
+
+def test_fused_layers_validation(lib):
+    good = _layer_desc()
+    bad = _layer_desc(experts=_bank(inter=512))                                   # shapes differ across layers
+    arr = (_lib.MoeLayerDesc * 2)(good, bad)
+    n = lib.moe_layer_workspace_bytes(1, 8, 512, 2560, 768)
+    assert lib.moe_layers_mxfp4(arr, A, 2, 1, 8, A, n, None) == _lib.QWS_ERR_SHAPE
+    arr2 = (_lib.MoeLayerDesc * 2)(good, good)
+    assert lib.moe_layers_mxfp4(arr2, None, 2, 1, 8, A, n, None) == _lib.QWS_ERR_ARG  # no device copy
+    assert lib.moe_layers_mxfp4(arr2, A, 0, 1, 8, A, n, None) == _lib.QWS_ERR_ARG
+    assert lib.moe_layer_workspace_bytes(1, 8, 512, 2560, 768) > 512 * 4 + 9 * 768 * 4
+    assert lib.moe_layer_workspace_bytes(5, 8, 512, 2560, 768) == 0

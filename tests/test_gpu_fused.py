@@ -1,0 +1,167 @@
+"""GPU parity of the fused one-launch MoE layer (moe_layer_mxfp4) and of the multi-layer launch
+(moe_layers_mxfp4) against the oracle and against the two-call path; graph replay; the full
+42-layer decode step on sampled layers."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_weight_streaming_amd as qws
+import synth
+
+from .helpers import Layer, assert_close, check_topk, say
+from .test_gpu_experts import TINY, _assert_bf16_is_rne_of_f32, _bank
+
+pytestmark = pytest.mark.gpu
+
+
+def _fused(layer: Layer, ws=None, logits=True):
+    lg = torch.empty((layer.M, layer.shape.n_routed), dtype=torch.float32, device="cuda") if logits else None
+    L = qws.MoeLayer(layer.x_t, layer.wr_t, _bank(layer), layer.shape.topk, bias=layer.bias_t, logits_out=lg)
+    qws.moe_layer_mxfp4(L, workspace=ws)
+    return L
+
+
+def _check_layer(layer: Layer, L):
+    ridx, rw, rlg = layer.oracle_route()
+    near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, layer.shape.topk)
+    assert near == 0
+    e = assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"fused layer seed={layer.seed} M={layer.M}")
+    _assert_bf16_is_rne_of_f32(L.y_bf16, L.y_f32)
+    assert_close(L.topk_w.cpu().numpy(), rw, tol=1e-5, what="gate weights")
+    return e
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("si", range(len(TINY)))
+def test_fused_small_layers(M, si):
+    shape = TINY[si]
+    say("fused small", M, shape)
+    layer = Layer(20 + si, M, shape, M)
+    _check_layer(layer, _fused(layer))
+
+
+@pytest.mark.parametrize("E", [64, 512])
+def test_fused_layer_m1(E):
+    say("fused layer M=1 E", E)
+    _check_layer(Layer(0, 0, synth.LayerShape(n_routed=E), 1), _fused(Layer(0, 0, synth.LayerShape(n_routed=E), 1)))
+
+
+def test_fused_layer_zipf():
+    say("fused layer zipf")
+    layer = Layer(1, 0, synth.LayerShape(), 1, bias=synth.zipf_bias(1, 0, 512))
+    _check_layer(layer, _fused(layer))
+
+
+@pytest.mark.parametrize("regime,union", [("same", 8), ("half", 20), ("disjoint", 32), ("natural", None)])
+def test_fused_window_m4(regime, union):
+    say("fused M=4", regime)
+    bias = None if regime == "natural" else synth.regime_bias(synth.regime_sets(0, 0, regime, 4, 512), 512)
+    layer = Layer(0, 0, synth.LayerShape(), 4, bias=bias)
+    L = _fused(layer)
+    _check_layer(layer, L)
+    if union:
+        assert len(set(L.topk_idx.cpu().numpy().reshape(-1).tolist())) == union
+
+
+def test_fused_matches_two_call_routing():
+    say("fused vs two-call")
+    layer = Layer(8, 0, synth.LayerShape(), 4)
+    L = _fused(layer)
+    idx, w = qws.moe_route_topk(layer.x_t, layer.wr_t, 8)
+    assert torch.equal(idx.cpu(), L.topk_idx.cpu())
+    assert torch.equal(w.cpu().view(torch.int32), L.topk_w.cpu().view(torch.int32))
+    _, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, idx, w)
+    assert_close(L.y_f32.cpu().numpy(), y32.cpu().numpy(), tol=1e-6, what="fused vs two-call")
+
+
+def test_fused_deterministic_and_workspace_healthy():
+    say("fused determinism")
+    layer = Layer(9, 0, synth.LayerShape(), 2)
+    ws = qws.moe_layer_workspace(2, 8, 512, 2560, 768, "cuda")
+    a = _fused(layer, ws).y_f32.cpu().numpy()
+    b = _fused(layer, ws).y_f32.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert qws.moe_workspace_errors(ws, 2, 8, 512, 768) == 0
+
+
+def _multi(n, M, seed=30):
+    shape = synth.LayerShape()
+    layers = [Layer(seed, l, shape, M) for l in range(n)]
+    Ls = [qws.MoeLayer(t.x_t, t.wr_t, _bank(t), 8) for t in layers]
+    return layers, Ls, qws.MoeLayers(Ls)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_multi_layer_launch(M):
+    say("multi-layer launch M", M)
+    layers, Ls, seq = _multi(3, M)
+    ws = qws.moe_layer_workspace(M, 8, 512, 2560, 768, "cuda")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    for t, L in zip(layers, Ls):
+        ridx, rw, _ = t.oracle_route()
+        assert np.array_equal(L.topk_idx.cpu().numpy(), ridx)
+        assert_close(L.y_f32.cpu().numpy(), t.oracle_y(ridx, rw), what=f"layer {t.layer}")
+        single = qws.moe_layer_mxfp4(qws.MoeLayer(t.x_t, t.wr_t, _bank(t), 8), workspace=ws)
+        assert np.array_equal(single.y_f32.cpu().numpy().view(np.uint32), L.y_f32.cpu().numpy().view(np.uint32))
+    assert qws.moe_workspace_errors(ws, M, 8, 512, 768) == 0
+
+
+def test_multi_layer_graph_replay():
+    say("multi-layer graph replay")
+    layers, Ls, seq = _multi(4, 1, seed=31)
+    ws = qws.moe_layer_workspace(1, 8, 512, 2560, 768, "cuda")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    ref = [L.y_f32.clone() for L in Ls]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq.run(ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq.run(ws)
+    for i in range(5):
+        for L in Ls:
+            L.y_f32.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for L, r in zip(Ls, ref):
+            assert torch.equal(L.y_f32.view(torch.int32), r.view(torch.int32)), f"replay {i}"
+        seq.run(ws)                                                  # eager work between replays
+        torch.cuda.synchronize()
+    assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 0
+
+
+def test_decode_step_42_layers_sampled():
+    """The full decode step's 42 layers (67.6 GB of seeded MXFP4 banks) in one launch; sampled
+    layers against the oracle, all layers' routing against the oracle's."""
+    say("decode step 42 layers")
+    shape = synth.LayerShape()
+    banks, Ls, xs, wrs = [], [], [], []
+    for l in range(synth.N_LAYERS):
+        bank_t = synth.expert_bank_torch(0, l, shape, device="cuda")
+        banks.append(bank_t)
+        wr = synth.router_weights(0, l, 512)
+        x = synth.token_vectors(0, l, 1)
+        wrs.append(wr)
+        xs.append(x)
+        from .helpers import bf16
+        Ls.append(qws.MoeLayer(bf16(x), bf16(wr), qws.ExpertBank.from_dict(bank_t, 512, True), 8))
+    seq = qws.MoeLayers(Ls)
+    ws = qws.moe_layer_workspace(1, 8, 512, 2560, 768, "cuda")
+    say("decode step: run")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    from oracle import moe as OM
+    for l in range(synth.N_LAYERS):
+        ridx, rw, _ = OM.route(xs[l], wrs[l], 8)
+        assert np.array_equal(Ls[l].topk_idx.cpu().numpy(), ridx), f"layer {l} routing"
+        if l in (0, 17, 41):
+            experts = {e: synth.expert_np(0, l, e, shape) for e in set(ridx.reshape(-1).tolist()) | {512}}
+            ref = OM.moe_layer(xs[l], ridx, rw, experts, 512)
+            assert_close(Ls[l].y_f32.cpu().numpy(), ref, what=f"decode step layer {l}")
+    assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 0
