@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the batch-size-1 MoE decode-step weight stream on one MI355X.
 
-One step = 42 independent full-shape MoE layers (router over 512 experts, top-8 + shared expert,
+One step = 42 chained full-shape MoE layers (router over 512 experts, top-8 + shared expert,
 MXFP4 gate_up/down with SwiGLU, hidden 2560, intermediate 768; each layer with its own seeded
-weights and token vector) followed by the FP8 LM head (157,184 x 2,560), at M = 1 token. Inputs are
-resident in HBM before timing starts. The value is whole-step algorithmic bytes / step time.
+weights; layer 0 reads a seeded token vector and layer l+1 reads layer l's bf16 output) followed
+by the FP8 LM head (157,184 x 2,560), at M = 1 token. Inputs are resident in HBM before timing
+starts. The value is whole-step algorithmic bytes / step time.
 
 The 42 layers of a step run as ONE persistent launch (moe_layers_mxfp4: each layer's router,
-top-K, experts and combine inside one grid, layer l+1 starting after layer l's output is written);
+top-K, experts and combine inside one grid; layer l+1 reads x only once layer l has written it);
 the FP8 head follows on the same stream. HIP events bracket both launches in every timed step,
 which gives the live per-launch duration of the head for the roofline entry.
 
@@ -110,16 +111,17 @@ class MoeLayer:
     """Device-resident inputs and outputs of one MoE layer, runnable through the fused one-launch
     entry point or through the two-call path (router kernel, then the expert kernels)."""
 
-    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None):
+    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None, packed=None, x=None):
         import torch
         import synth
         shape = synth.LayerShape()
         self.bank_t = bank if bank is not None else synth.expert_bank_torch(seed, layer, shape, device=dev)
-        self.bank = qws.ExpertBank.from_dict(self.bank_t, shape.n_routed, True)
+        self.bank = qws.ExpertBank.from_dict(self.bank_t, shape.n_routed, True)       # canonical: two-call path
+        self.packed = packed if packed is not None else qws.moe_pack_mxfp4(self.bank)  # block-major: fused path
         self.wr = _bf16(synth.router_weights(seed, layer, shape.n_routed), dev)
-        self.x = _bf16(synth.token_vectors(seed, layer, M), dev)
+        self.x = x if x is not None else _bf16(synth.token_vectors(seed, layer, M), dev)
         self.bias = None if bias is None else torch.from_numpy(bias).to(dev)
-        self.fused = qws.MoeLayer(self.x, self.wr, self.bank, K_TOP, bias=self.bias, want_f32=False)
+        self.fused = qws.MoeLayer(self.x, self.wr, self.packed, K_TOP, bias=self.bias, want_f32=False)
         self.idx, self.w, self.y = self.fused.topk_idx, self.fused.topk_w, self.fused.y_bf16
         self.M = M
         self.qws = qws
@@ -152,14 +154,18 @@ def probe_ceiling(qws, dev):
 
 # ------------------------------------------------------------------------------------ decode step
 class DecodeStep:
-    """42 MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head."""
+    """42 chained MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head."""
 
-    def __init__(self, qws, M, dev, n_layers, head, banks=None):
+    def __init__(self, qws, M, dev, n_layers, head, banks=None, packed=None):
         import torch
         import synth
         self.qws, self.M, self.dev = qws, M, dev
         log(f"building {n_layers} layers (M={M})")
-        self.layers = [MoeLayer(qws, 0, l, M, dev, bank=None if banks is None else banks[l]) for l in range(n_layers)]
+        self.layers = []
+        for l in range(n_layers):
+            x = self.layers[-1].fused.y_bf16 if self.layers else None     # layer l+1 reads layer l's output
+            self.layers.append(MoeLayer(qws, 0, l, M, dev, bank=None if banks is None else banks[l],
+                                        packed=None if packed is None else packed[l], x=x))
         self.seq = qws.MoeLayers([L.fused for L in self.layers])
         self.ws = qws.moe_layer_workspace(M, K_TOP, 512, 2560, 768, dev)
         self.xh = _bf16(synth.token_vectors(0, 1000, M), dev)
@@ -327,12 +333,13 @@ def main():
         wse1 = qws.expert_workspace(1, K_TOP, 2560, 768, dev)
         lay = {}
         L0 = step.layers[0]
-        lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, bank=L0.bank_t)
+        lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, bank=L0.bank_t, packed=L0.packed)
         bank1 = synth.expert_bank_torch(1, 0, synth.LayerShape(), device=dev)
         lay["moe_layer_m1_seed1_zipf"] = MoeLayer(qws, 1, 0, 1, dev, bias=synth.zipf_bias(1, 0, 512), bank=bank1)
         for reg in synth.REGIMES:
             sets = synth.regime_sets(0, 0, reg, 4, 512)
-            lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), bank=L0.bank_t)
+            lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), bank=L0.bank_t,
+                                                 packed=L0.packed)
         for name, Lr in lay.items():
             t = time_cold(lambda: Lr.run(wsf[Lr.M]), dev, flush=flush)
             u = Lr.union()
@@ -360,7 +367,8 @@ def main():
             breakdown[name] = t
             log(name, t)
         # decode step at M = 4 (natural routing), sharing the M = 1 step's expert banks
-        step4 = DecodeStep(qws, 4, dev, args.layers, head8, banks=[L.bank_t for L in step.layers])
+        step4 = DecodeStep(qws, 4, dev, args.layers, head8, banks=[L.bank_t for L in step.layers],
+                           packed=[L.packed for L in step.layers])
         step4.layers_call()
         torch.cuda.synchronize(dev)
         r4 = step4.timed(max(5, args.steps // 2), 2)
@@ -410,8 +418,8 @@ def main():
            "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "fp32-accumulate (bf16 activations x MXFP4/FP8-dequantised weights)",
            "data": "synthetic: seeded MXFP4 bytes, bf16 N(0,0.02^2) router/head weights, bf16 N(0,1) tokens",
-           "config": {"workload": f"decode step: {args.layers} MoE layers (512 routed + 1 shared, top-8, hidden 2560, "
-                                  "inter 768, MXFP4) + FP8 E4M3 LM head 157184x2560, M=1",
+           "config": {"workload": f"decode step: {args.layers} chained MoE layers (512 routed + 1 shared, top-8, "
+                                  "hidden 2560, inter 768, MXFP4) + FP8 E4M3 LM head 157184x2560, M=1",
                       "layers": args.layers, "M": 1, "bytes_per_step": sb},
            "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
            "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown}

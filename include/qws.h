@@ -49,7 +49,8 @@ enum qws_status {
 enum qws_format {
   QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634, /* e2m1 nibbles + one E8M0 scale per 32 elements */
   QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes + one fp32 scale per row */
-  QWS_FMT_BF16 = 0x42463136                 /* plain bf16 */
+  QWS_FMT_BF16 = 0x42463136,                /* plain bf16 */
+  QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR = 0x4D584642 /* MXFP4 experts, down block-major */
 };
 
 /* Text for a status code. For QWS_ERR_DEVICE the text of the calling thread's last HIP error is
@@ -70,7 +71,8 @@ int qws_selfcheck(qws_stream_t stream);
  * MoE router: logits, top-k, renormalised softmax gate weights.
  *   logits[m, e] = sum_k x[m, k] * w_router[e, k] + bias[m, e]
  *   topk_idx[m, :] = the K largest logits, ordered by (logit descending, expert index
- *                    ascending): ties go to the lower index; -0.0 equals +0.0; NaN ranks lowest.
+ *                    ascending): ties go to the lower index; -0.0 equals +0.0; NaN ranks as
+ *                    -inf (below every other value; ties with -inf by index).
  *   topk_w[m, i]   = exp(l_i - l_max) / sum_j exp(l_j - l_max) over the K selected logits.
  * Each MoE layer routes a token to eight of 512 routed experts plus one shared expert
  * (posts/593 paragraph 2); the score function is not stated on the pages, softmax over the
@@ -103,7 +105,7 @@ int moe_route_topk(const void* x_bf16, int M, int H, const void* w_router_bf16, 
  * kernels compile at run time ..."); element and scale encodings are OCP MX v1.0.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
-  unsigned format; /* must be QWS_FMT_MXFP4_E2M1_E8M0_B32 */
+  unsigned format; /* QWS_FMT_MXFP4_E2M1_E8M0_B32, or ..._DOWN_BLOCKMAJOR after moe_pack_mxfp4 */
   int n_routed;    /* 1 .. 1024 */
   int has_shared;  /* 0 or 1 */
   int hidden;      /* H: multiple of 32, 32 .. 2560 */
@@ -138,12 +140,30 @@ int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
                           qws_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Block-major down projection for the fused entry points (a one-off conversion at load time,
+ * like lmhead_quantize_fp8). The fused layer splits each expert's FFN into blocks of 32
+ * activations; block j needs columns 32j .. 32j+31 of the down projection for every output row,
+ * which this layout stores contiguously:
+ *   down_q_out [n][I/32][H][16] bytes: [e][j][row] = canonical down_q[e][row][16j .. 16j+15]
+ *   down_s_out [n][I/32][H]           : [e][j][row] = canonical down_s[e][row][j]
+ * (n = n_routed + has_shared; the codes themselves are unchanged). desc_out receives `src` with
+ * the down pointers replaced and format QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR; the gate_up
+ * arrays are shared with `src`, which must stay valid. src must be canonical (QWS_ERR_FORMAT
+ * otherwise); down_q_out 16-byte aligned; the outputs must not overlap the inputs.
+ * -------------------------------------------------------------------------------------------*/
+int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* down_q_out, unsigned char* down_s_out,
+                   qws_mxfp4_experts* desc_out, qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * One MoE layer in ONE launch: router GEMV, top-K, softmax, expert union, MXFP4 gate_up + SwiGLU,
  * MXFP4 down + gate-weighted combine with the shared expert -- the same arithmetic as
  * moe_route_topk followed by moe_expert_gemv_mxfp4, without the kernel boundaries between them
  * (each costs ~1.7 us on MI355X, a third of a layer's streaming time at M = 1). The grid is one
- * persistent workgroup per compute unit; its three internal hand-offs use device-coherent stores
- * and arrival counters in the workspace.
+ * persistent workgroup per compute unit. Its hand-offs are 64-bit words that carry a 32-bit value
+ * with a tag unique to (launch, layer, kind), so a reader polls the data itself. Experts must be
+ * packed by moe_pack_mxfp4 (QWS_ERR_FORMAT otherwise). The down projection is summed per block of
+ * 32 activations and then over blocks, so results agree with moe_expert_gemv_mxfp4 to float32
+ * rounding, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   const void* x_bf16;         /* [M, H] bf16, ready before the launch                               */
@@ -159,18 +179,24 @@ typedef struct {
 } qws_moe_layer;
 
 /* Workspace for moe_layer_mxfp4 / moe_layers_mxfp4: ZERO-FILLED before its first use and then
- * reused as is (its arrival counters only increase; nothing needs resetting, so a launch may be
- * captured in a HIP graph and replayed). One workspace per device and stream; calls sharing it
- * must not overlap in time. E <= 1024, H <= 2560, I <= 1024, K <= 8, M <= 4. */
+ * reused as is (counters only increase and tags change per launch; nothing needs resetting, so a
+ * launch may be captured in a HIP graph and replayed; every 2^20 launches the kernel clears the
+ * tagged words itself before the tags repeat). One workspace per device and stream; calls sharing
+ * it must not overlap in time. E <= 1024, H <= 2560, I <= 1024, K <= 8, M <= 4. The size covers
+ * grids of up to 512 compute units. */
 size_t moe_layer_workspace_bytes(int M, int K, int E, int hidden, int inter);
 
 /* One layer; `layer` is host memory. Same contract as the two-call path above. */
 int moe_layer_mxfp4(const qws_moe_layer* layer, int M, int K, void* workspace, size_t workspace_bytes,
                     qws_stream_t stream);
 
-/* n_layers layers in stream order in one launch: layer l+1 starts its x-dependent work only
- * after layer l's output is written. layers_host (host memory) is validated; layers_device must
- * be an identical copy in device memory (read by the kernel for layers 1 .. n_layers-1). */
+/* n_layers (<= 1024) layers in stream order in one launch: layer l+1 starts its x-dependent work
+ * only after layer l's output is written. layers_host (host memory) is validated; layers_device
+ * must be an identical copy in device memory (read by the kernel for layers 1 .. n_layers-1).
+ * When every layer's x_bf16 is the previous layer's y_bf16 (a decode step's chain), layer l+1
+ * reads its x from tagged copies that layer l's row owners publish, with no barrier between the
+ * layers; otherwise the layers are separated by a grid barrier. The results are the same. Weight
+ * loads that do not depend on x (router rows, the shared expert) are issued before x is ready. */
 int moe_layers_mxfp4(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
                      int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream);
 
@@ -237,10 +263,10 @@ int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t strea
 /* Tracing of the fused MoE launches on the current device: while `buf` is registered (device
  * memory, 16-byte aligned), every moe_layer_mxfp4 / moe_layers_mxfp4 launch whose trace fits in
  * `bytes` writes, per layer and workgroup, 16 timestamps of the device wall clock (100 MHz,
- * uint64): [0] layer start, [1] router/shared done, [2] after the first hand-off, [3] top-K and
- * union done, [4] gate_up done, [5] after the second hand-off, [6] activations staged, [7] output
- * written, [8]/[9] first hand-off drained/polled, [10]/[11] second, [12]/[13] layer boundary,
- * [14] top-K done; layout [n_layers][grid][16]. NULL unregisters. Diagnostics only. */
+ * uint64): [0] layer start, [1] x staged, [2] router rows done, [3] shared-expert task done,
+ * [4] top-K chunks done, [5] selection and union done, [6] routed tasks done, [7] partial sums
+ * received (row owners), [8] output written, [9] layer barrier passed (unchained sequences);
+ * layout [n_layers][grid][16]. NULL unregisters. Diagnostics only. */
 int qws_debug_trace_buffer(void* buf, size_t bytes);
 
 /* Streaming-read probe: reads `bytes` (multiple of 16, 16-byte aligned) with 128-bit loads and

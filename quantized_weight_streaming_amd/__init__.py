@@ -6,6 +6,8 @@ if libqws.so is missing, the first call raises (there is no CPU fallback).
 
     route  = moe_route_topk(x, w_router, K)               # router GEMV + top-K + softmax
     y      = moe_expert_gemv_mxfp4(bank, x, idx, w)       # union of experts, SwiGLU, combine
+    packed = moe_pack_mxfp4(bank)                         # block-major down, once per bank
+    layer  = moe_layer_mxfp4(MoeLayer(x, w_router, packed, K))   # the whole layer, one launch
     head   = lmhead_quantize_fp8(w_head_bf16)             # online FP8 head, once
     logits = lmhead_gemv_fp8(head, x)
 """
@@ -17,10 +19,12 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32, LMHeadDesc,  # noqa: F401
-                   MoeLayerDesc, MxFp4Experts, QwsError, check)
+from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32,  # noqa: F401
+                   QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR, LMHeadDesc, MoeLayerDesc, MxFp4Experts, QwsError,
+                   check)
 
-__all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "LMHead", "lmhead_bf16",
+__all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
+           "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "route_workspace", "expert_workspace", "QwsError", "lib"]
@@ -89,34 +93,61 @@ def moe_route_topk(x: torch.Tensor, w_router: torch.Tensor, K: int, bias: torch.
 # ----------------------------------------------------------------------------------- experts
 @dataclass
 class ExpertBank:
-    """MXFP4 experts in the canonical layout (uint8 tensors [n_experts, rows, bytes]); the shared
-    expert, if any, is the last one."""
+    """MXFP4 experts (uint8 tensors); the shared expert, if any, is the last one.
+
+    layout "canonical": gate_up_q [n, 2I, H/2], gate_up_s [n, 2I, H/32], down_q [n, H, I/2],
+    down_s [n, H, I/32] (row-major per expert).
+    layout "down_blockmajor" (from moe_pack_mxfp4): gate_up as above, down_q [n, I/32, H*16],
+    down_s [n, I/32, H] -- block j of the down projection stored contiguously for all rows."""
     gate_up_q: torch.Tensor
     gate_up_s: torch.Tensor
     down_q: torch.Tensor
     down_s: torch.Tensor
     n_routed: int
     has_shared: bool = True
+    layout: str = "canonical"
 
     def __post_init__(self):
         n = self.n_routed + int(self.has_shared)
         two_i, hb = self.gate_up_q.shape[1:]
+        H, I = hb * 2, two_i // 2
+        if self.layout == "canonical":
+            down = (("down_q", self.down_q, (n, H, I // 2)), ("down_s", self.down_s, (n, H, I // 32)))
+            fmt = QWS_FMT_MXFP4_E2M1_E8M0_B32
+        elif self.layout == "down_blockmajor":
+            down = (("down_q", self.down_q, (n, I // 32, H * 16)), ("down_s", self.down_s, (n, I // 32, H)))
+            fmt = QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR
+        else:
+            raise ValueError(f"unknown layout {self.layout!r}")
         for name, t, shape in (("gate_up_q", self.gate_up_q, (n, two_i, hb)),
-                               ("gate_up_s", self.gate_up_s, (n, two_i, hb * 2 // 32)),
-                               ("down_q", self.down_q, (n, hb * 2, two_i // 4)),
-                               ("down_s", self.down_s, (n, hb * 2, two_i // 2 // 32))):
+                               ("gate_up_s", self.gate_up_s, (n, two_i, H // 32))) + down:
             _need(t, name, torch.uint8, 3)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-        self.hidden = hb * 2
-        self.inter = two_i // 2
-        self.desc = MxFp4Experts(QWS_FMT_MXFP4_E2M1_E8M0_B32, self.n_routed, int(self.has_shared), self.hidden,
-                                 self.inter, self.gate_up_q.data_ptr(), self.gate_up_s.data_ptr(),
-                                 self.down_q.data_ptr(), self.down_s.data_ptr())
+        self.hidden = H
+        self.inter = I
+        self.desc = MxFp4Experts(fmt, self.n_routed, int(self.has_shared), self.hidden, self.inter,
+                                 self.gate_up_q.data_ptr(), self.gate_up_s.data_ptr(), self.down_q.data_ptr(),
+                                 self.down_s.data_ptr())
 
     @classmethod
     def from_dict(cls, d: dict, n_routed: int, has_shared: bool = True):
         return cls(d["gate_up_q"], d["gate_up_s"], d["down_q"], d["down_s"], n_routed, has_shared)
+
+
+def moe_pack_mxfp4(bank: ExpertBank) -> ExpertBank:
+    """The bank with its down projection re-laid block-major for the fused entry points (new down
+    tensors; gate_up tensors shared with `bank`)."""
+    if bank.layout != "canonical":
+        raise ValueError("moe_pack_mxfp4 needs a canonical bank")
+    n = bank.n_routed + int(bank.has_shared)
+    dev = bank.down_q.device
+    dq = torch.empty((n, bank.inter // 32, bank.hidden * 16), dtype=torch.uint8, device=dev)
+    ds = torch.empty((n, bank.inter // 32, bank.hidden), dtype=torch.uint8, device=dev)
+    out = MxFp4Experts()
+    st = lib().moe_pack_mxfp4(C.byref(bank.desc), _p(dq), _p(ds), C.byref(out), _stream(dev))
+    check("moe_pack_mxfp4", st)
+    return ExpertBank(bank.gate_up_q, bank.gate_up_s, dq, ds, bank.n_routed, bank.has_shared, "down_blockmajor")
 
 
 def expert_workspace(M: int, K: int, hidden: int, inter: int, device) -> torch.Tensor:
@@ -157,10 +188,13 @@ def moe_layer_workspace(M: int, K: int, E: int, hidden: int, inter: int, device)
 
 
 class MoeLayer:
-    """Tensors and the qws_moe_layer descriptor of one layer for the fused entry points."""
+    """Tensors and the qws_moe_layer descriptor of one layer for the fused entry points. The bank
+    must be packed (moe_pack_mxfp4). Passing the previous layer's y_bf16 as x chains the layers."""
 
     def __init__(self, x, w_router, bank: ExpertBank, K: int, bias=None, y_bf16=None, y_f32=None,
                  topk_idx=None, topk_w=None, logits_out=None, want_bf16=True, want_f32=True):
+        if bank.layout != "down_blockmajor":
+            raise ValueError("the fused entry points need a bank packed by moe_pack_mxfp4")
         _need(x, "x", torch.bfloat16, 2)
         _need(w_router, "w_router", torch.bfloat16, 2)
         M, H = x.shape

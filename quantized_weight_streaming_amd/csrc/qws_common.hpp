@@ -16,7 +16,20 @@ namespace qws {
 constexpr int kWave = 64;
 
 // ------------------------------------------------------------------------------ loads
-__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// Every pointer these helpers take is device (global) memory. The casts state that address space
+// explicitly: a pointer read from a descriptor in memory is otherwise generic, and generic
+// accesses become flat instructions (no scalar base + 32-bit offset form, and they also count
+// against the LDS wait counter).
+#define QWS_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const QWS_GLOBAL u32x4_t*)p; }
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  return *(const QWS_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void stg(T* p, T v) {
+  *(QWS_GLOBAL T*)p = v;
+}
 
 // ------------------------------------------------------------------------------ formats
 // E8M0 byte -> the float32 scale 2^(s-127). Bytes 1..254 are normal float32 exponents; byte 0 is
@@ -90,11 +103,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // a counter, and a reader only issues its loads after it has observed the signal.
 template <typename T>
 __device__ __forceinline__ void st_coherent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((QWS_GLOBAL T*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <typename T>
 __device__ __forceinline__ T ld_coherent(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((QWS_GLOBAL T*)const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }

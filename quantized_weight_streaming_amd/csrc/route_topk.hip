@@ -14,9 +14,10 @@ constexpr int kRouteCpl = 5;            // 16-byte chunks per lane: H <= 64 * 5 
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;
 
-// Order-preserving map float -> uint32 (larger float, larger key); -0 equals +0; NaN lowest.
+// Order-preserving map float -> uint32 (larger float, larger key); -0 equals +0; NaN ranks as
+// -inf (ties with it go to the lower index, as for any equal logits).
 __device__ __forceinline__ uint32_t ordered_key(float f) {
-  if (f != f) return 0u;
+  if (f != f) f = -__builtin_inff();
   if (f == 0.0f) f = 0.0f;
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

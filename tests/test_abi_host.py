@@ -160,8 +160,12 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
         _lib.load(str(tmp_path / "missing.so"))
 
 
+def _packed(**kw):
+    return _bank(**{"format": _lib.QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR, **kw})
+
+
 def _layer_desc(**kw):
-    d = dict(x_bf16=A, w_router_bf16=A, bias=None, bias_row_stride=0, experts=_bank(), topk_idx=A, topk_w=A,
+    d = dict(x_bf16=A, w_router_bf16=A, bias=None, bias_row_stride=0, experts=_packed(), topk_idx=A, topk_w=A,
              logits_out=None, y_bf16=A, y_f32=A)
     d.update(kw)
     return _lib.MoeLayerDesc(**d)
@@ -171,13 +175,14 @@ def _layer_desc(**kw):
     (dict(x_bf16=None), 1, 8, None, _lib.QWS_ERR_ARG),
     (dict(y_bf16=None, y_f32=None), 1, 8, None, _lib.QWS_ERR_ARG),
     (dict(experts=_bank(format=_lib.QWS_FMT_BF16)), 1, 8, None, _lib.QWS_ERR_FORMAT),
-    (dict(experts=_bank(down_q=None)), 1, 8, None, _lib.QWS_ERR_ARG),
+    (dict(experts=_bank()), 1, 8, None, _lib.QWS_ERR_FORMAT),               # canonical: not packed
+    (dict(experts=_packed(down_q=None)), 1, 8, None, _lib.QWS_ERR_ARG),
     ({}, 5, 8, None, _lib.QWS_ERR_SHAPE), ({}, 1, 9, None, _lib.QWS_ERR_SHAPE),
-    (dict(experts=_bank(hidden=2592)), 1, 8, None, _lib.QWS_ERR_SHAPE),
-    (dict(experts=_bank(n_routed=4)), 1, 8, None, _lib.QWS_ERR_SHAPE),       # E < K
+    (dict(experts=_packed(hidden=2592)), 1, 8, None, _lib.QWS_ERR_SHAPE),
+    (dict(experts=_packed(n_routed=4)), 1, 8, None, _lib.QWS_ERR_SHAPE),       # E < K
     (dict(bias=A, bias_row_stride=3), 1, 8, None, _lib.QWS_ERR_SHAPE),
     (dict(x_bf16=MIS), 1, 8, None, _lib.QWS_ERR_ALIGN),
-    (dict(experts=_bank(gate_up_q=MIS)), 1, 8, None, _lib.QWS_ERR_ALIGN),
+    (dict(experts=_packed(gate_up_q=MIS)), 1, 8, None, _lib.QWS_ERR_ALIGN),
     ({}, 1, 8, 64, _lib.QWS_ERR_WORKSPACE),
 ])
 def test_fused_layer_validation(lib, kw, M, K, wsb, status):
@@ -188,12 +193,38 @@ def test_fused_layer_validation(lib, kw, M, K, wsb, status):
 
 def test_fused_layers_validation(lib):
     good = _layer_desc()
-    bad = _layer_desc(experts=_bank(inter=512))                                   # shapes differ across layers
+    bad = _layer_desc(experts=_packed(inter=512))                                 # shapes differ across layers
     arr = (_lib.MoeLayerDesc * 2)(good, bad)
     n = lib.moe_layer_workspace_bytes(1, 8, 512, 2560, 768)
     assert lib.moe_layers_mxfp4(arr, A, 2, 1, 8, A, n, None) == _lib.QWS_ERR_SHAPE
     arr2 = (_lib.MoeLayerDesc * 2)(good, good)
     assert lib.moe_layers_mxfp4(arr2, None, 2, 1, 8, A, n, None) == _lib.QWS_ERR_ARG  # no device copy
     assert lib.moe_layers_mxfp4(arr2, A, 0, 1, 8, A, n, None) == _lib.QWS_ERR_ARG
-    assert lib.moe_layer_workspace_bytes(1, 8, 512, 2560, 768) > 512 * 4 + 9 * 768 * 4
+    # tagged logits, tagged y and the tagged partial sums of M * (K + 1) pairs x I/32 blocks x H rows
+    assert lib.moe_layer_workspace_bytes(1, 8, 512, 2560, 768) >= 512 * 8 + 2560 * 4 + 9 * 24 * 2560 * 8
     assert lib.moe_layer_workspace_bytes(5, 8, 512, 2560, 768) == 0
+    arr3 = (_lib.MoeLayerDesc * 1025)(*([good] * 1025))
+    assert lib.moe_layers_mxfp4(arr3, A, 1025, 1, 8, A, n, None) == _lib.QWS_ERR_SHAPE   # > 1024 layers
+
+
+def test_expert_gemv_refuses_packed_bank(lib):
+    # the two-call path reads the canonical layout only
+    assert _experts(lib, _packed()) == _lib.QWS_ERR_FORMAT
+
+
+def _pack(lib, src=None, qo=A, so=A, out=True):
+    o = _lib.MxFp4Experts()
+    return lib.moe_pack_mxfp4(C.byref(src if src is not None else _bank()), qo, so, C.byref(o) if out else None,
+                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=_packed()), _lib.QWS_ERR_FORMAT), (dict(src=_bank(format=_lib.QWS_FMT_BF16)), _lib.QWS_ERR_FORMAT),
+    (dict(qo=None), _lib.QWS_ERR_ARG), (dict(so=None), _lib.QWS_ERR_ARG), (dict(out=False), _lib.QWS_ERR_ARG),
+    (dict(src=_bank(down_s=None)), _lib.QWS_ERR_ARG), (dict(src=_bank(has_shared=3)), _lib.QWS_ERR_ARG),
+    (dict(src=_bank(n_routed=0)), _lib.QWS_ERR_SHAPE), (dict(src=_bank(hidden=2592)), _lib.QWS_ERR_SHAPE),
+    (dict(src=_bank(inter=48)), _lib.QWS_ERR_SHAPE), (dict(src=_bank(down_q=MIS)), _lib.QWS_ERR_ALIGN),
+    (dict(qo=MIS), _lib.QWS_ERR_ALIGN),
+])
+def test_pack_validation(lib, kw, status):
+    assert _pack(lib, **kw) == status

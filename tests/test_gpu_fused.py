@@ -1,6 +1,7 @@
 """GPU parity of the fused one-launch MoE layer (moe_layer_mxfp4) and of the multi-layer launch
-(moe_layers_mxfp4) against the oracle and against the two-call path; graph replay; the full
-42-layer decode step on sampled layers."""
+(moe_layers_mxfp4) against the oracle and against the two-call path; the block-major pack; chained
+sequences (x of layer l+1 = y of layer l) against an oracle chain; graph replay; the full 42-layer
+decode step."""
 import numpy as np
 import pytest
 import torch
@@ -14,9 +15,15 @@ from .test_gpu_experts import TINY, _assert_bf16_is_rne_of_f32, _bank
 pytestmark = pytest.mark.gpu
 
 
+def _packed(layer: Layer):
+    if not hasattr(layer, "_packed"):
+        layer._packed = qws.moe_pack_mxfp4(_bank(layer))
+    return layer._packed
+
+
 def _fused(layer: Layer, ws=None, logits=True):
     lg = torch.empty((layer.M, layer.shape.n_routed), dtype=torch.float32, device="cuda") if logits else None
-    L = qws.MoeLayer(layer.x_t, layer.wr_t, _bank(layer), layer.shape.topk, bias=layer.bias_t, logits_out=lg)
+    L = qws.MoeLayer(layer.x_t, layer.wr_t, _packed(layer), layer.shape.topk, bias=layer.bias_t, logits_out=lg)
     qws.moe_layer_mxfp4(L, workspace=ws)
     return L
 
@@ -29,6 +36,22 @@ def _check_layer(layer: Layer, L):
     _assert_bf16_is_rne_of_f32(L.y_bf16, L.y_f32)
     assert_close(L.topk_w.cpu().numpy(), rw, tol=1e-5, what="gate weights")
     return e
+
+
+@pytest.mark.parametrize("si", range(len(TINY)))
+def test_pack_is_the_block_major_relayout(si):
+    """moe_pack_mxfp4 moves bytes only: block j of row r of expert e lands at [e][j][r]."""
+    shape = TINY[si]
+    say("pack", shape)
+    layer = Layer(40 + si, 0, shape, 1)
+    pk = _packed(layer)
+    torch.cuda.synchronize()
+    n, H, J = shape.n_routed + int(shape.has_shared), shape.hidden, shape.inter // 32
+    dq = layer.bank_t["down_q"].cpu().numpy().reshape(n, H, J, 16).transpose(0, 2, 1, 3).reshape(n, J, H * 16)
+    ds = layer.bank_t["down_s"].cpu().numpy().reshape(n, H, J).transpose(0, 2, 1)
+    assert np.array_equal(pk.down_q.cpu().numpy(), dq)
+    assert np.array_equal(pk.down_s.cpu().numpy(), ds)
+    assert pk.gate_up_q.data_ptr() == layer.bank_t["gate_up_q"].data_ptr()
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
@@ -71,6 +94,7 @@ def test_fused_matches_two_call_routing():
     assert torch.equal(idx.cpu(), L.topk_idx.cpu())
     assert torch.equal(w.cpu().view(torch.int32), L.topk_w.cpu().view(torch.int32))
     _, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, idx, w)
+    # same arithmetic, different float32 summation order (blocks of 32 activations, then blocks)
     assert_close(L.y_f32.cpu().numpy(), y32.cpu().numpy(), tol=1e-6, what="fused vs two-call")
 
 
@@ -87,7 +111,7 @@ def test_fused_deterministic_and_workspace_healthy():
 def _multi(n, M, seed=30):
     shape = synth.LayerShape()
     layers = [Layer(seed, l, shape, M) for l in range(n)]
-    Ls = [qws.MoeLayer(t.x_t, t.wr_t, _bank(t), 8) for t in layers]
+    Ls = [qws.MoeLayer(t.x_t, t.wr_t, _packed(t), 8) for t in layers]
     return layers, Ls, qws.MoeLayers(Ls)
 
 
@@ -102,7 +126,7 @@ def test_multi_layer_launch(M):
         ridx, rw, _ = t.oracle_route()
         assert np.array_equal(L.topk_idx.cpu().numpy(), ridx)
         assert_close(L.y_f32.cpu().numpy(), t.oracle_y(ridx, rw), what=f"layer {t.layer}")
-        single = qws.moe_layer_mxfp4(qws.MoeLayer(t.x_t, t.wr_t, _bank(t), 8), workspace=ws)
+        single = qws.moe_layer_mxfp4(qws.MoeLayer(t.x_t, t.wr_t, _packed(t), 8), workspace=ws)
         assert np.array_equal(single.y_f32.cpu().numpy().view(np.uint32), L.y_f32.cpu().numpy().view(np.uint32))
     assert qws.moe_workspace_errors(ws, M, 8, 512, 768) == 0
 
@@ -150,7 +174,7 @@ def test_decode_step_42_layers_sampled():
         wrs.append(wr)
         xs.append(x)
         from .helpers import bf16
-        Ls.append(qws.MoeLayer(bf16(x), bf16(wr), qws.ExpertBank.from_dict(bank_t, 512, True), 8))
+        Ls.append(qws.MoeLayer(bf16(x), bf16(wr), qws.moe_pack_mxfp4(qws.ExpertBank.from_dict(bank_t, 512, True)), 8))
     seq = qws.MoeLayers(Ls)
     ws = qws.moe_layer_workspace(1, 8, 512, 2560, 768, "cuda")
     say("decode step: run")
@@ -164,4 +188,93 @@ def test_decode_step_42_layers_sampled():
             experts = {e: synth.expert_np(0, l, e, shape) for e in set(ridx.reshape(-1).tolist()) | {512}}
             ref = OM.moe_layer(xs[l], ridx, rw, experts, 512)
             assert_close(Ls[l].y_f32.cpu().numpy(), ref, what=f"decode step layer {l}")
+    assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 0
+
+
+# ------------------------------------------------------------------------------- chained sequences
+def _chain(n, M, shape, seed):
+    """Layers whose x is the previous layer's y_bf16 (layer 0 from the seeded token vectors)."""
+    layers = [Layer(seed, l, shape, M) for l in range(n)]
+    Ls = []
+    for l, t in enumerate(layers):
+        x = t.x_t if l == 0 else Ls[-1].y_bf16
+        lg = torch.empty((M, shape.n_routed), dtype=torch.float32, device="cuda")
+        Ls.append(qws.MoeLayer(x, t.wr_t, _packed(t), shape.topk, logits_out=lg))
+    return layers, Ls, qws.MoeLayers(Ls)
+
+
+def _oracle_chain_check(layers, Ls):
+    """Each layer against the oracle run as its own chain (x_{l+1} = bf16 RNE of the oracle's y_l).
+    Routing must agree up to near-ties; after a layer whose routing needed the near-tie allowance,
+    the two chains legitimately part and later layers are not compared. Returns layers compared."""
+    x = layers[0].x
+    compared = 0
+    for t, L in zip(layers, Ls):
+        t.x = x                                            # the oracle chain's own input
+        ridx, rw, rlg = t.oracle_route()
+        near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, t.shape.topk)
+        if near:
+            break
+        y = t.oracle_y(ridx, rw)
+        assert_close(L.y_f32.cpu().numpy(), y, what=f"chained layer {t.layer} M={t.M}")
+        compared += 1
+        x = synth.f32_to_bf16_bits(y.astype(np.float32))
+    return compared
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_chained_sequence_vs_oracle_chain(M):
+    say("chained sequence M", M)
+    layers, Ls, seq = _chain(4, M, synth.LayerShape(), seed=50 + M)
+    ws = qws.moe_layer_workspace(M, 8, 512, 2560, 768, "cuda")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    assert qws.moe_workspace_errors(ws, M, 8, 512, 768) == 0
+    assert _oracle_chain_check(layers, Ls) >= 1
+
+
+@pytest.mark.parametrize("M,shape", [(1, synth.LayerShape()), (4, synth.LayerShape()), (2, TINY[1])])
+def test_chained_sequence_matches_layer_by_layer(M, shape):
+    """The barrier-free chained launch equals launching the layers one by one, bit for bit."""
+    say("chained vs single M", M, shape)
+    layers, Ls, seq = _chain(3, M, shape, seed=60 + M)
+    ws = qws.moe_layer_workspace(M, shape.topk, shape.n_routed, shape.hidden, shape.inter, "cuda")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    chained = [(L.y_f32.clone(), L.topk_idx.clone()) for L in Ls]
+    for L in Ls:                                           # x of layer l is y_bf16 of layer l-1
+        qws.moe_layer_mxfp4(L, workspace=ws)
+    torch.cuda.synchronize()
+    for l, (L, (y, idx)) in enumerate(zip(Ls, chained)):
+        assert torch.equal(idx, L.topk_idx), f"layer {l} routing"
+        assert torch.equal(y.view(torch.int32), L.y_f32.view(torch.int32)), f"layer {l} output"
+    assert qws.moe_workspace_errors(ws, M, shape.topk, shape.n_routed, shape.inter) == 0
+
+
+def test_chained_graph_replay():
+    say("chained graph replay")
+    layers, Ls, seq = _chain(4, 1, synth.LayerShape(), seed=70)
+    ws = qws.moe_layer_workspace(1, 8, 512, 2560, 768, "cuda")
+    seq.run(ws)
+    torch.cuda.synchronize()
+    ref = [L.y_f32.clone() for L in Ls]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq.run(ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq.run(ws)
+    for i in range(5):
+        for L in Ls:
+            L.y_f32.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for L, r in zip(Ls, ref):
+            assert torch.equal(L.y_f32.view(torch.int32), r.view(torch.int32)), f"replay {i}"
+        seq.run(ws)
+        torch.cuda.synchronize()
     assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 0
