@@ -264,9 +264,11 @@ int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t strea
  * memory, 16-byte aligned), every moe_layer_mxfp4 / moe_layers_mxfp4 launch whose trace fits in
  * `bytes` writes, per layer and workgroup, 16 timestamps of the device wall clock (100 MHz,
  * uint64): [0] layer start, [1] x staged, [2] router rows done, [3] shared-expert task done,
- * [4] top-K chunks done, [5] selection and union done, [6] routed tasks done, [7] partial sums
- * received (row owners), [8] output written, [9] layer barrier passed (unchained sequences);
- * layout [n_layers][grid][16]. NULL unregisters. Diagnostics only. */
+ * [4] logits received, [10] wave maxima shared, [11] selection candidates gathered, [12] ranks
+ * done, [5] selection and union done, [6] routed tasks done, [7] partial sums received (row
+ * owners), [13] row sums done, [8] output written, [14] layer-end stores acknowledged, [9] layer
+ * barrier passed (sequences that are not chained); layout [n_layers][grid][16]. NULL unregisters.
+ * Diagnostics only. */
 int qws_debug_trace_buffer(void* buf, size_t bytes);
 
 /* Streaming-read probe: reads `bytes` (multiple of 16, 16-byte aligned) with 128-bit loads and

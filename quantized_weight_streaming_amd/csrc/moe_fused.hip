@@ -12,24 +12,29 @@
 // block j of expert id(u), plus the 32-column block j of that expert's down projection for all H
 // output rows. One workgroup issues all of a task's loads in one burst (2 x 32 x H/2 gate/up bytes
 // + H x 16 down bytes: 120 KB of codes at H = 2560), computes the block's 32 activations itself --
-// activations never cross workgroups -- and writes H partial sums per token. The down projection
-// is stored block-major (moe_pack_mxfp4) so that block j of an expert is one contiguous stream.
+// activations never cross workgroups -- and writes H partial sums per token, already multiplied by
+// the token's gate weight. The down projection is stored block-major (moe_pack_mxfp4) so that
+// block j of an expert is one contiguous stream. Weights are read with non-temporal loads: each
+// byte is used once per step, and on MI355X a burst of such loads streams ~2x faster than cached
+// loads when the caches hold dirty lines.
 //
 // Hand-offs between workgroups carry their own validity: a 64-bit word holds a 32-bit value and a
 // 32-bit tag unique to (launch, layer, kind), written with one device-coherent store and polled
 // with device-coherent loads (64-bit accesses are single-copy atomic), so a reader needs no
-// separate signal, fence or counter. Per layer:
-//   1  this workgroup's router rows are loaded (they need no x), then x into LDS: layer 0 from the
-//      caller's buffer; in a chained sequence (x of layer l+1 is y of layer l) from the tagged copy
-//      of y the previous layer published.
-//   2  router dots -> tagged logits; workgroups G-J .. G-1 run the shared expert's J tasks (they
-//      need no routing) -> tagged partials.
-//   3  every workgroup selects top-K itself from the tagged logits: 8 waves take 64-expert chunks
-//      (one logit per lane, K rounds of DPP max + lowest lane), one wave per token merges the chunk
-//      candidates; softmax; union of the window's selections in LDS.
+// separate signal, fence or counter; a poll reloads only the words that are not yet valid. Per
+// layer:
+//   1  x into LDS: layer 0 from the caller's buffer; in a chained sequence (x of layer l+1 is y of
+//      layer l) from the tagged copy of y the previous layer published.
+//   2  router dots of this workgroup's rows (prefetched into LDS during the previous layer) ->
+//      tagged logits; workgroups G-J .. G-1 then run the shared expert's J tasks (they need no
+//      routing).
+//   3  every workgroup selects top-K itself from the tagged logits, in parallel: a threshold from
+//      the per-wave maxima leaves a few candidates, each of which counts the candidates that beat
+//      it (logit descending, index ascending) to find its rank; softmax over the selected; union of
+//      the window's selections (first-occurrence order).
 //   4  routed tasks, round-robin over workgroups (at M = 1 one task per workgroup).
-//   5  workgroup b owns output rows [b*R, b*R + R): it polls their tagged partials, adds blocks then
-//      slots in a fixed order (deterministic), writes y and, in a chained sequence, a tagged copy.
+//   5  workgroup b owns output rows [b*R, b*R + R): it polls their tagged partial sums, sums them in
+//      a fixed order (deterministic), writes y and, in a chained sequence, a tagged copy.
 // Layers that are not chained are separated by a counter barrier instead.
 #include "qws_common.hpp"
 
@@ -44,23 +49,26 @@ constexpr int kMaxK = 8;
 constexpr int kMaxSlots = kMaxM * kMaxK + 1;    // routed union + shared
 constexpr int kMaxPairs = kMaxM * (kMaxK + 1);  // (slot, token) pairs
 constexpr int kMaxE = 1024;
-constexpr int kMaxChunks = kMaxE / kWave;
+constexpr int kEpt = kMaxE / kThreads;          // experts per thread in the selection
 constexpr int kHMax = 2560;
 constexpr int kIMax = 1024;
 constexpr int kBlk = 32;        // activations per task: one MX block of the down projection
 constexpr int kGuCpl = 5;       // 16-byte chunks per lane of a gate/up row: H <= 16 * 5 * 32
-constexpr int kRtCpl = 5;       // router row: H <= 64 * 5 * 8
+constexpr int kRtCpl = 5;       // 16-byte chunks per lane of a router row: H <= 64 * 5 * 8
 constexpr int kDnRpl = 5;       // down rows per thread in a task: H <= 512 * 5
 constexpr int kMaxRows = 16;    // output rows owned by one workgroup
 constexpr int kMaxGrid = 512;
 constexpr int kRowsPad = 2 * kMaxGrid;   // partial buffer rows allowed beyond H (G * R >= H)
-constexpr int kPollBatch = 12;  // tagged words per thread in flight while polling partials
+constexpr int kPollBatch = 12;  // tagged words per thread in flight while reading partials
+constexpr int kSumLanes = 8;    // lanes that share the sum of one (token, row) in the combine
 constexpr int kSyncCounters = 16;
 constexpr int kSyncStride = 16;             // 64-bit words: 128 bytes apart
 constexpr unsigned kSpinLimit = 1u << 20;   // polls before a wait gives up (~1 s)
 constexpr int kTracePoints = 16;            // timestamps per (layer, workgroup) when tracing
 constexpr int kTagsPerLaunch = 4096;        // tag space of one launch: 4 per layer
 constexpr int kMaxLayers = kTagsPerLaunch / 4;
+constexpr int kDescWords = sizeof(qws_moe_layer) / 8;
+static_assert(sizeof(qws_moe_layer) % 8 == 0 && kDescWords <= kWave, "descriptor copy");
 
 struct Layer {
   const uint16_t* x;
@@ -90,6 +98,7 @@ struct Shape {
   int P;        // (slot, token) pairs the partial buffer holds per block: M * (K + 1)
   int chained;  // x of layer l+1 is y (bf16) of layer l, for every l
   int rows_total;  // G * R: rows of the partial buffer, H and padding
+  int nrw;      // router rows per workgroup (one wave each)
 };
 
 struct Work {
@@ -99,16 +108,20 @@ struct Work {
   unsigned* errors;              // count of bounded waits that timed out (sticky)
   unsigned long long* logits;    // [M][E] tagged logits
   unsigned long long* ytag;      // [M][H/2] tagged bf16 pairs of y (chained sequences)
-  unsigned long long* partial;   // [G][P][J][R] tagged partial sums of the down projection
+  unsigned long long* done;      // [G] tagged "layer finished" words (layers that are not chained)
+  unsigned long long* partial;   // [G][P][J][R] tagged, gate-weighted partial sums of the down projection
 };
 
+// Routing of the current layer, shared by the workgroup (LDS).
 struct Union {
-  int n;                       // slots: 0 = shared (if any), then routed ids ascending
+  int n;                         // slots: 0 = shared (if any), then routed ids in first-occurrence order
   int id[kMaxSlots];
-  unsigned mask[kMaxSlots];    // tokens using the slot
-  int pair0[kMaxSlots];        // first (slot, token) pair index of the slot
-  float w[kMaxSlots][kMaxM];   // gate weight of (slot, token)
+  unsigned mask[kMaxSlots];      // tokens using the slot
+  int pair0[kMaxSlots];          // first (slot, token) pair index of the slot
+  float w[kMaxSlots][kMaxM];     // gate weight of (slot, token)
   int n_pairs;
+  int tok_n[kMaxM];              // pairs of each token, in slot order
+  int tok_pair[kMaxM][kMaxSlots];
 };
 
 __device__ __forceinline__ void stamp(const Work& w, int l, int k) {
@@ -137,33 +150,34 @@ __device__ __forceinline__ bool wait_expired(const Work& w, unsigned& spins) {
   return false;
 }
 
-// Reloads word Q .. N-1 of a poll, keeping those that already carry `tag` (compile-time recursion
-// rather than a loop: the loop form was not unrolled inside the wait loop, which put v in scratch).
+// Reloads the words Q .. N-1 of a poll that do not carry `tag` yet (compile-time recursion rather
+// than a loop: a loop inside the wait loop was not unrolled, which put v in scratch memory).
 template <int Q, int N>
-__device__ __forceinline__ void reload_tagged(const unsigned long long* src, int i0, int stride, int n, uint32_t tag,
-                                              unsigned long long (&v)[N]) {
+__device__ __forceinline__ void reload_missing(const unsigned long long* src, const int (&idx)[N], uint32_t tag,
+                                               unsigned long long (&v)[N]) {
   if constexpr (Q < N) {
-    const unsigned long long nv = ld_coherent(src + min(i0 + Q * stride, n - 1));
-    v[Q] = tag_of(v[Q]) == tag ? v[Q] : nv;
-    reload_tagged<Q + 1, N>(src, i0, stride, n, tag, v);
+    if (tag_of(v[Q]) != tag) v[Q] = ld_coherent(src + idx[Q]);
+    reload_missing<Q + 1, N>(src, idx, tag, v);
   }
 }
+template <int Q, int N>
+__device__ __forceinline__ bool all_tagged(const unsigned long long (&v)[N], uint32_t tag) {
+  if constexpr (Q < N) return tag_of(v[Q]) == tag && all_tagged<Q + 1, N>(v, tag);
+  else return true;
+}
 
-// Loads src[i0 + q * stride] (clamped to n - 1) for q < N and waits until each carries `tag`.
-// Every lane of the wave must call it (the wait is wave-wide).
+// Loads src[idx[q]] for q < N (idx < 0: no load, the word counts as valid) and waits until each
+// carries `tag`, reloading only the words that do not yet. Every lane of the wave must call it
+// (the wait is wave-wide).
 template <int N>
-__device__ __forceinline__ void poll_tagged(const Work& w, const unsigned long long* src, int i0, int stride, int n,
+__device__ __forceinline__ void poll_tagged(const Work& w, const unsigned long long* src, const int (&idx)[N],
                                             uint32_t tag, unsigned long long (&v)[N]) {
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = ld_coherent(src + min(i0 + q * stride, n - 1));
+  for (int q = 0; q < N; ++q) v[q] = idx[q] >= 0 ? ld_coherent(src + idx[q]) : tagged(tag, 0u);
   unsigned spins = 0;
-  while (true) {
-    bool ok = true;
-#pragma unroll
-    for (int q = 0; q < N; ++q) ok = ok && tag_of(v[q]) == tag;
-    if (__all(ok)) break;
+  while (!__all(all_tagged<0, N>(v, tag))) {
     if (wait_expired(w, spins)) break;
-    reload_tagged<0, N>(src, i0, stride, n, tag, v);
+    reload_missing<0, N>(src, idx, tag, v);
   }
 }
 
@@ -207,34 +221,27 @@ __device__ void grid_sync(const Work& w, SyncState& st) {
   __syncthreads();
 }
 
-// ------------------------------------------------------------------------------ DPP reductions
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-// Wave-uniform max / min of a uint32 across 64 lanes: quad xor-1, xor-2, half-row and row mirrors
-// leave each 16-lane row with its extreme in every lane; four readlanes finish it.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp<0xB1>(v));
-  v = max(v, dpp<0x4E>(v));
-  v = max(v, dpp<0x141>(v));
-  v = max(v, dpp<0x140>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp<0xB1>(v));
-  v = min(v, dpp<0x4E>(v));
-  v = min(v, dpp<0x141>(v));
-  v = min(v, dpp<0x140>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return min(min(a, b), min(c, d));
+// Between layers that are not chained: every workgroup publishes a tagged word once all of its
+// stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
+// round trip to a counter before the wait starts.
+__device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l) {
+  wait_mem();
+  __syncthreads();
+  stamp(w, l, 14);
+  if (tid == 0) st_coherent(w.done + blockIdx.x, tagged(tag, 0u));
+  if (tid < kWave) {
+    constexpr int kPer = kMaxGrid / kWave;
+    int idx[kPer];
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) idx[q] = tid + q * kWave < (int)gridDim.x ? tid + q * kWave : -1;
+    poll_tagged<kPer>(w, w.done, idx, tag, v);
+  }
+  __syncthreads();
 }
 
 // Selection key: order-preserving float -> uint32 (larger float, larger key; -0 == +0; NaN ranks
-// as -inf). Every logit maps to >= 0x007fffff; 0 marks a taken or absent entry.
+// as -inf). Every logit maps to >= 0x007fffff; 0 marks an absent entry.
 __device__ __forceinline__ uint32_t sel_key(float f) {
   if (f != f) f = -__builtin_inff();
   if (f == 0.0f) f = 0.0f;
@@ -243,6 +250,18 @@ __device__ __forceinline__ uint32_t sel_key(float f) {
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Total order of the selection: larger key first, then lower expert index.
+__device__ __forceinline__ unsigned long long rank_key(uint32_t key, int e) {
+  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+}
+
+// Non-temporal 16-byte load of weights that are read once per step.
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);
+}
+__device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load((const QWS_GLOBAL uint8_t*)p);
 }
 
 // ------------------------------------------------------------------------------ tasks
@@ -253,8 +272,6 @@ struct TaskRegs {
 
 // Issues the loads of task (expert e, block j). 16-lane group g of the workgroup takes gate row
 // 32j+g and up row I+32j+g (lane j16: chunks j16, j16+16, ...); thread t takes down rows t, t+512, ...
-// Addresses are a wave-uniform 64-bit base plus a 32-bit per-thread offset, so that the per-thread
-// part stays one register across the layer loop.
 __device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r) {
   const unsigned g = tid >> 4, j16 = tid & 15;
   const int H = sh.H, I = sh.I, J = I / kBlk;
@@ -266,14 +283,14 @@ __device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e
   const uint8_t* us = gs + (size_t)I * nch;
   // unconditional loads from clamped (in-bounds) addresses: no branch around a load, so a task's
   // loads issue back to back. A chunk past the row end is loaded from the last chunk and skipped
-  // by the compute; a down row past H is loaded from row H-1 and its partial sum is zeroed.
+  // by the compute; a down row past H is loaded from row H-1 and its partial sum is not stored.
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
     const unsigned c = min(j16 + 16u * t, nch - 1);
-    r.g[t] = ld16(gq + g * rb + c * 16u);
-    r.u[t] = ld16(uq + g * rb + c * 16u);
-    r.gs[t] = ldg(gs + g * nch + c);
-    r.us[t] = ldg(us + g * nch + c);
+    r.g[t] = ld16_stream(gq + g * rb + c * 16u);
+    r.u[t] = ld16_stream(uq + g * rb + c * 16u);
+    r.gs[t] = ldb_stream(gs + g * nch + c);
+    r.us[t] = ldb_stream(us + g * nch + c);
   }
   const size_t blk = ((size_t)e * J + j) * (size_t)H;
   const uint8_t* dq = L.dq + blk * 16;
@@ -281,20 +298,23 @@ __device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e
 #pragma unroll
   for (int t = 0; t < kDnRpl; ++t) {
     const unsigned row = min(tid + (unsigned)(kThreads * t), (unsigned)H - 1);
-    r.d[t] = ld16(dq + row * 16u);
-    r.ds[t] = ldg(ds + row);
+    r.d[t] = ld16_stream(dq + row * 16u);
+    r.ds[t] = ldb_stream(ds + row);
   }
 }
 
-// Computes task (block j, tokens in `mask`, pairs p0 + rank) from its loaded registers: the block's
-// activations silu(gate) * up into LDS, then partial[p][j][row] = sum_k W_down[row][32j+k] * a[k]
-// for every row, stored tagged at this thread's row offsets.
+// Computes task (slot u: tokens in un.mask[u], pairs un.pair0[u] + rank, gate weights un.w[u][m],
+// block j) from its loaded registers: the block's activations silu(gate) * up into LDS, then
+// partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every row, stored tagged at this
+// thread's row offsets in the owners' regions.
 template <int M>
-__device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, const TaskRegs& r, unsigned mask,
-                                             int p0, int j, const uint16_t* xs, float* a_s, unsigned tid,
+__device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, const TaskRegs& r, const Union& un,
+                                             int u, int j, const uint16_t* xs, float* a_s, unsigned tid,
                                              uint32_t tag) {
   const int g = tid >> 4, j16 = tid & 15;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
+  const unsigned mask = un.mask[u];
+  const int p0 = un.pair0[u];
   float ag[M], au[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) ag[m] = au[m] = 0.0f;
@@ -337,11 +357,18 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float hg = group_sum<16>(ag[m]);
-    const float hu = group_sum<16>(au[m]);
+    const float hg = row16_sum(ag[m]);
+    const float hu = row16_sum(au[m]);
     if (j16 == 0) a_s[m * kBlk + g] = silu(hg) * hu;
   }
   __syncthreads();
+  float wt[M];
+  int pm[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    wt[m] = un.w[u][m];
+    pm[m] = p0 + __popc(mask & ((1u << m) - 1u));
+  }
 #pragma unroll
   for (int t = 0; t < kDnRpl; ++t) {
     const int row = tid + kThreads * t;
@@ -360,7 +387,6 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       if ((mask >> m) & 1u) {
-        const int p = p0 + __popc(mask & ((1u << m) - 1u));
         const float4* ap = reinterpret_cast<const float4*>(a_s + m * kBlk);
         float s = 0.0f;
 #pragma unroll
@@ -372,15 +398,211 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
           s = fmaf(wf[4 * q + 3], a4.w, s);
         }
         // rows H .. G*R-1 (zero weights) pad the last owner's region so that it is written whole
-        if (row >= H) s = 0.0f;
-        if (row < sh.rows_total) st_coherent(w.partial + (size_t)(p * J + j) * R + rowoff, tagged(tag, __float_as_uint(s)));
+        s = row < H ? wt[m] * s : 0.0f;
+        if (row < sh.rows_total)
+          st_coherent(w.partial + (size_t)(pm[m] * J + j) * R + rowoff, tagged(tag, __float_as_uint(s)));
       }
     }
   }
   __syncthreads();  // a_s is rewritten by the next task
 }
 
+// ------------------------------------------------------------------------------ top-K + union
+// Every workgroup selects the top-K of each token from the tagged logits (same result in every
+// workgroup). Thread t holds experts t + 512 i. A candidate must reach T = the smallest of the
+// per-wave maxima when at least K waves hold experts (then >= K logits reach T, so every one of
+// the top K does); otherwise T admits every expert. Each candidate's rank is the number of
+// candidates that beat it; ranks < K are the selection, in order.
+template <int M>
+__device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint32_t tag, int tid, int wave, int lane,
+                                            unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
+                                            float (*s_w)[kMaxK], uint32_t (*s_wmax)[kWaves],
+                                            int (*s_cnt)[kEpt][kWaves], uint32_t (*s_sel)[kMaxK], int l) {
+  const int E = sh.E, K = sh.K;
+  uint32_t key[M][kEpt];
+  {
+    int idx[M * kEpt];
+    unsigned long long v[M * kEpt];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const int e = tid + kThreads * i;
+        idx[m * kEpt + i] = e < E ? m * E + e : -1;
+      }
+    poll_tagged<M * kEpt>(w, w.logits, idx, tag, v);
+    stamp(w, l, 4);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i)
+        key[m][i] = idx[m * kEpt + i] >= 0 ? sel_key(__uint_as_float((uint32_t)v[m * kEpt + i])) : 0u;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t k = key[m][0];
+#pragma unroll
+    for (int i = 1; i < kEpt; ++i) k = max(k, key[m][i]);
+    const uint32_t wm = wave_max_u32(k);
+    if (lane == 0) s_wmax[m][wave] = wm;
+  }
+  __syncthreads();
+  stamp(w, l, 10);
+  // waves holding at least one expert: wave v holds experts v*64 .. v*64+63 (+ 512 i)
+  const int nvw = min(kWaves, (E + kWave - 1) / kWave);
+  bool cf[M][kEpt];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t T = 0u;
+    if (nvw >= K) {
+      T = 0xffffffffu;
+      for (int v = 0; v < nvw; ++v) T = min(T, s_wmax[m][v]);
+    }
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) {
+      cf[m][i] = key[m][i] != 0u && key[m][i] >= T;
+      const unsigned long long b = __ballot(cf[m][i]);
+      if (lane == 0) s_cnt[m][i][wave] = __popcll(b);
+    }
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int ncand[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    // candidate order in the buffer: (i, wave, lane); any order would do, ranks are counted
+    int pos[kEpt], total = 0;
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) {
+      pos[i] = total;
+      for (int v = 0; v < kWaves; ++v) {
+        const int c = s_cnt[m][i][v];
+        pos[i] += v < wave ? c : 0;
+        total += c;
+      }
+    }
+    ncand[m] = total;
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) {
+      const unsigned long long bl = __ballot(cf[m][i]);
+      if (cf[m][i]) cand[m * E + pos[i] + __popcll(bl & lt)] = rank_key(key[m][i], tid + kThreads * i);
+    }
+  }
+  __syncthreads();
+  stamp(w, l, 11);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) {
+      if (cf[m][i]) {
+        const unsigned long long mine = rank_key(key[m][i], tid + kThreads * i);
+        const unsigned long long* cm = cand + m * E;
+        int rank = 0;
+        for (int q = 0; q < ncand[m] && rank < K; ++q) rank += cm[q] > mine ? 1 : 0;
+        if (rank < K) {
+          s_idx[m][rank] = tid + kThreads * i;
+          s_sel[m][rank] = key[m][i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  stamp(w, l, 12);
+  if (wave == 0) {
+    // softmax over the selected logits of each token: lane l is selection (l / K, l % K); every
+    // lane of a token sums the same terms in the same order
+    const int n = M * K;
+    const int mj = lane < n ? lane / K : 0, rj = lane - mj * K;
+    const float z = lane < n ? expf(key_to_float(s_sel[mj][rj]) - key_to_float(s_sel[mj][0])) : 0.0f;
+    float s = 0.0f;   // sum of the token's K terms in rank order, the same in each of its lanes
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float sm = 0.0f;
+      for (int r = 0; r < K; ++r) sm += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), m * K + r));
+      s = m == mj ? sm : s;
+    }
+    float wj = 0.0f;
+    int e = -1;
+    if (lane < n) {
+      wj = z / s;
+      e = s_idx[mj][rj];
+      s_w[mj][rj] = wj;
+    }
+    // union in first-occurrence order over (token, rank); slot 0 is the shared expert (if any)
+    const int ns = sh.has_shared ? 1 : 0;
+    bool first = lane < n;
+    unsigned mask = 0;
+    float wsum[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
+    for (int i = 0; i < n; ++i) {
+      const int ei = __builtin_amdgcn_readlane(e, i);
+      const int mi = i / K;
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i));
+      if (ei == e) {
+        if (i < lane) first = false;
+        mask |= 1u << mi;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          if (m == mi) wsum[m] += wi;
+      }
+    }
+    const unsigned long long firsts = __ballot(first);
+    const int cnt = first ? __popc(mask) : 0;
+    int pair0 = ns * M;
+    for (int i = 0; i < n; ++i) {
+      const int ci = __builtin_amdgcn_readlane(cnt, i);
+      pair0 += i < lane ? ci : 0;
+    }
+    const int slot = ns + __popcll(firsts & lt);
+    if (first) {
+      un.id[slot] = e;
+      un.mask[slot] = mask;
+      un.pair0[slot] = pair0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) un.w[slot][m] = wsum[m];
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const unsigned long long bm = __ballot(first && ((mask >> m) & 1u));
+      if (first && ((mask >> m) & 1u)) un.tok_pair[m][ns + __popcll(bm & lt)] = pair0 + __popc(mask & ((1u << m) - 1u));
+      if (lane == 0) {
+        un.tok_n[m] = ns + __popcll(bm);
+        if (ns) un.tok_pair[m][0] = m;
+      }
+    }
+    if (lane == 0) {
+      if (ns) {
+        un.id[0] = E;
+        un.mask[0] = (1u << M) - 1u;
+        un.pair0[0] = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
+      }
+      int total = ns * M;
+      for (int i = 0; i < n; ++i) total += __builtin_amdgcn_readlane(cnt, i);
+      un.n = __popcll(firsts) + ns;
+      un.n_pairs = total;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ the kernel
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+// A layer descriptor copied into LDS (raw words of a qws_moe_layer), read as wave-uniform values.
+__device__ __forceinline__ Layer desc_from_lds(const unsigned long long* raw) {
+  unsigned long long v[kDescWords];
+#pragma unroll
+  for (int i = 0; i < kDescWords; ++i) v[i] = uniform_u64(raw[i]);
+  qws_moe_layer d;
+  __builtin_memcpy(&d, v, sizeof(d));
+  return to_layer(d);
+}
+
 template <int M>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
                                                               int n_layers, Shape sh, Work w) {
@@ -388,28 +610,35 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   __shared__ Union un;
   __shared__ int s_idx[kMaxM][kMaxK];
   __shared__ float s_w[kMaxM][kMaxK];
-  __shared__ uint32_t s_ck[kMaxM][kMaxChunks][kMaxK];   // chunk candidates: key
-  __shared__ int s_ci[kMaxM][kMaxChunks][kMaxK];        // chunk candidates: expert index
+  __shared__ uint32_t s_sel[kMaxM][kMaxK];
+  __shared__ uint32_t s_wmax[kMaxM][kWaves];
+  __shared__ int s_cnt[kMaxM][kEpt][kWaves];
   __shared__ __attribute__((aligned(16))) float a_s[kMaxM * kBlk];
-  __shared__ float s_red2[kMaxPairs][kMaxRows];
+  __shared__ float s_y[kMaxM][kMaxRows];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_desc[2][kDescWords];
   __shared__ unsigned long long s_launch;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
   const int G = gridDim.x, b = blockIdx.x;
-  const int E = sh.E, K = sh.K, H = sh.H, I = sh.I, R = sh.R, P = sh.P;
+  const int E = sh.E, H = sh.H, I = sh.I, R = sh.R;
   const int J = I / kBlk;
   const int ns = sh.has_shared ? 1 : 0;
 
-  // dynamic LDS: x [M][H] bf16 | partial sums of this workgroup's rows [pairs][J][R] fp32
+  // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates
+  // [M][E] u64, later this workgroup's partial sums [pairs][J][R] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-  float* red = reinterpret_cast<float*>(lds + (size_t)M * H * 2);
+  uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
+  unsigned char* scratch = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(scratch);
+  float* red = reinterpret_cast<float*>(scratch);
 
-  const int nrw = (E + G - 1) / G;   // router rows (waves) per workgroup
   const int row0 = b * R;
   const int my_rows = max(0, min(R, H - row0));
-  const int nchunks = (E + kWave - 1) / kWave;
   const bool shared_task = sh.has_shared && b >= G - J;
+  const int r_row = b + G * wave;                       // this wave's router row
+  const bool is_router = wave < sh.nrw && r_row < E;
   SyncState sync{0ull, false};
 
   // launch number -> this launch's tag base (every workgroup adds 1 per launch)
@@ -419,35 +648,44 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const uint32_t tag_base = (uint32_t)(s_launch * kTagsPerLaunch);
   if (s_launch > 0 && tag_base == 0) {
     // tags repeat from here on: clear every tagged word (tag 0 is never valid) before any use
-    const size_t own = (size_t)P * J * R;
+    const size_t own = (size_t)sh.P * J * R;
     for (size_t i = tid; i < own; i += kThreads) st_coherent(w.partial + (size_t)b * own + i, 0ull);
     for (int i = b * kThreads + tid; i < M * E; i += G * kThreads) st_coherent(w.logits + i, 0ull);
     for (int i = b * kThreads + tid; i < M * H / 2; i += G * kThreads) st_coherent(w.ytag + i, 0ull);
+    if (tid == 0) st_coherent(w.done + b, 0ull);
     grid_sync(w, sync);
   }
 
+  // router rows of layer 0 -> LDS (asynchronous; this wave waits for them before its dots)
+  if (is_router) {
+    const uint16_t* row = first.wr + (size_t)r_row * H;
+    for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
+      if (c0 + lane < (H >> 3))
+        __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
+                                         (__attribute__((address_space(3))) void*)(wr_s + (size_t)wave * H + c0 * 8),
+                                         16, 0, 0);
+  }
+
   for (int l = 0; l < n_layers; ++l) {
-    const Layer L = l == 0 ? first : to_layer(rest[l]);
     // an opaque copy of the thread index per layer: addresses derived from it are recomputed where
     // they are used instead of being hoisted out of the layer loop and kept live (spilled) across it
     unsigned tid_l = threadIdx.x;
     asm volatile("" : "+v"(tid_l));
-    const int tid = (int)tid_l, lane = tid % kWave;   // shadows the kernel-level index in this layer
+    const int tid = (int)tid_l, lane = tid % kWave;   // shadow the kernel-level indices in this layer
+    // descriptor of layer l: layer 0 from the kernel arguments, later ones from the LDS copy made
+    // during the previous layer
+    Layer L = first;
+    if (l > 0) L = desc_from_lds(s_desc[l & 1]);
     // tags never 0: a zero-filled workspace holds tag 0
     const uint32_t tag_lg = tag_base + 4u * (uint32_t)l + 1u, tag_pt = tag_lg + 1u, tag_y = tag_lg + 2u;
+    // the next layer's descriptor -> registers now, LDS after the router (its load has landed by then)
+    unsigned long long next_desc = 0;
+    const bool has_next = l + 1 < n_layers;
+    if (has_next && wave == kWaves - 1 && lane < kDescWords)
+      next_desc = ldg(reinterpret_cast<const unsigned long long*>(rest + (l + 1)) + lane);
     stamp(w, l, 0);
-    // ------------------------------------------------------------------ 1: loads without x, then x
-    const int r_row = b + G * wave;
-    const bool is_router = wave < nrw && r_row < E;
-    u32x4_t rw[kRtCpl];
-    if (is_router) {
-      const uint16_t* row = L.wr + (size_t)r_row * H;
-#pragma unroll
-      for (int t = 0; t < kRtCpl; ++t) {
-        const unsigned c = (unsigned)(lane + t * kWave), nc = (unsigned)(H >> 3);
-        rw[t] = ld16(row + min(c, nc - 1) * 8u);   // a chunk past the row end is skipped below
-      }
-    }
+
+    // ------------------------------------------------------------------ 1: x
     if (l == 0) {
       for (int v = tid; v < M * H / 8; v += kThreads)
         *reinterpret_cast<u32x4_t*>(xs + v * 8) = ld16(L.x + (size_t)v * 8);
@@ -455,11 +693,14 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       // y of the previous layer, as its owners published it
       const int n = M * H / 2;
       constexpr int kXw = (M * kHMax / 2 + kThreads - 1) / kThreads;
+      int idx[kXw];
       unsigned long long v[kXw];
-      poll_tagged<kXw>(w, w.ytag, tid, kThreads, n, tag_y - 4u, v);
+#pragma unroll
+      for (int q = 0; q < kXw; ++q) idx[q] = tid + q * kThreads < n ? tid + q * kThreads : -1;
+      poll_tagged<kXw>(w, w.ytag, idx, tag_y - 4u, v);
 #pragma unroll
       for (int q = 0; q < kXw; ++q)
-        if (tid + q * kThreads < n) reinterpret_cast<uint32_t*>(xs)[tid + q * kThreads] = (uint32_t)v[q];
+        if (idx[q] >= 0) reinterpret_cast<uint32_t*>(xs)[idx[q]] = (uint32_t)v[q];
     } else {
       // x may have been written earlier in this launch: device-coherent loads
       const unsigned long long* src = reinterpret_cast<const unsigned long long*>(L.x);
@@ -470,176 +711,72 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 2: router, shared task
     if (is_router) {
+      wait_mem();   // this wave's router-row copy into LDS has landed
+      const uint16_t* wrow = wr_s + (size_t)wave * H;
       float acc[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[m] = 0.0f;
+      for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kRtCpl; ++t) {
-          const int c = lane + t * kWave;
-          if (c < (H >> 3)) {
+      for (int t = 0; t < kRtCpl; ++t) {
+        const int c = lane + t * kWave;
+        if (c < (H >> 3)) {
+          const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(wrow + c * 8);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
             const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + m * H + c * 8);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(rw[t][d]), as_bf16x2(xv[d]), acc[m]);
+            for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(rv[d]), as_bf16x2(xv[d]), acc[m]);
           }
         }
-        acc[m] = group_sum<kWave>(acc[m]);
       }
-      if (lane == 0) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float v = acc[m] + (L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f);
+      for (int m = 0; m < M; ++m) {
+        const float s = wave_sum(acc[m]);
+        if (lane == 0) {
+          const float v = s + (L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f);
           st_coherent(w.logits + (size_t)m * E + r_row, tagged(tag_lg, __float_as_uint(v)));
           if (L.logits_out) stg(L.logits_out + (size_t)m * E + r_row, v);
         }
       }
     }
+    if (has_next && wave == kWaves - 1 && lane < kDescWords) s_desc[(l + 1) & 1][lane] = next_desc;
     stamp(w, l, 2);
     if (shared_task) {
-      // off the critical path (the routed tasks start a selection later), so its loads are not held
-      // in registers across the x hand-off
+      // the shared expert needs no routing: its tasks run while the logits are exchanged
+      if (tid == 0) {
+        un.mask[0] = (1u << M) - 1u;
+        un.pair0[0] = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
+      }
+      __syncthreads();
       TaskRegs sreg;
-      task_load(L, sh, E, b - (G - J), tid_l, sreg);
-      task_compute<M>(sh, w, sreg, (1u << M) - 1u, 0, b - (G - J), xs, a_s, tid_l, tag_pt);
+      task_load(L, sh, E, b - (G - J), tid, sreg);
+      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, a_s, tid, tag_pt);
     }
     stamp(w, l, 3);
 
     // ------------------------------------------------------------------ 3: top-K and union
-    // chunk pass: (token m, chunk c) per wave; K rounds of (max key, lowest lane holding it), so
-    // equal logits go to the lower expert index
-    for (int t = wave; t < M * nchunks; t += kWaves) {
-      const int m = t / nchunks, c = t - m * nchunks;
-      const int e = c * kWave + lane;
-      unsigned long long v[1];
-      poll_tagged<1>(w, w.logits + (size_t)m * E, e, 0, E, tag_lg, v);
-      uint32_t key = e < E ? sel_key(__uint_as_float((uint32_t)v[0])) : 0u;
-#pragma unroll
-      for (int r = 0; r < kMaxK; ++r) {
-        if (r < K) {
-          const uint32_t vmax = wave_max_u32(key);
-          const int win = __ffsll((unsigned long long)__ballot(key == vmax)) - 1;
-          if (lane == win) key = 0u;
-          if (lane == 0) {
-            s_ck[m][c][r] = vmax;
-            s_ci[m][c][r] = c * kWave + win;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    stamp(w, l, 4);
-    if (wave < M) {
-      // merge token `wave`'s candidates; candidate c*K + r precedes c*K + r + 1 and chunk c + 1,
-      // so among equal keys the lowest candidate position is the lowest expert index
-      const int m = wave;
-      const int nc = nchunks * K;
-      uint32_t key[2];
-      int idx[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int i = lane + h * kWave;
-        const int c = i / K, r = i - c * K;
-        key[h] = i < nc ? s_ck[m][c][r] : 0u;
-        idx[h] = i < nc ? s_ci[m][c][r] : 0;
-      }
-      uint32_t kv[kMaxK];
-      int ki[kMaxK];
-#pragma unroll
-      for (int r = 0; r < kMaxK; ++r) {
-        if (r < K) {
-          const uint32_t vmax = wave_max_u32(max(key[0], key[1]));
-          uint32_t li = key[1] == vmax ? (uint32_t)(lane + kWave) : 0xffffffffu;
-          li = key[0] == vmax ? (uint32_t)lane : li;
-          const uint32_t win = wave_min_u32(li);
-          const int hw = (int)(win / kWave), lw = (int)(win % kWave);
-          ki[r] = __builtin_amdgcn_readlane(hw ? idx[1] : idx[0], lw);
-          kv[r] = vmax;
-          if (lane == lw) {
-            if (hw) key[1] = 0u;
-            else key[0] = 0u;
-          }
-        }
-      }
-      if (lane == 0) {
-        const float vmax = key_to_float(kv[0]);
-        float z[kMaxK], s = 0.0f;
-#pragma unroll
-        for (int r = 0; r < kMaxK; ++r)
-          if (r < K) {
-            z[r] = expf(key_to_float(kv[r]) - vmax);
-            s += z[r];
-          }
-#pragma unroll
-        for (int r = 0; r < kMaxK; ++r)
-          if (r < K) {
-            s_idx[m][r] = ki[r];
-            s_w[m][r] = z[r] / s;
-          }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // union of the window's selections: slot 0 = shared expert (if any), then routed ids
-      // ascending. Lane j holds selection j (token j / K); loops over a uniform index use readlane.
-      const int n = M * K;
-      const int mj = lane / K;
-      const int e = lane < n ? s_idx[mj][lane - mj * K] : -1;
-      const float wj = lane < n ? s_w[mj][lane - mj * K] : 0.0f;
-      bool first_occ = lane < n;
-      unsigned mask = 0;
-      float wsum[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
-      for (int i = 0; i < n; ++i) {
-        const int ei = __builtin_amdgcn_readlane(e, i);
-        const int mi = __builtin_amdgcn_readlane(mj, i);
-        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i));
-        if (ei == e) {
-          if (i < lane) first_occ = false;
-          mask |= 1u << mi;
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            if (m == mi) wsum[m] += wi;
-        }
-      }
-      const unsigned long long firsts = __ballot(first_occ);
-      int rank = 0;
-      for (int i = 0; i < n; ++i)
-        if ((firsts >> i) & 1ull) rank += __builtin_amdgcn_readlane(e, i) < e ? 1 : 0;
-      const int cnt = __popc(mask);
-      int pair0 = ns * M, total = pair0;
-      for (int i = 0; i < n; ++i)
-        if ((firsts >> i) & 1ull) {
-          const int ci = __builtin_amdgcn_readlane(cnt, i);
-          pair0 += __builtin_amdgcn_readlane(rank, i) < rank ? ci : 0;
-          total += ci;
-        }
-      if (first_occ) {
-        const int slot = ns + rank;
-        un.id[slot] = e;
-        un.mask[slot] = mask;
-        un.pair0[slot] = pair0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) un.w[slot][m] = wsum[m];
-      }
-      if (lane == 0) {
-        if (ns) {
-          un.id[0] = E;
-          un.mask[0] = (1u << M) - 1u;
-          un.pair0[0] = 0;
-#pragma unroll
-          for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
-        }
-        un.n = __popcll(firsts) + ns;
-        un.n_pairs = total;
-      }
-    }
-    if (b == 0 && tid < M * K) {
-      if (L.topk_idx) stg(L.topk_idx + tid, s_idx[tid / K][tid % K]);
-      if (L.topk_w) stg(L.topk_w + tid, s_w[tid / K][tid % K]);
+    select_topk<M>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_wmax, s_cnt, s_sel, l);
+    if (b == 0 && tid < M * sh.K) {
+      const int m = tid / sh.K, r = tid - m * sh.K;
+      if (L.topk_idx) stg(L.topk_idx + tid, s_idx[m][r]);
+      if (L.topk_w) stg(L.topk_w + tid, s_w[m][r]);
     }
     __syncthreads();
     stamp(w, l, 5);
+
+    // the next layer's router rows -> LDS, behind this layer's task loads
+    if (has_next && is_router) {
+      const uint16_t* nwr = reinterpret_cast<const uint16_t*>(
+          uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8]));
+      const uint16_t* row = nwr + (size_t)r_row * H;
+      for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
+        if (c0 + lane < (H >> 3))
+          __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
+                                           (__attribute__((address_space(3))) void*)(wr_s + (size_t)wave * H + c0 * 8),
+                                           16, 0, 0);
+    }
 
     // ------------------------------------------------------------------ 4: routed tasks
     {
@@ -647,8 +784,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       for (int q = b; q < n_rt; q += G) {
         TaskRegs cur;
         const int u = ns + q / J;
-        task_load(L, sh, un.id[u], q % J, tid_l, cur);
-        task_compute<M>(sh, w, cur, un.mask[u], un.pair0[u], q % J, xs, a_s, tid_l, tag_pt);
+        task_load(L, sh, un.id[u], q % J, tid, cur);
+        task_compute<M>(sh, w, cur, un, u, q % J, xs, a_s, tid, tag_pt);
       }
     }
     stamp(w, l, 6);
@@ -657,40 +794,43 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     if (my_rows > 0) {
       const int np = un.n_pairs;
       const int n_words = np * J * R;
-      const unsigned long long* src = w.partial + (size_t)b * P * J * R;
+      const unsigned long long* src = w.partial + (size_t)b * sh.P * J * R;
       for (int base = 0; base < n_words; base += kPollBatch * kThreads) {
+        int idx[kPollBatch];
         unsigned long long v[kPollBatch];
-        poll_tagged<kPollBatch>(w, src, base + tid, kThreads, n_words, tag_pt, v);
 #pragma unroll
         for (int q = 0; q < kPollBatch; ++q) {
           const int i = base + tid + q * kThreads;
-          if (i < n_words) red[i] = __uint_as_float((uint32_t)v[q]);
+          idx[q] = i < n_words ? i : -1;
         }
+        poll_tagged<kPollBatch>(w, src, idx, tag_pt, v);
+#pragma unroll
+        for (int q = 0; q < kPollBatch; ++q)
+          if (idx[q] >= 0) red[idx[q]] = __uint_as_float((uint32_t)v[q]);
       }
       __syncthreads();
       stamp(w, l, 7);
-      // blocks first: s_red2[p][row] = sum_j partial[p][j][row], j ascending
-      for (int t = tid; t < np * R; t += kThreads) {
-        const int p = t / R, rl = t - p * R;
-        float s = 0.0f;
-        for (int j = 0; j < J; ++j) s += red[(p * J + j) * R + rl];
-        s_red2[p][rl] = s;
-      }
-      __syncthreads();
-      // then slots, in slot order: y[m][row] = sum_u w[u][m] * s_red2[pair(u, m)][row]; a thread
-      // takes two adjacent rows of one token so that the tagged copy holds a bf16 pair
-      const int U = un.n;
-      for (int t = tid; t < (my_rows / 2) * M; t += kThreads) {
-        const int rp = t / M, m = t - rp * M;
-        float y0 = 0.0f, y1 = 0.0f;
-        for (int u = 0; u < U; ++u) {
-          const unsigned mk = un.mask[u];
-          if ((mk >> m) & 1u) {
-            const int p = un.pair0[u] + __popc(mk & ((1u << m) - 1u));
-            y0 += un.w[u][m] * s_red2[p][2 * rp];
-            y1 += un.w[u][m] * s_red2[p][2 * rp + 1];
+      // y[m][row] = sum over token m's pairs (slot order) and blocks; kSumLanes lanes per (m, row)
+      {
+        const int grp = tid / kSumLanes, s = tid % kSumLanes;
+        const int m = grp / kMaxRows, rl = grp % kMaxRows;
+        float acc = 0.0f;
+        if (m < M && rl < my_rows) {
+          const int npm = un.tok_n[m];
+          for (int i = 0; i < npm; ++i) {
+            const float* rp = red + (size_t)un.tok_pair[m][i] * J * R + rl;
+            for (int j = s; j < J; j += kSumLanes) acc += rp[j * R];
           }
         }
+        acc = row8_sum(acc);
+        if (s == 0 && m < M && rl < my_rows) s_y[m][rl] = acc;
+      }
+      __syncthreads();
+      stamp(w, l, 13);
+      // outputs: a thread takes two adjacent rows of one token (the tagged copy holds a bf16 pair)
+      for (int t = tid; t < (my_rows / 2) * M; t += kThreads) {
+        const int rp = t / M, m = t - rp * M;
+        const float y0 = s_y[m][2 * rp], y1 = s_y[m][2 * rp + 1];
         const size_t o = (size_t)m * H + row0 + 2 * rp;
         const uint16_t h0 = f32_to_bf16_rne(y0), h1 = f32_to_bf16_rne(y1);
         if (L.y32) {
@@ -707,8 +847,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     }
     stamp(w, l, 8);
     if (!sh.chained && l + 1 < n_layers) {
-      grid_sync(w, sync);   // layer l's output is written before layer l+1 starts
+      tagged_barrier(w, tag_y, tid, l);   // layer l's output is written before layer l+1 starts
       stamp(w, l, 9);
+    } else {
+      __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer
     }
   }
 }
@@ -735,13 +877,17 @@ unsigned long long* g_trace[64];  // per device: trace buffer registered by qws_
 size_t g_trace_bytes[64];
 constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 
-size_t lds_bytes(int M, int H, int P, int J, int R) { return (size_t)M * H * 2 + (size_t)P * J * R * 4; }
+size_t lds_bytes(int M, int E, int H, int P, int J, int R, int nrw) {
+  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * R * 4;
+  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + (sel > comb ? sel : comb);
+}
 
 size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
   const size_t sync = qws_host::align256(kSyncCounters * kSyncStride * 8);
   const size_t misc = 256;   // launch counter, error count
   const size_t lg = qws_host::align256((size_t)M * E * 8);
   const size_t yt = qws_host::align256((size_t)M * H * 4);
+  const size_t dn = qws_host::align256((size_t)kMaxGrid * 8);
   const size_t part = qws_host::align256((size_t)M * (K + 1) * (I / kBlk) * (H + kRowsPad) * 8);
   if (w) {
     w->trace = nullptr;
@@ -750,9 +896,10 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
     w->errors = reinterpret_cast<unsigned*>(base + sync + 128);
     w->logits = reinterpret_cast<unsigned long long*>(base + sync + misc);
     w->ytag = reinterpret_cast<unsigned long long*>(base + sync + misc + lg);
-    w->partial = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt);
+    w->done = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt);
+    w->partial = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn);
   }
-  return sync + misc + lg + yt + part;
+  return sync + misc + lg + yt + dn + part;
 }
 
 int grid_for_device(int* G) {
@@ -819,6 +966,7 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   }
   if (!workspace || workspace_bytes < ws_layout(M, K, E, H, I, nullptr, nullptr)) return QWS_ERR_WORKSPACE;
   if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
+  if (dev_copy && (reinterpret_cast<uintptr_t>(dev_copy) & 7u)) return QWS_ERR_ALIGN;
   int G = 0;
   int st = grid_for_device(&G);
   if (st != QWS_OK) return st;
@@ -826,10 +974,10 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   const int nrw = (E + G - 1) / G;
   const int R = ((H + G - 1) / G + 1) & ~1;   // even, so a thread writes a bf16 pair of one token
   if (G > kMaxGrid || G < J || nrw > kWaves || R > kMaxRows || (size_t)G * R > (size_t)H + kRowsPad ||
-      G * R > kThreads * kDnRpl)
+      G * R > kThreads * kDnRpl || M * kMaxRows * kSumLanes > kThreads)
     return QWS_ERR_SHAPE;
   const int P = M * (K + 1);
-  const size_t lds = lds_bytes(M, H, P, J, R);
+  const size_t lds = lds_bytes(M, E, H, P, J, R, nrw);
   if (lds > kMaxDynLds) return QWS_ERR_SHAPE;
   // Chained: layer l+1 reads y of layer l. Then the layers need no barrier, provided every
   // workgroup computes router rows and owns output rows, so that no workgroup can fall a layer
@@ -845,7 +993,7 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
     const size_t need = (size_t)n_layers * G * kTracePoints * 8;
     w.trace = (dev >= 0 && dev < 64 && g_trace[dev] && g_trace_bytes[dev] >= need) ? g_trace[dev] : nullptr;
   }
-  const Shape sh{E, K, H, I, hs, R, P, chained ? 1 : 0, G * R};
+  const Shape sh{E, K, H, I, hs, R, P, chained ? 1 : 0, G * R, nrw};
   const Layer first = to_layer(host[0]);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (M) {

@@ -90,6 +90,51 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// DPP (data-parallel primitive) lane moves: cross-lane operands without an LDS round trip.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+// v + (the DPP-moved v), with lanes outside ROWS adding 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+// Sum over each aligned group of 16 lanes; every lane of the group gets it (quad swaps, then
+// half-row and row mirrors).
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  return v;
+}
+// Sum over each aligned group of 8 lanes; every lane of the group gets it.
+__device__ __forceinline__ float row8_sum(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  return v;
+}
+// Wave-uniform sum of 64 lanes: 16-lane sums, then row 15 -> next row and lane 31 -> rows 2, 3
+// broadcasts; lane 63 ends with the total. The order of additions is fixed.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v = dpp_add<0x142, 0xA>(v);
+  v = dpp_add<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Wave-uniform max of a uint32 across 64 lanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------------------ sync

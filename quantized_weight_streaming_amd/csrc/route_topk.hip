@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_topk_kernel(
           for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(w[t][d]), as_bf16x2(xv[d]), acc[m]);
         }
       }
-      acc[m] = group_sum<kWave>(acc[m]);
+      acc[m] = wave_sum(acc[m]);   // the fused layer kernel reduces the same way
     }
     if (lane == 0) {
 #pragma unroll
