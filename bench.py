@@ -409,10 +409,11 @@ def main():
                                                        "top1_in_bf16_top10": round(in10 / n, 4)}
             log("agreement", breakdown["fp8_vs_bf16_head_agreement"])
 
-    # a plain device copy of known size: the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE readings
-    cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    # a plain device copy of known size (probe_copy_kernel, 256 MiB read + 256 MiB written): the
+    # scale for rocprofv3 FETCH_SIZE / WRITE_SIZE readings of the kernels above
+    cp_src = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
     cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
+    qws.probe_copy(cp_src, cp_dst, 4096)
     torch.cuda.synchronize(dev)
     del cp_src, cp_dst
 

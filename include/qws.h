@@ -264,10 +264,10 @@ int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t strea
  * memory, 16-byte aligned), every moe_layer_mxfp4 / moe_layers_mxfp4 launch whose trace fits in
  * `bytes` writes, per layer and workgroup, 16 timestamps of the device wall clock (100 MHz,
  * uint64): [0] layer start, [1] x staged, [2] router rows done, [3] shared-expert task done,
- * [4] logits received, [10] wave maxima shared, [11] selection candidates gathered, [12] ranks
- * done, [5] selection and union done, [6] routed tasks done, [7] partial sums received (row
- * owners), [13] row sums done, [8] output written, [14] layer-end stores acknowledged, [9] layer
- * barrier passed (sequences that are not chained); layout [n_layers][grid][16]. NULL unregisters.
+ * [4] logits received, [10] selection threshold found, [11] candidates above it compacted,
+ * [12] candidate ranks done, [5] selection and union done, [6] routed tasks done, [7] partial
+ * sums received (row owners), [13] row sums done, [8] output written, [14] layer-end stores
+ * acknowledged, [9] layer barrier passed (sequences that are not chained); layout [n_layers][grid][16]. NULL unregisters.
  * Diagnostics only. */
 int qws_debug_trace_buffer(void* buf, size_t bytes);
 
@@ -275,6 +275,12 @@ int qws_debug_trace_buffer(void* buf, size_t bytes);
  * writes one checksum word per workgroup into sink[0 .. blocks) (blocks <= 65536). Measures the
  * device's practical read bandwidth.                                                        */
 int qws_probe_read(const void* buf, size_t bytes, unsigned* sink, int blocks, qws_stream_t stream);
+
+/* Copy probe: copies `bytes` (multiple of 16; both buffers 16-byte aligned, not overlapping) from
+ * `src` to `dst` with 128-bit loads and stores, grid-strided over `blocks` workgroups (<= 65536).
+ * A kernel of known traffic (reads and writes `bytes` each) against which HBM traffic counters
+ * are scaled.                                                                                 */
+int qws_probe_copy(const void* src, void* dst, size_t bytes, int blocks, qws_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -163,6 +163,15 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4_t* __restri
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// --------------------------------------------------------------------------- copy probe
+// A plain copy of known size: the reference point that turns the HBM traffic counters of other
+// kernels into bytes (read and write both equal `bytes` here).
+__global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                         size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 namespace qws_host {
@@ -277,5 +286,17 @@ extern "C" int qws_probe_read(const void* buf, size_t bytes, unsigned* sink, int
   if (!qws_host::aligned16(buf)) return QWS_ERR_ALIGN;
   hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4_t*>(buf), bytes / 16, sink);
+  return qws_host::check_launch();
+}
+
+extern "C" int qws_probe_copy(const void* src, void* dst, size_t bytes, int blocks, qws_stream_t stream) {
+  if (!src || !dst) return QWS_ERR_ARG;
+  if (bytes == 0 || bytes % 16 || blocks < 1 || blocks > 65536) return QWS_ERR_SHAPE;
+  if (!qws_host::aligned16(src) || !qws_host::aligned16(dst)) return QWS_ERR_ALIGN;
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return QWS_ERR_ARG;
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), bytes / 16);
   return qws_host::check_launch();
 }

@@ -42,25 +42,32 @@ namespace {
 
 using namespace qws;
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;   // 16 waves: 4 per SIMD to hide the task's load and LDS latency
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxM = 4;
 constexpr int kMaxK = 8;
 constexpr int kMaxSlots = kMaxM * kMaxK + 1;    // routed union + shared
 constexpr int kMaxPairs = kMaxM * (kMaxK + 1);  // (slot, token) pairs
 constexpr int kMaxE = 1024;
-constexpr int kEpt = kMaxE / kThreads;          // experts per thread in the selection
 constexpr int kHMax = 2560;
 constexpr int kIMax = 1024;
 constexpr int kBlk = 32;        // activations per task: one MX block of the down projection
-constexpr int kGuCpl = 5;       // 16-byte chunks per lane of a gate/up row: H <= 16 * 5 * 32
+constexpr int kGuCpl = 5;       // 16-byte chunks per lane of a gate or up row: H <= 16 * 5 * 32
 constexpr int kRtCpl = 5;       // 16-byte chunks per lane of a router row: H <= 64 * 5 * 8
-constexpr int kDnRpl = 5;       // down rows per thread in a task: H <= 512 * 5
+constexpr int kDnRpl = 3;       // down rows per thread in a task: H <= 1024 * 3
 constexpr int kMaxRows = 16;    // output rows owned by one workgroup
 constexpr int kMaxGrid = 512;
-constexpr int kRowsPad = 2 * kMaxGrid;   // partial buffer rows allowed beyond H (G * R >= H)
-constexpr int kPollBatch = 12;  // tagged words per thread in flight while reading partials
-constexpr int kSumLanes = 8;    // lanes that share the sum of one (token, row) in the combine
+constexpr int kPollBatch = 8;   // tagged words per thread in flight while reading partials
+constexpr int kLine = 16;       // 64-bit words per 128-byte line: hand-off words of one writer share no line
+constexpr int kBlkLanes = 8;   // lanes of a row-sum group that read one block's partial lines
+// Lanes that share one (token, row) output sum in the combine: fewer tokens, wider groups.
+template <int M>
+__host__ __device__ constexpr int sum_lanes() { return M == 1 ? 32 : (M == 2 ? 16 : 8); }
+static_assert(kMaxRows <= kLine, "an owner's rows of one (pair, block) share one line");
+static_assert(kMaxM <= kLine, "an expert's logits of all tokens share one line");
+static_assert(sum_lanes<1>() * kMaxRows <= 512 && 2 * sum_lanes<2>() * kMaxRows <= 512 &&
+                  3 * sum_lanes<3>() * kMaxRows <= 512 && 4 * sum_lanes<4>() * kMaxRows <= 512,
+              "combine groups exceed the workgroup");
 constexpr int kSyncCounters = 16;
 constexpr int kSyncStride = 16;             // 64-bit words: 128 bytes apart
 constexpr unsigned kSpinLimit = 1u << 20;   // polls before a wait gives up (~1 s)
@@ -97,8 +104,10 @@ struct Shape {
   int R;        // output rows per workgroup (even)
   int P;        // (slot, token) pairs the partial buffer holds per block: M * (K + 1)
   int chained;  // x of layer l+1 is y (bf16) of layer l, for every l
-  int rows_total;  // G * R: rows of the partial buffer, H and padding
   int nrw;      // router rows per workgroup (one wave each)
+  float inv_r;     // 1 / R: owner of a row = floor((row + 0.5) / R) without an integer division
+  int y_stride;    // tagged y words per row owner (M * R / 2, padded to whole lines)
+  int x_fresh;  // no layer's x is written by this launch: x of layer l+1 is fetched during layer l's barrier
 };
 
 struct Work {
@@ -106,10 +115,12 @@ struct Work {
   unsigned long long* sync;      // kSyncCounters monotonic counters, kSyncStride apart
   unsigned long long* launches;  // launch counter (each workgroup adds 1 per launch)
   unsigned* errors;              // count of bounded waits that timed out (sticky)
-  unsigned long long* logits;    // [M][E] tagged logits
-  unsigned long long* ytag;      // [M][H/2] tagged bf16 pairs of y (chained sequences)
-  unsigned long long* done;      // [G] tagged "layer finished" words (layers that are not chained)
-  unsigned long long* partial;   // [G][P][J][R] tagged, gate-weighted partial sums of the down projection
+  // Hand-off buffers. Each 128-byte line is written by one workgroup only: on MI355X an exchange
+  // among all workgroups takes ~1.8 us that way and ~3 us when writers share lines.
+  unsigned long long* logits;    // [E][kLine] tagged logits: expert e, token m at e*kLine + m (one line per router row)
+  unsigned long long* ytag;      // [G][y_stride] tagged bf16 pairs of y (chained sequences): owner b, token m, pair q at b*y_stride + m*R/2 + q
+  unsigned long long* done;      // [G][kLine] tagged "layer finished" words (layers that are not chained)
+  unsigned long long* partial;   // [G][P][J][kLine] tagged, gate-weighted partial sums: owner, pair, block, row - owner*R
 };
 
 // Routing of the current layer, shared by the workgroup (LDS).
@@ -224,17 +235,26 @@ __device__ void grid_sync(const Work& w, SyncState& st) {
 // Between layers that are not chained: every workgroup publishes a tagged word once all of its
 // stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
 // round trip to a counter before the wait starts.
-__device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l) {
+__device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, const uint16_t* next_x, uint16_t* xs,
+                               int n_x) {
   wait_mem();
   __syncthreads();
   stamp(w, l, 14);
-  if (tid == 0) st_coherent(w.done + blockIdx.x, tagged(tag, 0u));
+  if (tid == 0) st_coherent(w.done + (size_t)blockIdx.x * kLine, tagged(tag, 0u));
+  if (next_x) {
+    // the next layer's x (written before this launch) -> LDS, in flight while the barrier waits
+    const int lane = tid % kWave, c0 = tid - lane;
+    for (int c = c0; c < n_x / 8; c += kThreads)
+      if (c + lane < n_x / 8)
+        __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(next_x + (size_t)(c + lane) * 8),
+                                         (__attribute__((address_space(3))) void*)(xs + (size_t)c * 8), 16, 0, 0);
+  }
   if (tid < kWave) {
     constexpr int kPer = kMaxGrid / kWave;
     int idx[kPer];
     unsigned long long v[kPer];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) idx[q] = tid + q * kWave < (int)gridDim.x ? tid + q * kWave : -1;
+    for (int q = 0; q < kPer; ++q) idx[q] = tid + q * kWave < (int)gridDim.x ? (tid + q * kWave) * kLine : -1;
     poll_tagged<kPer>(w, w.done, idx, tag, v);
   }
   __syncthreads();
@@ -266,101 +286,108 @@ __device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
 
 // ------------------------------------------------------------------------------ tasks
 struct TaskRegs {
-  u32x4_t g[kGuCpl], u[kGuCpl], d[kDnRpl];
-  uint32_t gs[kGuCpl], us[kGuCpl], ds[kDnRpl];
+  u32x4_t q[kGuCpl];
+  uint32_t qs[kGuCpl];
 };
 
-// Issues the loads of task (expert e, block j). 16-lane group g of the workgroup takes gate row
-// 32j+g and up row I+32j+g (lane j16: chunks j16, j16+16, ...); thread t takes down rows t, t+512, ...
-__device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r) {
-  const unsigned g = tid >> 4, j16 = tid & 15;
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)src, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+}
+
+// Issues the loads of task (expert e, block j). 32-lane group p = tid / 32 takes activation 32j+p:
+// its lanes 0-15 gate row 32j+p, lanes 16-31 up row I+32j+p (lane j16: chunks j16, j16+16, ...)
+// into registers. The block's down-projection codes (H x 16 bytes, contiguous in the block-major
+// layout) and scales (H bytes) go to LDS by DMA, issued after the gate/up loads so that waiting
+// for a gate/up chunk never waits for them (vector memory operations complete in order).
+__device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r,
+                                          uint8_t* dn_s) {
+  const unsigned p = tid >> 5, up = (tid >> 4) & 1u, j16 = tid & 15;
   const int H = sh.H, I = sh.I, J = I / kBlk;
   const unsigned nch = (unsigned)(H >> 5), rb = (unsigned)(H >> 1);
-  const size_t row_g = (size_t)e * 2 * I + (size_t)kBlk * j;   // first gate row of the block
-  const uint8_t* gq = L.gq + row_g * rb;
-  const uint8_t* uq = gq + (size_t)I * rb;
-  const uint8_t* gs = L.gs + row_g * nch;
-  const uint8_t* us = gs + (size_t)I * nch;
+  const size_t row = (size_t)e * 2 * I + (size_t)kBlk * j + p + (up ? (size_t)I : 0);
+  const uint8_t* rq = L.gq + row * rb;
+  const uint8_t* rs = L.gs + row * nch;
   // unconditional loads from clamped (in-bounds) addresses: no branch around a load, so a task's
-  // loads issue back to back. A chunk past the row end is loaded from the last chunk and skipped
-  // by the compute; a down row past H is loaded from row H-1 and its partial sum is not stored.
+  // loads issue back to back; a chunk past the row end is masked by the compute
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
     const unsigned c = min(j16 + 16u * t, nch - 1);
-    r.g[t] = ld16_stream(gq + g * rb + c * 16u);
-    r.u[t] = ld16_stream(uq + g * rb + c * 16u);
-    r.gs[t] = ldb_stream(gs + g * nch + c);
-    r.us[t] = ldb_stream(us + g * nch + c);
+    r.q[t] = ld16_stream(rq + c * 16u);
+    r.qs[t] = ldb_stream(rs + c);
   }
   const size_t blk = ((size_t)e * J + j) * (size_t)H;
   const uint8_t* dq = L.dq + blk * 16;
   const uint8_t* ds = L.ds + blk;
+  const unsigned lane = tid & (kWave - 1), c0 = tid - lane;
 #pragma unroll
   for (int t = 0; t < kDnRpl; ++t) {
-    const unsigned row = min(tid + (unsigned)(kThreads * t), (unsigned)H - 1);
-    r.d[t] = ld16_stream(dq + row * 16u);
-    r.ds[t] = ldb_stream(ds + row);
+    const unsigned rw = c0 + (unsigned)(kThreads * t);
+    if (rw + lane < (unsigned)H) lds_dma16(dq + (size_t)(rw + lane) * 16u, dn_s + (size_t)rw * 16u);
   }
+  // scales: H bytes as 4-byte words (H is a multiple of 32)
+  if (c0 * 4u < (unsigned)H && (c0 + lane) * 4u < (unsigned)H)
+    lds_dma4(ds + (size_t)(c0 + lane) * 4u, dn_s + (size_t)H * 16u + c0 * 4u);
 }
 
 // Computes task (slot u: tokens in un.mask[u], pairs un.pair0[u] + rank, gate weights un.w[u][m],
-// block j) from its loaded registers: the block's activations silu(gate) * up into LDS, then
-// partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every row, stored tagged at this
-// thread's row offsets in the owners' regions.
+// block j) from its loaded registers and the down block in LDS: the block's activations
+// silu(gate) * up into LDS, then partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every
+// row, stored tagged at this thread's row offsets in the owners' regions.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, const TaskRegs& r, const Union& un,
-                                             int u, int j, const uint16_t* xs, float* a_s, unsigned tid,
-                                             uint32_t tag) {
-  const int g = tid >> 4, j16 = tid & 15;
+                                             int u, int j, const uint16_t* xs, float* a_s, const uint8_t* dn_s,
+                                             unsigned tid, uint32_t tag) {
+  const int p = tid >> 5, j16 = tid & 15;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
   const unsigned mask = un.mask[u];
   const int p0 = un.pair0[u];
-  float ag[M], au[M];
+  float acc[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) ag[m] = au[m] = 0.0f;
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
-    const int c = j16 + 16 * t;
-    if (c < nch) {
-      const float scg = e8m0_to_f32(r.gs[t]), scu = e8m0_to_f32(r.us[t]);
-      bf16x2_t pg[16], pu[16];
+    // no branch on the chunk index: a chunk past the row end gets scale 0 and adds zeros. (With
+    // a branch the compiler sank that chunk's loads into it, behind the down-projection loads,
+    // and computed it first, so the first dot product waited for the whole task's bytes.)
+    const int c = min(j16 + 16 * t, nch - 1);
+    const float sc = j16 + 16 * t < nch ? e8m0_to_f32(r.qs[t]) : 0.0f;
+    bf16x2_t pw[16];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        pg[4 * d + 0] = fp4x2_to_bf16x2<0>(r.g[t][d], scg);
-        pg[4 * d + 1] = fp4x2_to_bf16x2<1>(r.g[t][d], scg);
-        pg[4 * d + 2] = fp4x2_to_bf16x2<2>(r.g[t][d], scg);
-        pg[4 * d + 3] = fp4x2_to_bf16x2<3>(r.g[t][d], scg);
-        pu[4 * d + 0] = fp4x2_to_bf16x2<0>(r.u[t][d], scu);
-        pu[4 * d + 1] = fp4x2_to_bf16x2<1>(r.u[t][d], scu);
-        pu[4 * d + 2] = fp4x2_to_bf16x2<2>(r.u[t][d], scu);
-        pu[4 * d + 3] = fp4x2_to_bf16x2<3>(r.u[t][d], scu);
-      }
+    for (int d = 0; d < 4; ++d) {
+      pw[4 * d + 0] = fp4x2_to_bf16x2<0>(r.q[t][d], sc);
+      pw[4 * d + 1] = fp4x2_to_bf16x2<1>(r.q[t][d], sc);
+      pw[4 * d + 2] = fp4x2_to_bf16x2<2>(r.q[t][d], sc);
+      pw[4 * d + 3] = fp4x2_to_bf16x2<3>(r.q[t][d], sc);
+    }
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        if ((mask >> m) & 1u) {
-          const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs + m * H + c * 32);
-          float a = ag[m], b = au[m];
+    for (int m = 0; m < M; ++m) {
+      // at M = 1 every task serves token 0: no branch (a branch used by one token only let the
+      // compiler sink the whole chunk's loads and conversions into it, behind later loads)
+      if (M == 1 || ((mask >> m) & 1u)) {
+        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs + m * H + c * 32);
+        float a = acc[m];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4_t xv = xp[q];
+        for (int q = 0; q < 4; ++q) {
+          const u32x4_t xv = xp[q];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              a = dot2(pg[4 * q + k], as_bf16x2(xv[k]), a);
-              b = dot2(pu[4 * q + k], as_bf16x2(xv[k]), b);
-            }
-          }
-          ag[m] = a;
-          au[m] = b;
+          for (int k = 0; k < 4; ++k) a = dot2(pw[4 * q + k], as_bf16x2(xv[k]), a);
         }
+        acc[m] = a;
       }
     }
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float hg = row16_sum(ag[m]);
-    const float hu = row16_sum(au[m]);
-    if (j16 == 0) a_s[m * kBlk + g] = silu(hg) * hu;
+    // 16-lane row sums: gate in DPP rows 0 and 2 of the wave, up in rows 1 and 3; the gate sum
+    // moves to the up row (row_bcast:15), whose first lane writes silu(gate) * up
+    const float h = row16_sum(acc[m]);
+    const float hg = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h), 0x142, 0xA, 0xF, false));
+    if ((tid & 31) == 16) a_s[m * kBlk + p] = silu(hg) * h;
   }
+  wait_mem();   // this thread's share of the down block has landed in LDS
   __syncthreads();
   float wt[M];
   int pm[M];
@@ -372,21 +399,22 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
 #pragma unroll
   for (int t = 0; t < kDnRpl; ++t) {
     const int row = tid + kThreads * t;
-    // this row's word in its owner's region [owner][P][J][R]
-    const int rc = min(row, sh.rows_total - 1), owner = rc / R;
-    const unsigned rowoff = (unsigned)(owner * sh.P * J * R + (rc - owner * R));
-    const float sc = e8m0_to_f32(r.ds[t]);
+    // this row's word in its owner's region [owner][P][J][kLine]
+    const int rc = min(row, H - 1), owner = (int)(((float)rc + 0.5f) * sh.inv_r);
+    const unsigned rowoff = (unsigned)(owner * sh.P * J * kLine + (rc - owner * R));
+    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dn_s + (size_t)rc * 16);
+    const float sc = e8m0_to_f32(dn_s[(size_t)H * 16 + rc]);
     float wf[kBlk];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const f32x2_t v0 = fp4x2_to_f32x2<0>(r.d[t][d], sc), v1 = fp4x2_to_f32x2<1>(r.d[t][d], sc);
-      const f32x2_t v2 = fp4x2_to_f32x2<2>(r.d[t][d], sc), v3 = fp4x2_to_f32x2<3>(r.d[t][d], sc);
+      const f32x2_t v0 = fp4x2_to_f32x2<0>(dv[d], sc), v1 = fp4x2_to_f32x2<1>(dv[d], sc);
+      const f32x2_t v2 = fp4x2_to_f32x2<2>(dv[d], sc), v3 = fp4x2_to_f32x2<3>(dv[d], sc);
       wf[8 * d + 0] = v0.x; wf[8 * d + 1] = v0.y; wf[8 * d + 2] = v1.x; wf[8 * d + 3] = v1.y;
       wf[8 * d + 4] = v2.x; wf[8 * d + 5] = v2.y; wf[8 * d + 6] = v3.x; wf[8 * d + 7] = v3.y;
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      if ((mask >> m) & 1u) {
+      if (M == 1 || ((mask >> m) & 1u)) {
         const float4* ap = reinterpret_cast<const float4*>(a_s + m * kBlk);
         float s = 0.0f;
 #pragma unroll
@@ -397,10 +425,7 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
           s = fmaf(wf[4 * q + 2], a4.z, s);
           s = fmaf(wf[4 * q + 3], a4.w, s);
         }
-        // rows H .. G*R-1 (zero weights) pad the last owner's region so that it is written whole
-        s = row < H ? wt[m] * s : 0.0f;
-        if (row < sh.rows_total)
-          st_coherent(w.partial + (size_t)(pm[m] * J + j) * R + rowoff, tagged(tag, __float_as_uint(s)));
+        if (row < H) st_coherent(w.partial + (size_t)(pm[m] * J + j) * kLine + rowoff, tagged(tag, __float_as_uint(wt[m] * s)));
       }
     }
   }
@@ -408,181 +433,177 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
 }
 
 // ------------------------------------------------------------------------------ top-K + union
-// Every workgroup selects the top-K of each token from the tagged logits (same result in every
-// workgroup). Thread t holds experts t + 512 i. A candidate must reach T = the smallest of the
-// per-wave maxima when at least K waves hold experts (then >= K logits reach T, so every one of
-// the top K does); otherwise T admits every expert. Each candidate's rank is the number of
-// candidates that beat it; ranks < K are the selection, in order.
-template <int M>
+// Every workgroup selects the top-K of each token from the tagged logits (the same result in every
+// workgroup), with one wave per token and no workgroup barrier: fewer polling waves make the
+// logits exchange faster, and the serial part stays short. Lane l holds experts l + 64 q. A
+// candidate must reach T = the smallest of the maxima of the 8 lane groups (lanes 8g .. 8g+7)
+// when at least K groups hold experts (then >= K logits reach T, so all of the top K do);
+// otherwise T admits every expert. A candidate's rank is the number of candidates that beat it
+// (larger logit, or equal logit and lower index); ranks < K are the selection, in order.
+template <int M, int kQ>
 __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint32_t tag, int tid, int wave, int lane,
                                             unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
-                                            float (*s_w)[kMaxK], uint32_t (*s_wmax)[kWaves],
-                                            int (*s_cnt)[kEpt][kWaves], uint32_t (*s_sel)[kMaxK], int l) {
+                                            float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK], int l) {
   const int E = sh.E, K = sh.K;
-  uint32_t key[M][kEpt];
-  {
-    int idx[M * kEpt];
-    unsigned long long v[M * kEpt];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i) {
-        const int e = tid + kThreads * i;
-        idx[m * kEpt + i] = e < E ? m * E + e : -1;
-      }
-    poll_tagged<M * kEpt>(w, w.logits, idx, tag, v);
-    stamp(w, l, 4);
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i)
-        key[m][i] = idx[m * kEpt + i] >= 0 ? sel_key(__uint_as_float((uint32_t)v[m * kEpt + i])) : 0u;
-  }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    uint32_t k = key[m][0];
-#pragma unroll
-    for (int i = 1; i < kEpt; ++i) k = max(k, key[m][i]);
-    const uint32_t wm = wave_max_u32(k);
-    if (lane == 0) s_wmax[m][wave] = wm;
-  }
-  __syncthreads();
-  stamp(w, l, 10);
-  // waves holding at least one expert: wave v holds experts v*64 .. v*64+63 (+ 512 i)
-  const int nvw = min(kWaves, (E + kWave - 1) / kWave);
-  bool cf[M][kEpt];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    uint32_t T = 0u;
-    if (nvw >= K) {
-      T = 0xffffffffu;
-      for (int v = 0; v < nvw; ++v) T = min(T, s_wmax[m][v]);
-    }
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      cf[m][i] = key[m][i] != 0u && key[m][i] >= T;
-      const unsigned long long b = __ballot(cf[m][i]);
-      if (lane == 0) s_cnt[m][i][wave] = __popcll(b);
-    }
-  }
-  __syncthreads();
   const unsigned long long lt = (1ull << lane) - 1ull;
-  int ncand[M];
+  const int ns = sh.has_shared ? 1 : 0;
+  (void)tid;
+  if (wave < M) {
+    const int m = wave;
+    uint32_t key[kQ];
+    {
+      int idx[kQ];
+      unsigned long long v[kQ];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    // candidate order in the buffer: (i, wave, lane); any order would do, ranks are counted
-    int pos[kEpt], total = 0;
+      for (int q = 0; q < kQ; ++q) {
+        const int e = lane + kWave * q;
+        idx[q] = e < E ? e * kLine + m : -1;
+      }
+      poll_tagged<kQ>(w, w.logits, idx, tag, v);
+      stamp(w, l, 4);
 #pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      pos[i] = total;
-      for (int v = 0; v < kWaves; ++v) {
-        const int c = s_cnt[m][i][v];
-        pos[i] += v < wave ? c : 0;
-        total += c;
+      for (int q = 0; q < kQ; ++q) key[q] = idx[q] >= 0 ? sel_key(__uint_as_float((uint32_t)v[q])) : 0u;
+    }
+    // threshold: maxima of the 8-lane groups (a group holds experts 8g .. 8g+7 + 64 q)
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int q = 1; q < kQ; ++q) lm = max(lm, key[q]);
+    lm = max(lm, dpp<0xB1>(lm));
+    lm = max(lm, dpp<0x4E>(lm));
+    lm = max(lm, dpp<0x141>(lm));
+    const int ngroups = min(kWave / 8, (E + 7) / 8);
+    uint32_t T = 0u;
+    if (ngroups >= K) {
+      T = 0xffffffffu;
+#pragma unroll
+      for (int g = 0; g < kWave / 8; ++g)
+        if (g < ngroups) T = min(T, (uint32_t)__builtin_amdgcn_readlane((int)lm, 8 * g));
+    }
+    stamp(w, l, 10);
+    // candidates -> LDS in (q, lane) order
+    unsigned long long* cm = cand + m * E;
+    int nc = 0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const bool f = key[q] != 0u && key[q] >= T;
+      const unsigned long long bl = __ballot(f);
+      if (f) cm[nc + __popcll(bl & lt)] = rank_key(key[q], lane + kWave * q);
+      nc += __popcll(bl);
+    }
+    stamp(w, l, 11);
+    // ranks (this wave's LDS writes above are visible to its reads: one wave's LDS operations run
+    // in order)
+    for (int j0 = 0; j0 < nc; j0 += kWave) {
+      const int j = j0 + lane;
+      const unsigned long long mine = j < nc ? cm[j] : 0ull;
+      int rank = 0;
+      if (nc <= 2 * kWave) {
+#pragma unroll 4
+        for (int q = 0; q < nc; ++q) rank += cm[q] > mine ? 1 : 0;
+      } else {
+        // many equal logits: stop counting once a candidate is known to be outside the top K
+        for (int q = 0; q < nc && rank < K; ++q) rank += cm[q] > mine ? 1 : 0;
+      }
+      if (j < nc && rank < K) {
+        s_sel[m][rank] = (uint32_t)(mine >> 32);
+        s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)mine);
       }
     }
-    ncand[m] = total;
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      const unsigned long long bl = __ballot(cf[m][i]);
-      if (cf[m][i]) cand[m * E + pos[i] + __popcll(bl & lt)] = rank_key(key[m][i], tid + kThreads * i);
+    stamp(w, l, 12);
+    // softmax over the K selected logits, summed in rank order (the same sum in every lane)
+    const float z = lane < K ? expf(key_to_float(s_sel[m][lane]) - key_to_float(s_sel[m][0])) : 0.0f;
+    float sum = 0.0f;
+    for (int r = 0; r < K; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), r));
+    const float wr = z / sum;
+    if (lane < K) s_w[m][lane] = wr;
+    if constexpr (M == 1) {
+      // one token: the union is the shared expert, then the selection in rank order
+      if (lane < K) {
+        const int slot = ns + lane;
+        un.id[slot] = s_idx[0][lane];
+        un.mask[slot] = 1u;
+        un.pair0[slot] = slot;
+        un.w[slot][0] = wr;
+        un.tok_pair[0][slot] = slot;
+      }
+      if (lane == 0) {
+        if (ns) {
+          un.id[0] = E;
+          un.mask[0] = 1u;
+          un.pair0[0] = 0;
+          un.w[0][0] = 1.0f;
+          un.tok_pair[0][0] = 0;
+        }
+        un.n = ns + K;
+        un.n_pairs = ns + K;
+        un.tok_n[0] = ns + K;
+      }
     }
   }
-  __syncthreads();
-  stamp(w, l, 11);
+  if constexpr (M > 1) {
+    __syncthreads();
+    stamp(w, l, 12);
+    if (wave == 0) {
+      // union in first-occurrence order over (token, rank); slot 0 is the shared expert (if any).
+      // Lane j holds selection (j / K, j % K).
+      const int n = M * K;
+      const int mj = lane < n ? lane / K : 0, rj = lane - mj * K;
+      const int e = lane < n ? s_idx[mj][rj] : -1;
+      const float wj = lane < n ? s_w[mj][rj] : 0.0f;
+      bool first = lane < n;
+      unsigned mask = 0;
+      float wsum[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
+      for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
+      for (int i = 0; i < n; ++i) {
+        const int ei = __builtin_amdgcn_readlane(e, i);
+        const int mi = i / K;
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i));
+        if (ei == e) {
+          if (i < lane) first = false;
+          mask |= 1u << mi;
 #pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      if (cf[m][i]) {
-        const unsigned long long mine = rank_key(key[m][i], tid + kThreads * i);
-        const unsigned long long* cm = cand + m * E;
-        int rank = 0;
-        for (int q = 0; q < ncand[m] && rank < K; ++q) rank += cm[q] > mine ? 1 : 0;
-        if (rank < K) {
-          s_idx[m][rank] = tid + kThreads * i;
-          s_sel[m][rank] = key[m][i];
+          for (int m = 0; m < M; ++m)
+            if (m == mi) wsum[m] += wi;
         }
       }
-    }
-  }
-  __syncthreads();
-  stamp(w, l, 12);
-  if (wave == 0) {
-    // softmax over the selected logits of each token: lane l is selection (l / K, l % K); every
-    // lane of a token sums the same terms in the same order
-    const int n = M * K;
-    const int mj = lane < n ? lane / K : 0, rj = lane - mj * K;
-    const float z = lane < n ? expf(key_to_float(s_sel[mj][rj]) - key_to_float(s_sel[mj][0])) : 0.0f;
-    float s = 0.0f;   // sum of the token's K terms in rank order, the same in each of its lanes
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float sm = 0.0f;
-      for (int r = 0; r < K; ++r) sm += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), m * K + r));
-      s = m == mj ? sm : s;
-    }
-    float wj = 0.0f;
-    int e = -1;
-    if (lane < n) {
-      wj = z / s;
-      e = s_idx[mj][rj];
-      s_w[mj][rj] = wj;
-    }
-    // union in first-occurrence order over (token, rank); slot 0 is the shared expert (if any)
-    const int ns = sh.has_shared ? 1 : 0;
-    bool first = lane < n;
-    unsigned mask = 0;
-    float wsum[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
-    for (int i = 0; i < n; ++i) {
-      const int ei = __builtin_amdgcn_readlane(e, i);
-      const int mi = i / K;
-      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i));
-      if (ei == e) {
-        if (i < lane) first = false;
-        mask |= 1u << mi;
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          if (m == mi) wsum[m] += wi;
+      const unsigned long long firsts = __ballot(first);
+      const int cnt = first ? __popc(mask) : 0;
+      int pair0 = ns * M;
+      for (int i = 0; i < n; ++i) {
+        const int ci = __builtin_amdgcn_readlane(cnt, i);
+        pair0 += i < lane ? ci : 0;
       }
-    }
-    const unsigned long long firsts = __ballot(first);
-    const int cnt = first ? __popc(mask) : 0;
-    int pair0 = ns * M;
-    for (int i = 0; i < n; ++i) {
-      const int ci = __builtin_amdgcn_readlane(cnt, i);
-      pair0 += i < lane ? ci : 0;
-    }
-    const int slot = ns + __popcll(firsts & lt);
-    if (first) {
-      un.id[slot] = e;
-      un.mask[slot] = mask;
-      un.pair0[slot] = pair0;
+      const int slot = ns + __popcll(firsts & lt);
+      if (first) {
+        un.id[slot] = e;
+        un.mask[slot] = mask;
+        un.pair0[slot] = pair0;
 #pragma unroll
-      for (int m = 0; m < M; ++m) un.w[slot][m] = wsum[m];
-    }
+        for (int m = 0; m < M; ++m) un.w[slot][m] = wsum[m];
+      }
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const unsigned long long bm = __ballot(first && ((mask >> m) & 1u));
-      if (first && ((mask >> m) & 1u)) un.tok_pair[m][ns + __popcll(bm & lt)] = pair0 + __popc(mask & ((1u << m) - 1u));
+      for (int m = 0; m < M; ++m) {
+        const unsigned long long bm = __ballot(first && ((mask >> m) & 1u));
+        if (first && ((mask >> m) & 1u)) un.tok_pair[m][ns + __popcll(bm & lt)] = pair0 + __popc(mask & ((1u << m) - 1u));
+        if (lane == 0) {
+          un.tok_n[m] = ns + __popcll(bm);
+          if (ns) un.tok_pair[m][0] = m;
+        }
+      }
       if (lane == 0) {
-        un.tok_n[m] = ns + __popcll(bm);
-        if (ns) un.tok_pair[m][0] = m;
-      }
-    }
-    if (lane == 0) {
-      if (ns) {
-        un.id[0] = E;
-        un.mask[0] = (1u << M) - 1u;
-        un.pair0[0] = 0;
+        if (ns) {
+          un.id[0] = E;
+          un.mask[0] = (1u << M) - 1u;
+          un.pair0[0] = 0;
 #pragma unroll
-        for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
+          for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
+        }
+        int total = ns * M;
+        for (int i = 0; i < n; ++i) total += __builtin_amdgcn_readlane(cnt, i);
+        un.n = __popcll(firsts) + ns;
+        un.n_pairs = total;
       }
-      int total = ns * M;
-      for (int i = 0; i < n; ++i) total += __builtin_amdgcn_readlane(cnt, i);
-      un.n = __popcll(firsts) + ns;
-      un.n_pairs = total;
     }
   }
 }
@@ -605,14 +626,12 @@ __device__ __forceinline__ Layer desc_from_lds(const unsigned long long* raw) {
 
 template <int M>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
-                                                              int n_layers, Shape sh, Work w) {
+                                                              int n_layers, Shape sh_arg, Work w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ Union un;
   __shared__ int s_idx[kMaxM][kMaxK];
   __shared__ float s_w[kMaxM][kMaxK];
   __shared__ uint32_t s_sel[kMaxM][kMaxK];
-  __shared__ uint32_t s_wmax[kMaxM][kWaves];
-  __shared__ int s_cnt[kMaxM][kEpt][kWaves];
   __shared__ __attribute__((aligned(16))) float a_s[kMaxM * kBlk];
   __shared__ float s_y[kMaxM][kMaxRows];
   __shared__ __attribute__((aligned(16))) unsigned long long s_desc[2][kDescWords];
@@ -622,23 +641,21 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int G = gridDim.x, b = blockIdx.x;
+  const Shape& sh = sh_arg;
   const int E = sh.E, H = sh.H, I = sh.I, R = sh.R;
   const int J = I / kBlk;
-  const int ns = sh.has_shared ? 1 : 0;
 
-  // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates
-  // [M][E] u64, later this workgroup's partial sums [pairs][J][R] fp32
+  // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | a task's down block: codes [H][16]
+  // + scales [H] | scratch: selection candidates [M][E] u64, later this workgroup's partial sums
+  // [pairs][J][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
-  unsigned char* scratch = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
+  uint8_t* dn_s = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
+  unsigned char* scratch = dn_s + (size_t)H * 17;
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(scratch);
   float* red = reinterpret_cast<float*>(scratch);
 
-  const int row0 = b * R;
-  const int my_rows = max(0, min(R, H - row0));
-  const bool shared_task = sh.has_shared && b >= G - J;
-  const int r_row = b + G * wave;                       // this wave's router row
-  const bool is_router = wave < sh.nrw && r_row < E;
+  const int r_row0 = b + G * wave;                      // this wave's router row
   SyncState sync{0ull, false};
 
   // launch number -> this launch's tag base (every workgroup adds 1 per launch)
@@ -648,17 +665,17 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const uint32_t tag_base = (uint32_t)(s_launch * kTagsPerLaunch);
   if (s_launch > 0 && tag_base == 0) {
     // tags repeat from here on: clear every tagged word (tag 0 is never valid) before any use
-    const size_t own = (size_t)sh.P * J * R;
+    const size_t own = (size_t)sh.P * J * kLine;
     for (size_t i = tid; i < own; i += kThreads) st_coherent(w.partial + (size_t)b * own + i, 0ull);
-    for (int i = b * kThreads + tid; i < M * E; i += G * kThreads) st_coherent(w.logits + i, 0ull);
-    for (int i = b * kThreads + tid; i < M * H / 2; i += G * kThreads) st_coherent(w.ytag + i, 0ull);
-    if (tid == 0) st_coherent(w.done + b, 0ull);
+    for (int i = b * kThreads + tid; i < E * kLine; i += G * kThreads) st_coherent(w.logits + i, 0ull);
+    for (int i = tid; i < sh.y_stride; i += kThreads) st_coherent(w.ytag + (size_t)b * sh.y_stride + i, 0ull);
+    if (tid < kLine) st_coherent(w.done + (size_t)b * kLine + tid, 0ull);
     grid_sync(w, sync);
   }
 
   // router rows of layer 0 -> LDS (asynchronous; this wave waits for them before its dots)
-  if (is_router) {
-    const uint16_t* row = first.wr + (size_t)r_row * H;
+  if (wave < sh.nrw && r_row0 < E) {
+    const uint16_t* row = first.wr + (size_t)r_row0 * H;
     for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
       if (c0 + lane < (H >> 3))
         __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
@@ -667,11 +684,23 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   }
 
   for (int l = 0; l < n_layers; ++l) {
-    // an opaque copy of the thread index per layer: addresses derived from it are recomputed where
-    // they are used instead of being hoisted out of the layer loop and kept live (spilled) across it
+    // opaque copies of the thread index and the shape per layer: values derived from them are
+    // recomputed where they are used instead of being hoisted out of the layer loop and kept live
+    // (spilled to memory) across it
     unsigned tid_l = threadIdx.x;
     asm volatile("" : "+v"(tid_l));
     const int tid = (int)tid_l, lane = tid % kWave;   // shadow the kernel-level indices in this layer
+    Shape sh = sh_arg;
+    asm volatile("" : "+s"(sh.E), "+s"(sh.K), "+s"(sh.H), "+s"(sh.I), "+s"(sh.has_shared), "+s"(sh.R), "+s"(sh.P),
+                 "+s"(sh.chained), "+s"(sh.nrw), "+s"(sh.inv_r), "+s"(sh.y_stride), "+s"(sh.x_fresh));
+    const int E = sh.E, H = sh.H, I = sh.I, R = sh.R;
+    const int J = I / kBlk;
+    const int ns = sh.has_shared ? 1 : 0;
+    const int row0 = b * R;
+    const int my_rows = max(0, min(R, H - row0));
+    const bool shared_task = sh.has_shared && b >= G - J;
+    const int r_row = b + G * wave;                       // this wave's router row
+    const bool is_router = wave < sh.nrw && r_row < E;
     // descriptor of layer l: layer 0 from the kernel arguments, later ones from the LDS copy made
     // during the previous layer
     Layer L = first;
@@ -690,17 +719,23 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       for (int v = tid; v < M * H / 8; v += kThreads)
         *reinterpret_cast<u32x4_t*>(xs + v * 8) = ld16(L.x + (size_t)v * 8);
     } else if (sh.chained) {
-      // y of the previous layer, as its owners published it
-      const int n = M * H / 2;
+      // y of the previous layer, as its owners published it: bf16 pair i = (m, row 2q) of x
+      const int n = M * H / 2, half_r = R / 2;
       constexpr int kXw = (M * kHMax / 2 + kThreads - 1) / kThreads;
       int idx[kXw];
       unsigned long long v[kXw];
 #pragma unroll
-      for (int q = 0; q < kXw; ++q) idx[q] = tid + q * kThreads < n ? tid + q * kThreads : -1;
+      for (int q = 0; q < kXw; ++q) {
+        const int i = tid + q * kThreads, m = i / (H / 2), qq = i - m * (H / 2);
+        const int owner = (int)(((float)qq + 0.5f) * (2.0f * sh.inv_r));
+        idx[q] = i < n ? owner * sh.y_stride + m * half_r + (qq - owner * half_r) : -1;
+      }
       poll_tagged<kXw>(w, w.ytag, idx, tag_y - 4u, v);
 #pragma unroll
       for (int q = 0; q < kXw; ++q)
-        if (idx[q] >= 0) reinterpret_cast<uint32_t*>(xs)[idx[q]] = (uint32_t)v[q];
+        if (tid + q * kThreads < n) reinterpret_cast<uint32_t*>(xs)[tid + q * kThreads] = (uint32_t)v[q];
+    } else if (sh.x_fresh) {
+      wait_mem();   // this thread's copy of x into LDS, issued during the barrier, has landed
     } else {
       // x may have been written earlier in this launch: device-coherent loads
       const unsigned long long* src = reinterpret_cast<const unsigned long long*>(L.x);
@@ -729,14 +764,21 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           }
         }
       }
+      // bias loaded before any store: a wait for a load between the stores would also wait for the
+      // previous store's acknowledgement, slow while other workgroups poll these lines
+      float bias[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float s = wave_sum(acc[m]);
-        if (lane == 0) {
-          const float v = s + (L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f);
-          st_coherent(w.logits + (size_t)m * E + r_row, tagged(tag_lg, __float_as_uint(v)));
-          if (L.logits_out) stg(L.logits_out + (size_t)m * E + r_row, v);
-        }
+      for (int m = 0; m < M; ++m) bias[m] = L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f;
+      float lg[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) lg[m] = wave_sum(acc[m]) + bias[m];
+      if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          st_coherent(w.logits + (size_t)r_row * kLine + m, tagged(tag_lg, __float_as_uint(lg[m])));
+        if (L.logits_out)
+#pragma unroll
+          for (int m = 0; m < M; ++m) stg(L.logits_out + (size_t)m * E + r_row, lg[m]);
       }
     }
     if (has_next && wave == kWaves - 1 && lane < kDescWords) s_desc[(l + 1) & 1][lane] = next_desc;
@@ -751,13 +793,15 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       TaskRegs sreg;
-      task_load(L, sh, E, b - (G - J), tid, sreg);
-      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, a_s, tid, tag_pt);
+      task_load(L, sh, E, b - (G - J), tid, sreg, dn_s);
+      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, a_s, dn_s, tid, tag_pt);
     }
     stamp(w, l, 3);
 
     // ------------------------------------------------------------------ 3: top-K and union
-    select_topk<M>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_wmax, s_cnt, s_sel, l);
+    // a lane holds experts lane + 64 q for q < kQ: 8 registers suffice up to 512 experts
+    if (E <= 8 * kWave) select_topk<M, 8>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+    else select_topk<M, kMaxE / kWave>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
     if (b == 0 && tid < M * sh.K) {
       const int m = tid / sh.K, r = tid - m * sh.K;
       if (L.topk_idx) stg(L.topk_idx + tid, s_idx[m][r]);
@@ -784,24 +828,26 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       for (int q = b; q < n_rt; q += G) {
         TaskRegs cur;
         const int u = ns + q / J;
-        task_load(L, sh, un.id[u], q % J, tid, cur);
-        task_compute<M>(sh, w, cur, un, u, q % J, xs, a_s, tid, tag_pt);
+        task_load(L, sh, un.id[u], q % J, tid, cur, dn_s);
+        task_compute<M>(sh, w, cur, un, u, q % J, xs, a_s, dn_s, tid, tag_pt);
       }
     }
     stamp(w, l, 6);
 
     // ------------------------------------------------------------------ 5: combine owned rows
     if (my_rows > 0) {
-      const int np = un.n_pairs;
-      const int n_words = np * J * R;
-      const unsigned long long* src = w.partial + (size_t)b * sh.P * J * R;
-      for (int base = 0; base < n_words; base += kPollBatch * kThreads) {
+      // slot (pair, block, row) at (p * J + j) * kLine + row: lane group tid / kLine takes one
+      // (pair, block) per batch step, lanes with row >= my_rows idle
+      const int n_slots = un.n_pairs * J * kLine;
+      const unsigned long long* src = w.partial + (size_t)b * sh.P * J * kLine;
+      const bool my_row = (tid % kLine) < my_rows;
+      for (int base = 0; base < n_slots; base += kPollBatch * kThreads) {
         int idx[kPollBatch];
         unsigned long long v[kPollBatch];
 #pragma unroll
         for (int q = 0; q < kPollBatch; ++q) {
           const int i = base + tid + q * kThreads;
-          idx[q] = i < n_words ? i : -1;
+          idx[q] = i < n_slots && my_row ? i : -1;
         }
         poll_tagged<kPollBatch>(w, src, idx, tag_pt, v);
 #pragma unroll
@@ -810,19 +856,29 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       stamp(w, l, 7);
-      // y[m][row] = sum over token m's pairs (slot order) and blocks; kSumLanes lanes per (m, row)
+      // y[m][row] = sum over token m's pairs and blocks. sum_lanes<M>() lanes share a (m, row): lane s
+      // takes blocks j = s % 8 (mod 8) of pairs i = s / 8 (mod lanes / 8), in a fixed order; then a
+      // fixed-order DPP reduction (deterministic)
       {
-        const int grp = tid / kSumLanes, s = tid % kSumLanes;
+        constexpr int W = sum_lanes<M>(), WP = W / kBlkLanes;
+        const int grp = tid / W, s = tid % W;
         const int m = grp / kMaxRows, rl = grp % kMaxRows;
+        const int sp = s / kBlkLanes, sj = s % kBlkLanes;
         float acc = 0.0f;
         if (m < M && rl < my_rows) {
           const int npm = un.tok_n[m];
-          for (int i = 0; i < npm; ++i) {
-            const float* rp = red + (size_t)un.tok_pair[m][i] * J * R + rl;
-            for (int j = s; j < J; j += kSumLanes) acc += rp[j * R];
+          for (int i = sp; i < npm; i += WP) {
+            const float* rp = red + (size_t)un.tok_pair[m][i] * J * kLine + rl;
+#pragma unroll
+            for (int jj = 0; jj < kIMax / kBlk / kBlkLanes; ++jj) {
+              const int j = sj + jj * kBlkLanes;
+              if (j < J) acc += rp[j * kLine];
+            }
           }
         }
         acc = row8_sum(acc);
+        if constexpr (W >= 16) acc = row16_sum_of_row8(acc);
+        if constexpr (W >= 32) acc += __shfl_xor(acc, 16, kWave);
         if (s == 0 && m < M && rl < my_rows) s_y[m][rl] = acc;
       }
       __syncthreads();
@@ -842,12 +898,16 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           st_coherent(L.y16 + o + 1, h1);
         }
         if (sh.chained && l + 1 < n_layers)
-          st_coherent(w.ytag + o / 2, tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
+          st_coherent(w.ytag + (size_t)b * sh.y_stride + m * (R / 2) + rp, tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
       }
     }
     stamp(w, l, 8);
     if (!sh.chained && l + 1 < n_layers) {
-      tagged_barrier(w, tag_y, tid, l);   // layer l's output is written before layer l+1 starts
+      // layer l's output is written before layer l+1 starts
+      const uint16_t* next_x = nullptr;
+      if (sh.x_fresh)
+        next_x = reinterpret_cast<const uint16_t*>(uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, x_bf16) / 8]));
+      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H);
       stamp(w, l, 9);
     } else {
       __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer
@@ -877,18 +937,24 @@ unsigned long long* g_trace[64];  // per device: trace buffer registered by qws_
 size_t g_trace_bytes[64];
 constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 
-size_t lds_bytes(int M, int E, int H, int P, int J, int R, int nrw) {
-  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * R * 4;
-  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + (sel > comb ? sel : comb);
+size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
+  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * kLine * 4;
+  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + (size_t)H * 17 + (sel > comb ? sel : comb);
 }
+
+// n words rounded up to whole 128-byte lines
+constexpr int line_words(int n) { return (n + kLine - 1) / kLine * kLine; }
 
 size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
   const size_t sync = qws_host::align256(kSyncCounters * kSyncStride * 8);
   const size_t misc = 256;   // launch counter, error count
-  const size_t lg = qws_host::align256((size_t)M * E * 8);
-  const size_t yt = qws_host::align256((size_t)M * H * 4);
-  const size_t dn = qws_host::align256((size_t)kMaxGrid * 8);
-  const size_t part = qws_host::align256((size_t)M * (K + 1) * (I / kBlk) * (H + kRowsPad) * 8);
+  // sized for the largest grid and per-workgroup strides (kWaves router rows, kMaxRows owned rows)
+  (void)E;
+  (void)H;
+  const size_t lg = qws_host::align256((size_t)kMaxE * kLine * 8);
+  const size_t yt = qws_host::align256((size_t)kMaxGrid * line_words(M * kMaxRows / 2) * 8);
+  const size_t dn = qws_host::align256((size_t)kMaxGrid * kLine * 8);
+  const size_t part = qws_host::align256((size_t)kMaxGrid * M * (K + 1) * (I / kBlk) * kLine * 8);
   if (w) {
     w->trace = nullptr;
     w->sync = reinterpret_cast<unsigned long long*>(base);
@@ -973,11 +1039,9 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   const int J = I / kBlk;
   const int nrw = (E + G - 1) / G;
   const int R = ((H + G - 1) / G + 1) & ~1;   // even, so a thread writes a bf16 pair of one token
-  if (G > kMaxGrid || G < J || nrw > kWaves || R > kMaxRows || (size_t)G * R > (size_t)H + kRowsPad ||
-      G * R > kThreads * kDnRpl || M * kMaxRows * kSumLanes > kThreads)
-    return QWS_ERR_SHAPE;
+  if (G > kMaxGrid || G < J || nrw > kWaves || R > kMaxRows) return QWS_ERR_SHAPE;
   const int P = M * (K + 1);
-  const size_t lds = lds_bytes(M, E, H, P, J, R, nrw);
+  const size_t lds = lds_bytes(M, E, H, P, J, nrw);
   if (lds > kMaxDynLds) return QWS_ERR_SHAPE;
   // Chained: layer l+1 reads y of layer l. Then the layers need no barrier, provided every
   // workgroup computes router rows and owns output rows, so that no workgroup can fall a layer
@@ -993,7 +1057,28 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
     const size_t need = (size_t)n_layers * G * kTracePoints * 8;
     w.trace = (dev >= 0 && dev < 64 && g_trace[dev] && g_trace_bytes[dev] >= need) ? g_trace[dev] : nullptr;
   }
-  const Shape sh{E, K, H, I, hs, R, P, chained ? 1 : 0, G * R, nrw};
+  // x_fresh: no layer's x overlaps an output of any layer of this launch (all x were written before it)
+  bool x_fresh = !chained;
+  {
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+      const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+      return a && b && pa < pb + nb && pb < pa + na;
+    };
+    for (int l = 1; x_fresh && l < n_layers; ++l) {
+      const size_t nx = (size_t)M * H * 2;
+      for (int o = 0; x_fresh && o < n_layers; ++o) {
+        const qws_moe_layer& d = host[o];
+        if (overlap(host[l].x_bf16, nx, d.y_bf16, (size_t)M * H * 2) ||
+            overlap(host[l].x_bf16, nx, d.y_f32, (size_t)M * H * 4) ||
+            overlap(host[l].x_bf16, nx, d.topk_idx, (size_t)M * K * 4) ||
+            overlap(host[l].x_bf16, nx, d.topk_w, (size_t)M * K * 4) ||
+            overlap(host[l].x_bf16, nx, d.logits_out, (size_t)M * E * 4))
+          x_fresh = false;
+      }
+    }
+  }
+  const Shape sh{E, K, H, I, hs, R, P, chained ? 1 : 0, nrw, 1.0f / (float)R, line_words(M * R / 2),
+                 x_fresh ? 1 : 0};
   const Layer first = to_layer(host[0]);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (M) {

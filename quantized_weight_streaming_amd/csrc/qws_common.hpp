@@ -116,6 +116,8 @@ __device__ __forceinline__ float row8_sum(float v) {
   v = dpp_add<0x141>(v);
   return v;
 }
+// After row8_sum: each lane gets the sum of its 16-lane row (adds the other half-row's sum).
+__device__ __forceinline__ float row16_sum_of_row8(float v) { return dpp_add<0x140>(v); }
 // Wave-uniform sum of 64 lanes: 16-lane sums, then row 15 -> next row and lane 31 -> rows 2, 3
 // broadcasts; lane 63 ends with the total. The order of additions is fixed.
 __device__ __forceinline__ float wave_sum(float v) {
