@@ -114,13 +114,19 @@ class MoeLayer:
     """Device-resident inputs and outputs of one MoE layer, runnable through the fused one-launch
     entry point or through the two-call path (router kernel, then the expert kernels)."""
 
-    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None, packed=None, x=None):
+    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None, packed=None, x=None, keep_canonical=True):
         import torch
         import synth
         shape = synth.LayerShape()
-        self.bank_t = bank if bank is not None else synth.expert_bank_torch(seed, layer, shape, device=dev)
-        self.bank = qws.ExpertBank.from_dict(self.bank_t, shape.n_routed, True)       # canonical: two-call path
-        self.packed = packed if packed is not None else qws.moe_pack_mxfp4(self.bank)  # block-major: fused path
+        # canonical bank: the two-call path; task-major copy: the fused path. Layers that only run
+        # fused drop the canonical bank once packed (a 42-layer step then holds ~70 GB, not ~137)
+        self.bank_t = bank
+        if self.bank_t is None and (packed is None or keep_canonical):
+            self.bank_t = synth.expert_bank_torch(seed, layer, shape, device=dev)
+        self.bank = None if self.bank_t is None else qws.ExpertBank.from_dict(self.bank_t, shape.n_routed, True)
+        self.packed = packed if packed is not None else qws.moe_pack_mxfp4(self.bank)
+        if not keep_canonical:
+            self.bank_t, self.bank = None, None
         self.wr = _bf16(synth.router_weights(seed, layer, shape.n_routed), dev)
         self.x = x if x is not None else _bf16(synth.token_vectors(seed, layer, M), dev)
         self.bias = None if bias is None else torch.from_numpy(bias).to(dev)
@@ -159,15 +165,15 @@ def probe_ceiling(qws, dev):
 class DecodeStep:
     """42 independent MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head."""
 
-    def __init__(self, qws, M, dev, n_layers, head, banks=None, packed=None):
+    def __init__(self, qws, M, dev, n_layers, head, packed=None):
         import torch
         import synth
         self.qws, self.M, self.dev = qws, M, dev
         log(f"building {n_layers} layers (M={M})")
         self.layers = []
         for l in range(n_layers):
-            self.layers.append(MoeLayer(qws, 0, l, M, dev, bank=None if banks is None else banks[l],
-                                        packed=None if packed is None else packed[l]))
+            self.layers.append(MoeLayer(qws, 0, l, M, dev, packed=None if packed is None else packed[l],
+                                        keep_canonical=False))
         self.seq = qws.MoeLayers([L.fused for L in self.layers])
         self.ws = qws.moe_layer_workspace(M, K_TOP, 512, 2560, 768, dev)
         self.xh = _bf16(synth.token_vectors(0, 1000, M), dev)
@@ -341,13 +347,13 @@ def main():
         wse1 = qws.expert_workspace(1, K_TOP, 2560, 768, dev)
         lay = {}
         L0 = step.layers[0]
-        lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, bank=L0.bank_t, packed=L0.packed)
+        lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, packed=L0.packed)   # canonical again: two-call path
         bank1 = synth.expert_bank_torch(1, 0, synth.LayerShape(), device=dev)
         lay["moe_layer_m1_seed1_zipf"] = MoeLayer(qws, 1, 0, 1, dev, bias=synth.zipf_bias(1, 0, 512), bank=bank1)
         for reg in synth.REGIMES:
             sets = synth.regime_sets(0, 0, reg, 4, 512)
-            lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), bank=L0.bank_t,
-                                                 packed=L0.packed)
+            lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), packed=L0.packed,
+                                                 keep_canonical=False)
         for name, Lr in lay.items():
             t = time_cold(lambda: Lr.run(wsf[Lr.M]), dev, flush=flush)
             u = Lr.union()
@@ -375,8 +381,7 @@ def main():
             breakdown[name] = t
             log(name, t)
         # decode step at M = 4 (natural routing), sharing the M = 1 step's expert banks
-        step4 = DecodeStep(qws, 4, dev, args.layers, head8, banks=[L.bank_t for L in step.layers],
-                           packed=[L.packed for L in step.layers])
+        step4 = DecodeStep(qws, 4, dev, args.layers, head8, packed=[L.packed for L in step.layers])
         step4.layers_call()
         torch.cuda.synchronize(dev)
         r4 = step4.timed(max(5, args.steps // 2), 2)

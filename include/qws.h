@@ -50,7 +50,7 @@ enum qws_format {
   QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634, /* e2m1 nibbles + one E8M0 scale per 32 elements */
   QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes + one fp32 scale per row */
   QWS_FMT_BF16 = 0x42463136,                /* plain bf16 */
-  QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR = 0x4D584642 /* MXFP4 experts, down block-major */
+  QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654 /* MXFP4 experts, task-major (moe_pack_mxfp4) */
 };
 
 /* Text for a status code. For QWS_ERR_DEVICE the text of the calling thread's last HIP error is
@@ -105,7 +105,7 @@ int moe_route_topk(const void* x_bf16, int M, int H, const void* w_router_bf16, 
  * kernels compile at run time ..."); element and scale encodings are OCP MX v1.0.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
-  unsigned format; /* QWS_FMT_MXFP4_E2M1_E8M0_B32, or ..._DOWN_BLOCKMAJOR after moe_pack_mxfp4 */
+  unsigned format; /* QWS_FMT_MXFP4_E2M1_E8M0_B32, or ..._TASKMAJOR after moe_pack_mxfp4 */
   int n_routed;    /* 1 .. 1024 */
   int has_shared;  /* 0 or 1 */
   int hidden;      /* H: multiple of 32, 32 .. 2560 */
@@ -140,19 +140,32 @@ int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
                           qws_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
- * Block-major down projection for the fused entry points (a one-off conversion at load time,
- * like lmhead_quantize_fp8). The fused layer splits each expert's FFN into blocks of 32
- * activations; block j needs columns 32j .. 32j+31 of the down projection for every output row,
- * which this layout stores contiguously:
- *   down_q_out [n][I/32][H][16] bytes: [e][j][row] = canonical down_q[e][row][16j .. 16j+15]
- *   down_s_out [n][I/32][H]           : [e][j][row] = canonical down_s[e][row][j]
- * (n = n_routed + has_shared; the codes themselves are unchanged). desc_out receives `src` with
- * the down pointers replaced and format QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR; the gate_up
- * arrays are shared with `src`, which must stay valid. src must be canonical (QWS_ERR_FORMAT
- * otherwise); down_q_out 16-byte aligned; the outputs must not overlap the inputs.
+ * Task-major copy of an MXFP4 bank for the fused entry points (a one-off conversion at load
+ * time, like lmhead_quantize_fp8; the codes and scales are moved, never changed). The fused layer
+ * splits each expert's FFN into tasks of 32 activations: task (e, j) needs gate rows 32j .. 32j+31,
+ * up rows I+32j .. I+32j+31 and columns 32j .. 32j+31 of every down-projection row. The copy stores
+ * each task as one record of QWS_TASK_BYTES bytes, in the order in which the 16 waves x 64 lanes
+ * of a workgroup read it, so that every load instruction of a wave reads 1 KB of consecutive
+ * bytes:
+ *   out[(e * I/32 + j) * QWS_TASK_BYTES + ((p * 16 + w) * 64 + l) * 16 + b],  p < 8 pieces,
+ * with w = 4 rg + ks, l = 16 g + i:
+ *   p 0     bytes 0..7: 4-byte words q = 8, 9 (below); bytes 8..12: the scales of the five
+ *           gate/up chunks of p 1..5; bytes 13..15: bytes 3 l .. 3 l + 2 of the wave's 160 down
+ *           scales, [q][i] = scale of down row 16 (w + 16 q) + i in block j;
+ *   p 1..5  gate/up codes: row i of row group rg (gate 32j + 16 rg + i for rg < 2, else up
+ *           I + 32j + 16 (rg - 2) + i), 16-byte chunk 20 ks + 4 (p - 1) + g of the row;
+ *   p 6, 7  4-byte words q = 4 (p - 6) .. +3: word q is bytes 4g .. 4g+3 of down row
+ *           16 (w + 16 q) + i in its columns 32j .. 32j+31.
+ * Chunks, rows and scales past H are zero. n = n_routed + has_shared; H <= 2560 (16 x 5 x 32
+ * elements per row), I a multiple of 32. desc_out receives `src` with format
+ * QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, gate_up_q = out and the other three pointers NULL.
+ * src must be canonical (QWS_ERR_FORMAT otherwise); out 16-byte aligned, out_bytes at least
+ * moe_pack_mxfp4_bytes(n, H, I), not overlapping the bank.
  * -------------------------------------------------------------------------------------------*/
-int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* down_q_out, unsigned char* down_s_out,
-                   qws_mxfp4_experts* desc_out, qws_stream_t stream);
+#define QWS_TASK_BYTES 131072
+size_t moe_pack_mxfp4_bytes(int n_experts, int hidden, int inter); /* 0 for an unsupported shape */
+int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* out, size_t out_bytes, qws_mxfp4_experts* desc_out,
+                   qws_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * One MoE layer in ONE launch: router GEMV, top-K, softmax, expert union, MXFP4 gate_up + SwiGLU,
@@ -161,9 +174,11 @@ int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* down_q_out, unsi
  * (each costs ~1.7 us on MI355X, a third of a layer's streaming time at M = 1). The grid is one
  * persistent workgroup per compute unit. Its hand-offs are 64-bit words that carry a 32-bit value
  * with a tag unique to (launch, layer, kind), so a reader polls the data itself. Experts must be
- * packed by moe_pack_mxfp4 (QWS_ERR_FORMAT otherwise). The down projection is summed per block of
- * 32 activations and then over blocks, so results agree with moe_expert_gemv_mxfp4 to float32
- * rounding, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
+ * packed by moe_pack_mxfp4 (QWS_ERR_FORMAT otherwise). The expert products run on the matrix
+ * cores (bf16 operands, exact dequantisation of e2m1 x E8M0; the fp32 SwiGLU activation enters as
+ * the exact sum of three bf16 parts; fp32 accumulation), and the down projection is summed per
+ * block of 32 activations and then over blocks, so results agree with moe_expert_gemv_mxfp4 to
+ * float32 rounding, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   const void* x_bf16;         /* [M, H] bf16, ready before the launch                               */

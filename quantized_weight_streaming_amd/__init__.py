@@ -6,7 +6,7 @@ if libqws.so is missing, the first call raises (there is no CPU fallback).
 
     route  = moe_route_topk(x, w_router, K)               # router GEMV + top-K + softmax
     y      = moe_expert_gemv_mxfp4(bank, x, idx, w)       # union of experts, SwiGLU, combine
-    packed = moe_pack_mxfp4(bank)                         # block-major down, once per bank
+    packed = moe_pack_mxfp4(bank)                         # task-major copy, once per bank
     layer  = moe_layer_mxfp4(MoeLayer(x, w_router, packed, K))   # the whole layer, one launch
     head   = lmhead_quantize_fp8(w_head_bf16)             # online FP8 head, once
     logits = lmhead_gemv_fp8(head, x)
@@ -15,13 +15,14 @@ from __future__ import annotations
 
 import ctypes as C
 from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
 from . import _lib
 from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32,  # noqa: F401
-                   QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR, LMHeadDesc, MoeLayerDesc, MxFp4Experts, QwsError,
-                   check)
+                   QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, QWS_TASK_BYTES, LMHeadDesc, MoeLayerDesc, MxFp4Experts,
+                   QwsError, check)
 
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
            "lmhead_bf16",
@@ -97,38 +98,41 @@ class ExpertBank:
 
     layout "canonical": gate_up_q [n, 2I, H/2], gate_up_s [n, 2I, H/32], down_q [n, H, I/2],
     down_s [n, H, I/32] (row-major per expert).
-    layout "down_blockmajor" (from moe_pack_mxfp4): gate_up as above, down_q [n, I/32, H*16],
-    down_s [n, I/32, H] -- block j of the down projection stored contiguously for all rows."""
+    layout "task_major" (from moe_pack_mxfp4): gate_up_q holds the task records [n, I/32,
+    QWS_TASK_BYTES] (the layout is stated with moe_pack_mxfp4 in include/qws.h); the other three
+    are None and `hidden` must be given."""
     gate_up_q: torch.Tensor
-    gate_up_s: torch.Tensor
-    down_q: torch.Tensor
-    down_s: torch.Tensor
+    gate_up_s: Optional[torch.Tensor]
+    down_q: Optional[torch.Tensor]
+    down_s: Optional[torch.Tensor]
     n_routed: int
     has_shared: bool = True
     layout: str = "canonical"
+    hidden: int = 0
 
     def __post_init__(self):
         n = self.n_routed + int(self.has_shared)
-        two_i, hb = self.gate_up_q.shape[1:]
-        H, I = hb * 2, two_i // 2
         if self.layout == "canonical":
-            down = (("down_q", self.down_q, (n, H, I // 2)), ("down_s", self.down_s, (n, H, I // 32)))
+            two_i, hb = self.gate_up_q.shape[1:]
+            H, I = hb * 2, two_i // 2
+            checks = (("gate_up_q", self.gate_up_q, (n, two_i, hb)), ("gate_up_s", self.gate_up_s, (n, two_i, H // 32)),
+                      ("down_q", self.down_q, (n, H, I // 2)), ("down_s", self.down_s, (n, H, I // 32)))
             fmt = QWS_FMT_MXFP4_E2M1_E8M0_B32
-        elif self.layout == "down_blockmajor":
-            down = (("down_q", self.down_q, (n, I // 32, H * 16)), ("down_s", self.down_s, (n, I // 32, H)))
-            fmt = QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR
+            ptrs = [t.data_ptr() for t in (self.gate_up_q, self.gate_up_s, self.down_q, self.down_s)]
+        elif self.layout == "task_major":
+            H, I = self.hidden, self.gate_up_q.shape[1] * 32
+            checks = (("records", self.gate_up_q, (n, I // 32, QWS_TASK_BYTES)),)
+            fmt = QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR
+            ptrs = [self.gate_up_q.data_ptr(), None, None, None]
         else:
             raise ValueError(f"unknown layout {self.layout!r}")
-        for name, t, shape in (("gate_up_q", self.gate_up_q, (n, two_i, hb)),
-                               ("gate_up_s", self.gate_up_s, (n, two_i, H // 32))) + down:
+        for name, t, shape in checks:
             _need(t, name, torch.uint8, 3)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
         self.hidden = H
         self.inter = I
-        self.desc = MxFp4Experts(fmt, self.n_routed, int(self.has_shared), self.hidden, self.inter,
-                                 self.gate_up_q.data_ptr(), self.gate_up_s.data_ptr(), self.down_q.data_ptr(),
-                                 self.down_s.data_ptr())
+        self.desc = MxFp4Experts(fmt, self.n_routed, int(self.has_shared), self.hidden, self.inter, *ptrs)
 
     @classmethod
     def from_dict(cls, d: dict, n_routed: int, has_shared: bool = True):
@@ -136,18 +140,20 @@ class ExpertBank:
 
 
 def moe_pack_mxfp4(bank: ExpertBank) -> ExpertBank:
-    """The bank with its down projection re-laid block-major for the fused entry points (new down
-    tensors; gate_up tensors shared with `bank`)."""
+    """A task-major copy of the bank for the fused entry points (new record tensor; `bank` is not
+    referenced afterwards and may be freed)."""
     if bank.layout != "canonical":
         raise ValueError("moe_pack_mxfp4 needs a canonical bank")
     n = bank.n_routed + int(bank.has_shared)
-    dev = bank.down_q.device
-    dq = torch.empty((n, bank.inter // 32, bank.hidden * 16), dtype=torch.uint8, device=dev)
-    ds = torch.empty((n, bank.inter // 32, bank.hidden), dtype=torch.uint8, device=dev)
+    dev = bank.gate_up_q.device
+    nbytes = lib().moe_pack_mxfp4_bytes(n, bank.hidden, bank.inter)
+    if nbytes == 0:
+        raise ValueError("unsupported expert shape for the task-major pack")
+    rec = torch.empty((n, bank.inter // 32, QWS_TASK_BYTES), dtype=torch.uint8, device=dev)
     out = MxFp4Experts()
-    st = lib().moe_pack_mxfp4(C.byref(bank.desc), _p(dq), _p(ds), C.byref(out), _stream(dev))
+    st = lib().moe_pack_mxfp4(C.byref(bank.desc), _p(rec), rec.numel(), C.byref(out), _stream(dev))
     check("moe_pack_mxfp4", st)
-    return ExpertBank(bank.gate_up_q, bank.gate_up_s, dq, ds, bank.n_routed, bank.has_shared, "down_blockmajor")
+    return ExpertBank(rec, None, None, None, bank.n_routed, bank.has_shared, "task_major", hidden=bank.hidden)
 
 
 def expert_workspace(M: int, K: int, hidden: int, inter: int, device) -> torch.Tensor:
@@ -193,7 +199,7 @@ class MoeLayer:
 
     def __init__(self, x, w_router, bank: ExpertBank, K: int, bias=None, y_bf16=None, y_f32=None,
                  topk_idx=None, topk_w=None, logits_out=None, want_bf16=True, want_f32=True):
-        if bank.layout != "down_blockmajor":
+        if bank.layout != "task_major":
             raise ValueError("the fused entry points need a bank packed by moe_pack_mxfp4")
         _need(x, "x", torch.bfloat16, 2)
         _need(w_router, "w_router", torch.bfloat16, 2)

@@ -19,7 +19,8 @@ QWS_ERR_SELFCHECK = -7
 QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634
 QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845
 QWS_FMT_BF16 = 0x42463136
-QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR = 0x4D584642
+QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654
+QWS_TASK_BYTES = 131072
 
 
 class MxFp4Experts(C.Structure):
@@ -53,7 +54,8 @@ SIGNATURES = {
     "moe_route_topk": (_I, [_P, _I, _I, _P, _I, _P, _LL, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moe_expert_gemv_mxfp4": (_I, [C.POINTER(MxFp4Experts), _P, _I, _P, _P, _I, _P, _P, _P, _SZ, _P]),
-    "moe_pack_mxfp4": (_I, [C.POINTER(MxFp4Experts), _P, _P, C.POINTER(MxFp4Experts), _P]),
+    "moe_pack_mxfp4_bytes": (_SZ, [_I, _I, _I]),
+    "moe_pack_mxfp4": (_I, [C.POINTER(MxFp4Experts), _P, _SZ, C.POINTER(MxFp4Experts), _P]),
     "moe_layer_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_layer_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _I, _I, _P, _SZ, _P]),
     "moe_layers_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _P, _I, _I, _I, _P, _SZ, _P]),

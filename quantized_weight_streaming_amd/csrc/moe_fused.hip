@@ -5,18 +5,20 @@
 // paragraph 5).
 //
 // Why one launch: a kernel boundary costs ~1.7 us on MI355X even inside a HIP graph, about a third
-// of a layer's streaming time at M = 1. The grid is one 512-thread workgroup per compute unit, all
-// resident at once.
+// of a layer's streaming time at M = 1. The grid is one 1024-thread workgroup per compute unit,
+// all resident at once.
 //
 // Work decomposition. A "task" is (slot u, block j): the 32 gate rows and 32 up rows of activation
 // block j of expert id(u), plus the 32-column block j of that expert's down projection for all H
 // output rows. One workgroup issues all of a task's loads in one burst (2 x 32 x H/2 gate/up bytes
 // + H x 16 down bytes: 120 KB of codes at H = 2560), computes the block's 32 activations itself --
 // activations never cross workgroups -- and writes H partial sums per token, already multiplied by
-// the token's gate weight. The down projection is stored block-major (moe_pack_mxfp4) so that
-// block j of an expert is one contiguous stream. Weights are read with non-temporal loads: each
-// byte is used once per step, and on MI355X a burst of such loads streams ~2x faster than cached
-// loads when the caches hold dirty lines.
+// the token's gate weight. Experts are stored task-major (moe_pack_mxfp4): a task is one 128 KB
+// record in the order its 16 waves read it, so each of a lane's eight loads is part of a 1 KB
+// run per wave. On MI355X one compute unit streams ~20 GB/s however its loads are shaped, but
+// many narrow or scattered loads per lane lower that further. Weights are read with
+// non-temporal loads: each byte is used once per step, and a burst of such loads streams ~2x
+// faster than cached loads when the caches hold dirty lines.
 //
 // Hand-offs between workgroups carry their own validity: a 64-bit word holds a 32-bit value and a
 // 32-bit tag unique to (launch, layer, kind), written with one device-coherent store and polled
@@ -82,10 +84,7 @@ struct Layer {
   const uint16_t* wr;
   const float* bias;
   long long bias_stride;
-  const uint8_t* gq;
-  const uint8_t* gs;
-  const uint8_t* dq;   // block-major [n][I/32][H][16]
-  const uint8_t* ds;   // block-major [n][I/32][H]
+  const uint8_t* rec;   // task-major experts: record (e, j) at (e * I/32 + j) * kTaskBytes
   int* topk_idx;
   float* topk_w;
   float* logits_out;
@@ -95,8 +94,7 @@ struct Layer {
 
 __host__ __device__ Layer to_layer(const qws_moe_layer& d) {
   return Layer{static_cast<const uint16_t*>(d.x_bf16), static_cast<const uint16_t*>(d.w_router_bf16), d.bias,
-               d.bias_row_stride, d.experts.gate_up_q, d.experts.gate_up_s, d.experts.down_q, d.experts.down_s,
-               d.topk_idx, d.topk_w, d.logits_out, static_cast<uint16_t*>(d.y_bf16), d.y_f32};
+               d.bias_row_stride, d.experts.gate_up_q, d.topk_idx, d.topk_w, d.logits_out, static_cast<uint16_t*>(d.y_bf16), d.y_f32};
 }
 
 struct Shape {
@@ -280,156 +278,145 @@ __device__ __forceinline__ unsigned long long rank_key(uint32_t key, int e) {
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);
 }
+__device__ __forceinline__ uint32_t ld4_stream(const void* p) {
+  return __builtin_nontemporal_load((const QWS_GLOBAL uint32_t*)p);
+}
 __device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
   return __builtin_nontemporal_load((const QWS_GLOBAL uint8_t*)p);
 }
 
 // ------------------------------------------------------------------------------ tasks
+// A task is (expert e, block j): gate rows 32j .. 32j+31 and up rows I+32j .. I+32j+31 of expert
+// e, whose SwiGLU gives activations 32j .. 32j+31, then the H x 32 slice of the down projection
+// that multiplies them. Both products run on the matrix cores (MFMA 16x16x32, bf16 operands
+// dequantised exactly from e2m1 x E8M0, fp32 accumulation), with the tokens as the MFMA's 16
+// columns. Gate/up: wave w takes row group rg = w / 4 (16 rows: gate 0-15, gate 16-31, up 0-15,
+// up 16-31 of the block) and k-slice ks = w % 4 (chunks 20ks .. 20ks+19 of those rows; a chunk is
+// 16 bytes = 32 codes = one MX block); MFMA lane (g, i) = (lane / 16, lane % 16) supplies row i at
+// k-group g, i.e. chunk 20ks + 4t + g for t < 5. Down: wave w takes the 16-row tiles w + 16q
+// (q < 10) of the block; lane (g, i) supplies word g (codes 8g .. 8g+7) of tile row i. The
+// task-major record (moe_pack_mxfp4) holds exactly these operands, lane by lane, in eight 16-byte
+// pieces per lane; the first carries the scales, so the first gate/up chunk waits for two loads.
+constexpr int kGuCpk = 4 * kGuCpl;            // chunks of a row per k-slice: H <= 4 * 20 * 32
+constexpr int kDnTpw = kHMax / 16 / kWaves;   // down-projection row tiles (16 rows) per wave
+constexpr int kPieces = 8;                    // 16-byte pieces per lane of a task record
+constexpr int kTaskBytes = kPieces * kThreads * 16;
+static_assert(kTaskBytes == QWS_TASK_BYTES, "task record size");
+static_assert(kGuCpl == 5 && kDnTpw == 10, "piece layout: 5 gate/up chunks + 10 down words + scales per lane");
 struct TaskRegs {
-  u32x4_t q[kGuCpl];
-  uint32_t qs[kGuCpl];
+  u32x4_t p[kPieces];   // piece 0: down words q 8, 9 + scales; 1-5: gate/up chunks t; 6, 7: down words q 0..7
 };
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)src, (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
-}
-
-// Issues the loads of task (expert e, block j). 32-lane group p = tid / 32 takes activation 32j+p:
-// its lanes 0-15 gate row 32j+p, lanes 16-31 up row I+32j+p (lane j16: chunks j16, j16+16, ...)
-// into registers. The block's down-projection codes (H x 16 bytes, contiguous in the block-major
-// layout) and scales (H bytes) go to LDS by DMA, issued after the gate/up loads so that waiting
-// for a gate/up chunk never waits for them (vector memory operations complete in order).
-__device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r,
-                                          uint8_t* dn_s) {
-  const unsigned p = tid >> 5, up = (tid >> 4) & 1u, j16 = tid & 15;
-  const int H = sh.H, I = sh.I, J = I / kBlk;
-  const unsigned nch = (unsigned)(H >> 5), rb = (unsigned)(H >> 1);
-  const size_t row = (size_t)e * 2 * I + (size_t)kBlk * j + p + (up ? (size_t)I : 0);
-  const uint8_t* rq = L.gq + row * rb;
-  const uint8_t* rs = L.gs + row * nch;
-  // unconditional loads from clamped (in-bounds) addresses: no branch around a load, so a task's
-  // loads issue back to back; a chunk past the row end is masked by the compute
+// Issues the eight loads of task (expert e, block j) into registers, piece by piece: for each
+// piece, the 64 lanes of a wave read 1 KB of consecutive bytes. All are plain vector loads: vector
+// memory operations of one kind complete in order, so the compute can wait for each gate/up chunk
+// alone (an LDS DMA among them would be another kind, and the compiler then waits for all of
+// them before the first use).
+__device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r) {
+  const int J = sh.I / kBlk;
+  const uint8_t* rec = L.rec + ((size_t)e * J + j) * kTaskBytes + (size_t)tid * 16;
 #pragma unroll
-  for (int t = 0; t < kGuCpl; ++t) {
-    const unsigned c = min(j16 + 16u * t, nch - 1);
-    r.q[t] = ld16_stream(rq + c * 16u);
-    r.qs[t] = ldb_stream(rs + c);
-  }
-  const size_t blk = ((size_t)e * J + j) * (size_t)H;
-  const uint8_t* dq = L.dq + blk * 16;
-  const uint8_t* ds = L.ds + blk;
-  const unsigned lane = tid & (kWave - 1), c0 = tid - lane;
-#pragma unroll
-  for (int t = 0; t < kDnRpl; ++t) {
-    const unsigned rw = c0 + (unsigned)(kThreads * t);
-    if (rw + lane < (unsigned)H) lds_dma16(dq + (size_t)(rw + lane) * 16u, dn_s + (size_t)rw * 16u);
-  }
-  // scales: H bytes as 4-byte words (H is a multiple of 32)
-  if (c0 * 4u < (unsigned)H && (c0 + lane) * 4u < (unsigned)H)
-    lds_dma4(ds + (size_t)(c0 + lane) * 4u, dn_s + (size_t)H * 16u + c0 * 4u);
+  for (int q = 0; q < kPieces; ++q) r.p[q] = ld16_stream(rec + (size_t)q * kThreads * 16);
 }
 
 // Computes task (slot u: tokens in un.mask[u], pairs un.pair0[u] + rank, gate weights un.w[u][m],
-// block j) from its loaded registers and the down block in LDS: the block's activations
-// silu(gate) * up into LDS, then partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every
-// row, stored tagged at this thread's row offsets in the owners' regions.
+// block j) from its loaded registers, and stores
+// partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every row, tagged, at the row's
+// offset in its owner's region. gu_s (LDS: 4 x M x 64 floats, then M x 4 x 32 bf16) takes the
+// k-slice sums of gate/up and the activation parts.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, const TaskRegs& r, const Union& un,
-                                             int u, int j, const uint16_t* xs, float* a_s, const uint8_t* dn_s,
-                                             unsigned tid, uint32_t tag) {
-  const int p = tid >> 5, j16 = tid & 15;
+                                             int u, int j, const uint16_t* xs, float* gu_s, unsigned tid,
+                                             uint32_t tag) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
+  const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
   const unsigned mask = un.mask[u];
-  const int p0 = un.pair0[u];
-  float acc[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+  // gate/up: B column i is token i, read from LDS by the lanes of this slot's tokens only (one
+  // exec mask per chunk); other columns are zero. Two accumulators (s even / odd) halve the chain
+  // of dependent MFMAs.
+  const bool xcol = i < M && (M == 1 || ((mask >> i) & 1u));
+  const uint16_t* xrow = xs + min(i, M - 1) * H;
+  f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
-    // no branch on the chunk index: a chunk past the row end gets scale 0 and adds zeros. (With
-    // a branch the compiler sank that chunk's loads into it, behind the down-projection loads,
-    // and computed it first, so the first dot product waited for the whole task's bytes.)
-    const int c = min(j16 + 16 * t, nch - 1);
-    const float sc = j16 + 16 * t < nch ? e8m0_to_f32(r.qs[t]) : 0.0f;
-    bf16x2_t pw[16];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      pw[4 * d + 0] = fp4x2_to_bf16x2<0>(r.q[t][d], sc);
-      pw[4 * d + 1] = fp4x2_to_bf16x2<1>(r.q[t][d], sc);
-      pw[4 * d + 2] = fp4x2_to_bf16x2<2>(r.q[t][d], sc);
-      pw[4 * d + 3] = fp4x2_to_bf16x2<3>(r.q[t][d], sc);
+    // no branch on the chunk index: a chunk past the row end gets scale 0 and adds zeros
+    // chunks past the row end are zero in the record (codes and scales): they add zeros
+    const int c = min(kGuCpk * ks + 4 * t + g, nch - 1);
+    const float sc = e8m0_to_f32(t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu);
+    u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = x0, x2 = x0, x3 = x0;
+    if (xcol) {
+      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow + c * 32);
+      x0 = xp[0];
+      x1 = xp[1];
+      x2 = xp[2];
+      x3 = xp[3];
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      // at M = 1 every task serves token 0: no branch (a branch used by one token only let the
-      // compiler sink the whole chunk's loads and conversions into it, behind later loads)
-      if (M == 1 || ((mask >> m) & 1u)) {
-        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs + m * H + c * 32);
-        float a = acc[m];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4_t xv = xp[q];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) a = dot2(pw[4 * q + k], as_bf16x2(xv[k]), a);
-        }
-        acc[m] = a;
-      }
-    }
+    d0 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][0], sc), x0, d0);
+    d1 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][1], sc), x1, d1);
+    d0 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][2], sc), x2, d0);
+    d1 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][3], sc), x3, d1);
   }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    // 16-lane row sums: gate in DPP rows 0 and 2 of the wave, up in rows 1 and 3; the gate sum
-    // moves to the up row (row_bcast:15), whose first lane writes silu(gate) * up
-    const float h = row16_sum(acc[m]);
-    const float hg = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h), 0x142, 0xA, 0xF, false));
-    if ((tid & 31) == 16) a_s[m * kBlk + p] = silu(hg) * h;
-  }
-  wait_mem();   // this thread's share of the down block has landed in LDS
+  // lane (g, i) holds rows 4g .. 4g+3 of the row group for token i
+  if (i < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + i) * 64 + rg * 16 + 4 * g) = d0 + d1;
   __syncthreads();
-  float wt[M];
-  int pm[M];
+
+  // a = silu(gate) * up in fp32, once per (token, activation), split exactly into three bf16 parts
+  // (hi + mid + lo, each truncated from the remainder), so the down products below stay exact fp32
+  // products of a. a_s holds them as the down MFMA's A rows: row 4m + s = part s of token m (s = 3
+  // and tokens outside the slot: zero), 32 activations each.
+  uint16_t* a_s = reinterpret_cast<uint16_t*>(gu_s + 4 * M * 64);
+  if (tid < 32 * M) {
+    const int am = tid >> 5, k = tid & 31;
+    const float* gp = gu_s + am * 64 + k;
+    float gate = gp[0], up = gp[32];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    wt[m] = un.w[u][m];
-    pm[m] = p0 + __popc(mask & ((1u << m) - 1u));
-  }
-#pragma unroll
-  for (int t = 0; t < kDnRpl; ++t) {
-    const int row = tid + kThreads * t;
-    // this row's word in its owner's region [owner][P][J][kLine]
-    const int rc = min(row, H - 1), owner = (int)(((float)rc + 0.5f) * sh.inv_r);
-    const unsigned rowoff = (unsigned)(owner * sh.P * J * kLine + (rc - owner * R));
-    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dn_s + (size_t)rc * 16);
-    const float sc = e8m0_to_f32(dn_s[(size_t)H * 16 + rc]);
-    float wf[kBlk];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f32x2_t v0 = fp4x2_to_f32x2<0>(dv[d], sc), v1 = fp4x2_to_f32x2<1>(dv[d], sc);
-      const f32x2_t v2 = fp4x2_to_f32x2<2>(dv[d], sc), v3 = fp4x2_to_f32x2<3>(dv[d], sc);
-      wf[8 * d + 0] = v0.x; wf[8 * d + 1] = v0.y; wf[8 * d + 2] = v1.x; wf[8 * d + 3] = v1.y;
-      wf[8 * d + 4] = v2.x; wf[8 * d + 5] = v2.y; wf[8 * d + 6] = v3.x; wf[8 * d + 7] = v3.y;
+    for (int q = 1; q < 4; ++q) {
+      gate += gp[q * M * 64];
+      up += gp[q * M * 64 + 32];
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      if (M == 1 || ((mask >> m) & 1u)) {
-        const float4* ap = reinterpret_cast<const float4*>(a_s + m * kBlk);
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kBlk / 4; ++q) {
-          const float4 a4 = ap[q];
-          s = fmaf(wf[4 * q + 0], a4.x, s);
-          s = fmaf(wf[4 * q + 1], a4.y, s);
-          s = fmaf(wf[4 * q + 2], a4.z, s);
-          s = fmaf(wf[4 * q + 3], a4.w, s);
-        }
-        if (row < H) st_coherent(w.partial + (size_t)(pm[m] * J + j) * kLine + rowoff, tagged(tag, __float_as_uint(wt[m] * s)));
-      }
-    }
+    const bool in = M == 1 || ((mask >> am) & 1u);
+    const float av = in ? silu(gate) * up : 0.0f;
+    const float hi = __uint_as_float(__float_as_uint(av) & 0xffff0000u);
+    const float r1 = av - hi;
+    const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    const float r2 = r1 - mid;
+    uint16_t* ap = a_s + am * 4 * 32 + k;
+    ap[0] = (uint16_t)(__float_as_uint(hi) >> 16);
+    ap[32] = (uint16_t)(__float_as_uint(mid) >> 16);
+    ap[64] = (uint16_t)(__float_as_uint(r2) >> 16);
+    ap[96] = 0;
   }
-  __syncthreads();  // a_s is rewritten by the next task
+  __syncthreads();
+
+  // down: A = the activation parts (lane (g, n): row n = 4m + s, k = 8g .. 8g+7), B = 16 down rows
+  // of the block (column n = tile row n); lane (g, n) of D then holds token g's three parts of
+  // tile row n.
+  const int n = lane & 15;
+  const u32x4_t ab = n < 4 * M ? *reinterpret_cast<const u32x4_t*>(a_s + n * 32 + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+  // D lane (g, n): token g (its partial is stored when the token is in the slot)
+  const bool tok = g < M && (M == 1 || ((mask >> g) & 1u));
+  const float wt = un.w[u][min(g, M - 1)];
+  const int pm = un.pair0[u] + __popc(mask & ((1u << g) - 1u));
+  unsigned long long* pdst = w.partial + (size_t)(pm * J + j) * kLine;
+  const unsigned ostride = (unsigned)(sh.P * J * kLine);   // an owner's region: [pairs][J][kLine]
+#pragma unroll
+  for (int q = 0; q < kDnTpw; ++q) {
+    const int rt = wave + kWaves * q;
+    if (rt >= (H >> 4)) break;
+    // this lane's down scale (row i of tile q) is byte b = 16q + i of the wave's 160 scales, which
+    // lane b / 3 holds in byte 13 + b % 3 of its first piece
+    const int sb = 16 * q + n, src = (sb * 171) >> 9, pos = sb - 3 * src;   // src = sb / 3 for sb < 160
+    const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)r.p[0][3]);
+    const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : r.p[0][q - 8];
+    const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, e8m0_to_f32((sw >> (8 + 8 * pos)) & 0xffu)),
+                                     f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+    const float v = (dd[0] + dd[1]) + dd[2];
+    const unsigned row = (unsigned)(rt * 16 + n);
+    const unsigned owner = (unsigned)(((float)row + 0.5f) * sh.inv_r);
+    if (tok) st_coherent(pdst + (owner * ostride + (row - owner * (unsigned)R)), tagged(tag, __float_as_uint(wt * v)));
+  }
+  __syncthreads();  // gu_s is rewritten by the next task
 }
 
 // ------------------------------------------------------------------------------ top-K + union
@@ -632,7 +619,6 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   __shared__ int s_idx[kMaxM][kMaxK];
   __shared__ float s_w[kMaxM][kMaxK];
   __shared__ uint32_t s_sel[kMaxM][kMaxK];
-  __shared__ __attribute__((aligned(16))) float a_s[kMaxM * kBlk];
   __shared__ float s_y[kMaxM][kMaxRows];
   __shared__ __attribute__((aligned(16))) unsigned long long s_desc[2][kDescWords];
   __shared__ unsigned long long s_launch;
@@ -645,13 +631,12 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int E = sh.E, H = sh.H, I = sh.I, R = sh.R;
   const int J = I / kBlk;
 
-  // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | a task's down block: codes [H][16]
-  // + scales [H] | scratch: selection candidates [M][E] u64, later this workgroup's partial sums
-  // [pairs][J][kLine] fp32
+  // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates [M][E]
+  // u64, then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
+  // then this workgroup's partial sums [pairs][J][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
-  uint8_t* dn_s = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
-  unsigned char* scratch = dn_s + (size_t)H * 17;
+  unsigned char* scratch = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(scratch);
   float* red = reinterpret_cast<float*>(scratch);
 
@@ -793,8 +778,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       TaskRegs sreg;
-      task_load(L, sh, E, b - (G - J), tid, sreg, dn_s);
-      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, a_s, dn_s, tid, tag_pt);
+      task_load(L, sh, E, b - (G - J), tid, sreg);
+      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, red, tid, tag_pt);
     }
     stamp(w, l, 3);
 
@@ -810,7 +795,18 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     __syncthreads();
     stamp(w, l, 5);
 
-    // the next layer's router rows -> LDS, behind this layer's task loads
+    // ------------------------------------------------------------------ 4: routed tasks
+    {
+      const int n_rt = (un.n - ns) * J;
+      for (int q = b; q < n_rt; q += G) {
+        TaskRegs cur;
+        const int u = ns + q / J;
+        task_load(L, sh, un.id[u], q % J, tid, cur);
+        task_compute<M>(sh, w, cur, un, u, q % J, xs, red, tid, tag_pt);
+      }
+    }
+    // the next layer's router rows -> LDS, after this layer's task loads: an LDS DMA pending among
+    // them would make every wait for a task load wait for all of them
     if (has_next && is_router) {
       const uint16_t* nwr = reinterpret_cast<const uint16_t*>(
           uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8]));
@@ -822,16 +818,6 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
                                            16, 0, 0);
     }
 
-    // ------------------------------------------------------------------ 4: routed tasks
-    {
-      const int n_rt = (un.n - ns) * J;
-      for (int q = b; q < n_rt; q += G) {
-        TaskRegs cur;
-        const int u = ns + q / J;
-        task_load(L, sh, un.id[u], q % J, tid, cur, dn_s);
-        task_compute<M>(sh, w, cur, un, u, q % J, xs, a_s, dn_s, tid, tag_pt);
-      }
-    }
     stamp(w, l, 6);
 
     // ------------------------------------------------------------------ 5: combine owned rows
@@ -915,19 +901,57 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   }
 }
 
-// ------------------------------------------------------------------------------ block-major down
-// down_q [n][H][I/2] -> [n][I/32][H][16] and down_s [n][H][I/32] -> [n][I/32][H]; one thread per
-// (expert, row, block) chunk, reading in canonical order.
-__global__ void pack_down_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, long long n_chunks,
-                                 int H, int J, uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks;
-       i += (long long)gridDim.x * blockDim.x) {
-    const long long per_e = (long long)H * J;
-    const long long e = i / per_e, rem = i - e * per_e;
-    const long long row = rem / J, j = rem - row * J;
-    const long long dst = (e * J + j) * H + row;
-    *reinterpret_cast<u32x4_t*>(qp + dst * 16) = ld16(q + i * 16);
-    sp[dst] = s[i];
+// ------------------------------------------------------------------------------ task-major pack
+// One thread per 16-byte piece (expert e, block j, piece p, wave w, lane l) of the task records;
+// it gathers the piece's bytes from the canonical bank (the layout is stated where
+// moe_pack_mxfp4 is declared). Bytes past H stay zero.
+__global__ void pack_tasks_kernel(const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gs,
+                                  const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds, long long n_pieces,
+                                  int H, int I, uint8_t* __restrict__ out) {
+  const int J = I / kBlk, nch = H / 32;
+  const long long gu_row = H / 2, gu_srow = nch, dn_row = I / 2, dn_srow = J;
+  for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n_pieces;
+       x += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(x % kWave), w = (int)((x / kWave) % kWaves), p = (int)((x / kThreads) % kPieces);
+    const long long task = x / ((long long)kPieces * kThreads);
+    const long long e = task / J;
+    const int j = (int)(task - e * J);
+    const int g = lane >> 4, i = lane & 15, rg = w >> 2, ks = w & 3;
+    // gate/up row of this lane and its chunk for step t
+    const long long grow = e * 2 * I + (rg >= 2 ? I : 0) + (long long)kBlk * j + 16 * (rg & 1) + i;
+    auto gu_chunk = [&](int t) { return kGuCpk * ks + 4 * t + g; };
+    // word g of down row 16 (w + 16 q) + i in block j (0 past H)
+    auto down_word = [&](int q) -> uint32_t {
+      const int row = 16 * (w + kWaves * q) + i;
+      if (row >= H) return 0u;
+      const uint8_t* src = dq + (e * H + row) * dn_row + 16 * j + 4 * g;
+      return (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) | ((uint32_t)src[3] << 24);
+    };
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (p == 0) {
+      v[0] = down_word(8);
+      v[1] = down_word(9);
+      uint8_t tail[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < kGuCpl; ++t) {
+        const int c = gu_chunk(t);
+        tail[t] = c < nch ? gs[grow * gu_srow + c] : 0;
+      }
+      for (int k = 0; k < 3; ++k) {
+        const int sb = 3 * lane + k;   // byte [q][i'] of the wave's 160 down scales
+        const int row = 16 * (w + kWaves * (sb >> 4)) + (sb & 15);
+        tail[5 + k] = (sb < 16 * kDnTpw && row < H) ? ds[(e * H + row) * dn_srow + j] : 0;
+      }
+      for (int b = 0; b < 8; ++b) v[2 + (b >> 2)] |= (uint32_t)tail[b] << (8 * (b & 3));
+    } else if (p <= kGuCpl) {
+      const int c = gu_chunk(p - 1);
+      if (c < nch) {
+        const uint8_t* src = gq + grow * gu_row + 16 * c;
+        for (int b = 0; b < 16; ++b) v[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
+      }
+    } else {
+      for (int d = 0; d < 4; ++d) v[d] = down_word(4 * (p - kGuCpl - 1) + d);
+    }
+    *reinterpret_cast<u32x4_t*>(out + x * 16) = u32x4_t{v[0], v[1], v[2], v[3]};
   }
 }
 
@@ -938,8 +962,9 @@ size_t g_trace_bytes[64];
 constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
-  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * kLine * 4;
-  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + (size_t)H * 17 + (sel > comb ? sel : comb);
+  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * kLine * 4, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
+  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
 }
 
 // n words rounded up to whole 128-byte lines
@@ -986,12 +1011,11 @@ int grid_for_device(int* G) {
 int check_layer(const qws_moe_layer& d, int E, int H, int I, int has_shared) {
   if (!d.x_bf16 || !d.w_router_bf16 || (!d.y_bf16 && !d.y_f32)) return QWS_ERR_ARG;
   const qws_mxfp4_experts& x = d.experts;
-  if (x.format != QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR) return QWS_ERR_FORMAT;
-  if (!x.gate_up_q || !x.gate_up_s || !x.down_q || !x.down_s) return QWS_ERR_ARG;
+  if (x.format != QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR) return QWS_ERR_FORMAT;
+  if (!x.gate_up_q) return QWS_ERR_ARG;
   if (x.n_routed != E || x.hidden != H || x.inter != I || x.has_shared != has_shared) return QWS_ERR_SHAPE;
   if (d.bias && !(d.bias_row_stride == 0 || d.bias_row_stride == E)) return QWS_ERR_SHAPE;
-  if (!qws_host::aligned16(d.x_bf16) || !qws_host::aligned16(d.w_router_bf16) || !qws_host::aligned16(x.gate_up_q) ||
-      !qws_host::aligned16(x.down_q))
+  if (!qws_host::aligned16(d.x_bf16) || !qws_host::aligned16(d.w_router_bf16) || !qws_host::aligned16(x.gate_up_q))
     return QWS_ERR_ALIGN;
   return QWS_OK;
 }
@@ -1123,28 +1147,37 @@ extern "C" int moe_workspace_errors(const void* workspace, int M, int K, int E, 
   return e == hipSuccess ? QWS_OK : qws_host::set_device_error(e);
 }
 
-extern "C" int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* down_q_out, unsigned char* down_s_out,
+extern "C" size_t moe_pack_mxfp4_bytes(int n_experts, int hidden, int inter) {
+  if (n_experts < 1 || n_experts > kMaxE + 1) return 0;
+  if (hidden < 32 || hidden > kHMax || hidden % 32 || inter < 32 || inter > kIMax || inter % 32) return 0;
+  return (size_t)n_experts * (inter / kBlk) * kTaskBytes;
+}
+
+extern "C" int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* out, size_t out_bytes,
                               qws_mxfp4_experts* desc_out, qws_stream_t stream) {
-  if (!src || !down_q_out || !down_s_out || !desc_out) return QWS_ERR_ARG;
+  if (!src || !out || !desc_out) return QWS_ERR_ARG;
   if (src->format != QWS_FMT_MXFP4_E2M1_E8M0_B32) return QWS_ERR_FORMAT;
   if (!src->gate_up_q || !src->gate_up_s || !src->down_q || !src->down_s) return QWS_ERR_ARG;
   if (src->has_shared != 0 && src->has_shared != 1) return QWS_ERR_ARG;
   if (src->n_routed < 1 || src->n_routed > kMaxE) return QWS_ERR_SHAPE;
-  if (src->hidden < 32 || src->hidden > kHMax || src->hidden % 32) return QWS_ERR_SHAPE;
-  if (src->inter < 32 || src->inter > kIMax || src->inter % 32) return QWS_ERR_SHAPE;
-  if (!qws_host::aligned16(src->down_q) || !qws_host::aligned16(down_q_out)) return QWS_ERR_ALIGN;
-  const int H = src->hidden, J = src->inter / kBlk;
-  const long long n = (long long)(src->n_routed + src->has_shared) * H * J;
-  const long long want = (n + 255) / 256;
+  const int n = src->n_routed + src->has_shared, H = src->hidden, I = src->inter;
+  const size_t need = moe_pack_mxfp4_bytes(n, H, I);
+  if (need == 0) return QWS_ERR_SHAPE;
+  if (out_bytes < need) return QWS_ERR_WORKSPACE;
+  if (!qws_host::aligned16(out)) return QWS_ERR_ALIGN;
+  const long long pieces = (long long)(need / 16);
+  const long long want = (pieces + 255) / 256;
   const int blocks = (int)(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL(pack_down_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), src->down_q,
-                     src->down_s, n, H, J, down_q_out, down_s_out);
+  hipLaunchKernelGGL(pack_tasks_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), src->gate_up_q,
+                     src->gate_up_s, src->down_q, src->down_s, pieces, H, I, out);
   const int st = qws_host::check_launch();
   if (st == QWS_OK) {
     *desc_out = *src;
-    desc_out->format = QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR;
-    desc_out->down_q = down_q_out;
-    desc_out->down_s = down_s_out;
+    desc_out->format = QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR;
+    desc_out->gate_up_q = out;
+    desc_out->gate_up_s = nullptr;
+    desc_out->down_q = nullptr;
+    desc_out->down_s = nullptr;
   }
   return st;
 }

@@ -71,6 +71,24 @@ __device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
 }
 
+// ------------------------------------------------------------------------------ matrix cores
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// D = A (16 x 32) * B (32 x 16) + C, bf16 inputs (products exact in fp32), fp32 accumulation, one
+// wave. Lane l holds A row l % 16 at k = 8 (l / 16) .. +7, B column l % 16 at the same k (8 bf16
+// each, lower k in the lower half-word), and D column l % 16 at rows 4 (l / 16) .. +3.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+// The 8 e2m1 codes of word `w` times `scale` as 8 bf16 (an MFMA operand; exact).
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  return u32x4_t{__builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<0>(w, scale)),
+                 __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<1>(w, scale)),
+                 __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<2>(w, scale)),
+                 __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<3>(w, scale))};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.

@@ -161,7 +161,8 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
 
 
 def _packed(**kw):
-    return _bank(**{"format": _lib.QWS_FMT_MXFP4_E2M1_E8M0_B32_DOWN_BLOCKMAJOR, **kw})
+    return _bank(**{"format": _lib.QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, "gate_up_s": None, "down_q": None,
+                    "down_s": None, **kw})
 
 
 def _layer_desc(**kw):
@@ -176,7 +177,7 @@ def _layer_desc(**kw):
     (dict(y_bf16=None, y_f32=None), 1, 8, None, _lib.QWS_ERR_ARG),
     (dict(experts=_bank(format=_lib.QWS_FMT_BF16)), 1, 8, None, _lib.QWS_ERR_FORMAT),
     (dict(experts=_bank()), 1, 8, None, _lib.QWS_ERR_FORMAT),               # canonical: not packed
-    (dict(experts=_packed(down_q=None)), 1, 8, None, _lib.QWS_ERR_ARG),
+    (dict(experts=_packed(gate_up_q=None)), 1, 8, None, _lib.QWS_ERR_ARG),
     ({}, 5, 8, None, _lib.QWS_ERR_SHAPE), ({}, 1, 9, None, _lib.QWS_ERR_SHAPE),
     (dict(experts=_packed(hidden=2592)), 1, 8, None, _lib.QWS_ERR_SHAPE),
     (dict(experts=_packed(n_routed=4)), 1, 8, None, _lib.QWS_ERR_SHAPE),       # E < K
@@ -212,19 +213,29 @@ def test_expert_gemv_refuses_packed_bank(lib):
     assert _experts(lib, _packed()) == _lib.QWS_ERR_FORMAT
 
 
-def _pack(lib, src=None, qo=A, so=A, out=True):
+def _pack(lib, src=None, dst=A, nbytes=None, out=True):
     o = _lib.MxFp4Experts()
-    return lib.moe_pack_mxfp4(C.byref(src if src is not None else _bank()), qo, so, C.byref(o) if out else None,
+    if nbytes is None:
+        nbytes = lib.moe_pack_mxfp4_bytes(513, 2560, 768)
+    return lib.moe_pack_mxfp4(C.byref(src if src is not None else _bank()), dst, nbytes, C.byref(o) if out else None,
                               None)
+
+
+def test_pack_bytes(lib):
+    # one 128 KB record per (expert, 32-activation block)
+    assert lib.moe_pack_mxfp4_bytes(513, 2560, 768) == 513 * 24 * _lib.QWS_TASK_BYTES == 513 * 24 * 131072
+    assert lib.moe_pack_mxfp4_bytes(65, 2560, 768) == 65 * 24 * 131072
+    for bad in ((0, 2560, 768), (1026, 2560, 768), (513, 2592, 768), (513, 2560, 48), (513, 48, 768)):
+        assert lib.moe_pack_mxfp4_bytes(*bad) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(src=_packed()), _lib.QWS_ERR_FORMAT), (dict(src=_bank(format=_lib.QWS_FMT_BF16)), _lib.QWS_ERR_FORMAT),
-    (dict(qo=None), _lib.QWS_ERR_ARG), (dict(so=None), _lib.QWS_ERR_ARG), (dict(out=False), _lib.QWS_ERR_ARG),
+    (dict(dst=None), _lib.QWS_ERR_ARG), (dict(out=False), _lib.QWS_ERR_ARG),
     (dict(src=_bank(down_s=None)), _lib.QWS_ERR_ARG), (dict(src=_bank(has_shared=3)), _lib.QWS_ERR_ARG),
     (dict(src=_bank(n_routed=0)), _lib.QWS_ERR_SHAPE), (dict(src=_bank(hidden=2592)), _lib.QWS_ERR_SHAPE),
-    (dict(src=_bank(inter=48)), _lib.QWS_ERR_SHAPE), (dict(src=_bank(down_q=MIS)), _lib.QWS_ERR_ALIGN),
-    (dict(qo=MIS), _lib.QWS_ERR_ALIGN),
+    (dict(src=_bank(inter=48)), _lib.QWS_ERR_SHAPE), (dict(dst=MIS), _lib.QWS_ERR_ALIGN),
+    (dict(nbytes=513 * 24 * 131072 - 16), _lib.QWS_ERR_WORKSPACE),
 ])
 def test_pack_validation(lib, kw, status):
     assert _pack(lib, **kw) == status

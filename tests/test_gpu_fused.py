@@ -1,5 +1,5 @@
 """GPU parity of the fused one-launch MoE layer (moe_layer_mxfp4) and of the multi-layer launch
-(moe_layers_mxfp4) against the oracle and against the two-call path; the block-major pack; chained
+(moe_layers_mxfp4) against the oracle and against the two-call path; the task-major pack; chained
 sequences (x of layer l+1 = y of layer l) against an oracle chain; graph replay; the full 42-layer
 decode step."""
 import numpy as np
@@ -38,20 +38,54 @@ def _check_layer(layer: Layer, L):
     return e
 
 
+def _task_major(bank: dict, n: int, H: int, I: int) -> np.ndarray:
+    """The task-major records, built by moving bytes of the canonical bank as the header states
+    (piece p of lane l = 16 g + i of wave w = 4 rg + ks in record (e, j))."""
+    J, nch = I // 32, H // 32
+    gq, gs, dq, ds = (bank[k].reshape(n, -1, bank[k].shape[-1]) for k in ("gate_up_q", "gate_up_s", "down_q", "down_s"))
+    w = np.arange(16)[:, None]
+    lane = np.arange(64)[None, :]
+    g, i, rg, ks = lane >> 4, lane & 15, w >> 2, w & 3
+    out = np.zeros((n, J, 8, 16, 64, 16), np.uint8)
+    b16 = np.arange(16)
+    for e in range(n):
+        for j in range(J):
+            grow = np.where(rg >= 2, I, 0) + 32 * j + 16 * (rg & 1) + i            # [16, 64]
+            for t in range(5):
+                c = 20 * ks + 4 * t + g
+                ok = c < nch
+                cc = np.minimum(c, nch - 1)
+                out[e, j, 1 + t] = np.where(ok[..., None], gq[e][grow[..., None], 16 * cc[..., None] + b16], 0)
+                out[e, j, 0, :, :, 8 + t] = np.where(ok, gs[e][grow, cc], 0)
+            for q in range(10):
+                row = 16 * (w + 16 * q) + i
+                ok = row < H
+                rr = np.minimum(row, H - 1)
+                word = np.where(ok[..., None], dq[e][rr[..., None], 16 * j + 4 * g[..., None] + np.arange(4)], 0)
+                if q < 8:
+                    out[e, j, 6 + q // 4, :, :, 4 * (q % 4):4 * (q % 4) + 4] = word
+                else:
+                    out[e, j, 0, :, :, 4 * (q - 8):4 * (q - 8) + 4] = word
+            for k in range(3):
+                sb = 3 * lane + k
+                row = 16 * (w + 16 * (sb >> 4)) + (sb & 15)
+                ok = (sb < 160) & (row < H)
+                out[e, j, 0, :, :, 13 + k] = np.where(ok, ds[e][np.minimum(row, H - 1), j], 0)
+    return out.reshape(n, J, 8 * 16 * 64 * 16)
+
+
 @pytest.mark.parametrize("si", range(len(TINY)))
-def test_pack_is_the_block_major_relayout(si):
-    """moe_pack_mxfp4 moves bytes only: block j of row r of expert e lands at [e][j][r]."""
+def test_pack_is_the_task_major_relayout(si):
+    """moe_pack_mxfp4 moves bytes only, to the places the header states (zeros past H)."""
     shape = TINY[si]
     say("pack", shape)
     layer = Layer(40 + si, 0, shape, 1)
     pk = _packed(layer)
     torch.cuda.synchronize()
-    n, H, J = shape.n_routed + int(shape.has_shared), shape.hidden, shape.inter // 32
-    dq = layer.bank_t["down_q"].cpu().numpy().reshape(n, H, J, 16).transpose(0, 2, 1, 3).reshape(n, J, H * 16)
-    ds = layer.bank_t["down_s"].cpu().numpy().reshape(n, H, J).transpose(0, 2, 1)
-    assert np.array_equal(pk.down_q.cpu().numpy(), dq)
-    assert np.array_equal(pk.down_s.cpu().numpy(), ds)
-    assert pk.gate_up_q.data_ptr() == layer.bank_t["gate_up_q"].data_ptr()
+    n, H, I = shape.n_routed + int(shape.has_shared), shape.hidden, shape.inter
+    bank = {k: layer.bank_t[k].cpu().numpy() for k in ("gate_up_q", "gate_up_s", "down_q", "down_s")}
+    assert np.array_equal(pk.gate_up_q.cpu().numpy(), _task_major(bank, n, H, I))
+    assert pk.layout == "task_major" and pk.gate_up_s is None
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
@@ -161,14 +195,13 @@ def test_multi_layer_graph_replay():
 
 
 def test_decode_step_42_layers_sampled():
-    """The full decode step's 42 layers (67.6 GB of seeded MXFP4 banks) in one launch; sampled
+    """The full decode step's 42 layers (67.6 GB of seeded MXFP4 banks, packed task-major) in one launch; sampled
     layers against the oracle, all layers' routing against the oracle's."""
     say("decode step 42 layers")
     shape = synth.LayerShape()
-    banks, Ls, xs, wrs = [], [], [], []
+    Ls, xs, wrs = [], [], []
     for l in range(synth.N_LAYERS):
-        bank_t = synth.expert_bank_torch(0, l, shape, device="cuda")
-        banks.append(bank_t)
+        bank_t = synth.expert_bank_torch(0, l, shape, device="cuda")   # freed once packed
         wr = synth.router_weights(0, l, 512)
         x = synth.token_vectors(0, l, 1)
         wrs.append(wr)
