@@ -150,8 +150,8 @@ int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
  *   out[(e * I/32 + j) * QWS_TASK_BYTES + ((p * 16 + w) * 64 + l) * 16 + b],  p < 8 pieces,
  * with w = 4 rg + ks, l = 16 g + i:
  *   p 0     bytes 0..7: 4-byte words q = 8, 9 (below); bytes 8..12: the scales of the five
- *           gate/up chunks of p 1..5; bytes 13..15: bytes 3 l .. 3 l + 2 of the wave's 160 down
- *           scales, [q][i] = scale of down row 16 (w + 16 q) + i in block j;
+ *           gate/up chunks of p 1..5; bytes 13 + k, k < 3: the scale of down row
+ *           16 (w + 16 q) + i in block j for q = 3 g + k (zero for q > 9);
  *   p 1..5  gate/up codes: row i of row group rg (gate 32j + 16 rg + i for rg < 2, else up
  *           I + 32j + 16 (rg - 2) + i), 16-byte chunk 20 ks + 4 (p - 1) + g of the row;
  *   p 6, 7  4-byte words q = 4 (p - 6) .. +3: word q is bytes 4g .. 4g+3 of down row

@@ -307,16 +307,19 @@ struct TaskRegs {
   u32x4_t p[kPieces];   // piece 0: down words q 8, 9 + scales; 1-5: gate/up chunks t; 6, 7: down words q 0..7
 };
 
-// Issues the eight loads of task (expert e, block j) into registers, piece by piece: for each
-// piece, the 64 lanes of a wave read 1 KB of consecutive bytes. All are plain vector loads: vector
+// This thread's first byte in the record of task (expert e, block j).
+__device__ __forceinline__ const uint8_t* task_rec(const Layer& L, const Shape& sh, int e, int j, unsigned tid) {
+  return L.rec + ((size_t)e * (sh.I / kBlk) + j) * kTaskBytes + (size_t)tid * 16;
+}
+// Issues the loads of pieces P0 .. P1-1 of a task record into registers: for each piece, the 64
+// lanes of a wave read 1 KB of consecutive bytes. All task loads are plain vector loads: vector
 // memory operations of one kind complete in order, so the compute can wait for each gate/up chunk
-// alone (an LDS DMA among them would be another kind, and the compiler then waits for all of
-// them before the first use).
-__device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e, int j, unsigned tid, TaskRegs& r) {
-  const int J = sh.I / kBlk;
-  const uint8_t* rec = L.rec + ((size_t)e * J + j) * kTaskBytes + (size_t)tid * 16;
+// alone (an LDS DMA among them would be another kind, and the compiler then waits for all of them
+// before the first use).
+template <int P0, int P1>
+__device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
 #pragma unroll
-  for (int q = 0; q < kPieces; ++q) r.p[q] = ld16_stream(rec + (size_t)q * kThreads * 16);
+  for (int q = P0; q < P1; ++q) r.p[q] = ld16_stream(rec + (size_t)q * kThreads * 16);
 }
 
 // Computes task (slot u: tokens in un.mask[u], pairs un.pair0[u] + rank, gate weights un.w[u][m],
@@ -325,9 +328,9 @@ __device__ __forceinline__ void task_load(const Layer& L, const Shape& sh, int e
 // offset in its owner's region. gu_s (LDS: 4 x M x 64 floats, then M x 4 x 32 bf16) takes the
 // k-slice sums of gate/up and the activation parts.
 template <int M>
-__device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, const TaskRegs& r, const Union& un,
-                                             int u, int j, const uint16_t* xs, float* gu_s, unsigned tid,
-                                             uint32_t tag) {
+__device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
+                                             int u, int j, const uint16_t* xs, float* gu_s, const uint32_t* rowoff,
+                                             unsigned tid, uint32_t tag, const uint8_t* nrec) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
   const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
@@ -343,7 +346,7 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
     // no branch on the chunk index: a chunk past the row end gets scale 0 and adds zeros
     // chunks past the row end are zero in the record (codes and scales): they add zeros
     const int c = min(kGuCpk * ks + 4 * t + g, nch - 1);
-    const float sc = e8m0_to_f32(t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu);
+    const float sc = e8m0_normal_to_f32(t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu);
     u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = x0, x2 = x0, x3 = x0;
     if (xcol) {
       const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow + c * 32);
@@ -359,6 +362,10 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
   }
   // lane (g, i) holds rows 4g .. 4g+3 of the row group for token i
   if (i < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + i) * 64 + rg * 16 + 4 * g) = d0 + d1;
+  // the next task's (nrec) gate/up pieces load into these registers during this task's down
+  // projection, its down pieces after it; the down-phase words of piece 0 are kept first
+  const uint32_t dn8 = r.p[0][0], dn9 = r.p[0][1], dsw = r.p[0][3];
+  if (nrec) task_load<0, kPieces - 2>(nrec, r);
   __syncthreads();
 
   // a = silu(gate) * up in fp32, once per (token, activation), split exactly into three bf16 parts
@@ -394,28 +401,48 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, con
   // tile row n.
   const int n = lane & 15;
   const u32x4_t ab = n < 4 * M ? *reinterpret_cast<const u32x4_t*>(a_s + n * 32 + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
-  // D lane (g, n): token g (its partial is stored when the token is in the slot)
-  const bool tok = g < M && (M == 1 || ((mask >> g) & 1u));
-  const float wt = un.w[u][min(g, M - 1)];
-  const int pm = un.pair0[u] + __popc(mask & ((1u << g) - 1u));
+  // D lane (g, n) holds token g's three parts of tile row n. With fewer than four tokens the D
+  // rows of absent tokens are empty, so the results of T = 4 / MP tiles are gathered into one
+  // register first (MP = M rounded up to a power of two): lane (g, n) then holds token g % MP of
+  // tile slot g / MP, and one store instruction per T tiles has every row of lanes busy.
+  constexpr int MP = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  constexpr int T = 4 / MP;
+  const int mt = g % MP;
+  const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
+  const float wt = un.w[u][min(mt, M - 1)];
+  const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
   unsigned long long* pdst = w.partial + (size_t)(pm * J + j) * kLine;
-  const unsigned ostride = (unsigned)(sh.P * J * kLine);   // an owner's region: [pairs][J][kLine]
+  const int ntile = H >> 4;
 #pragma unroll
-  for (int q = 0; q < kDnTpw; ++q) {
-    const int rt = wave + kWaves * q;
-    if (rt >= (H >> 4)) break;
-    // this lane's down scale (row i of tile q) is byte b = 16q + i of the wave's 160 scales, which
-    // lane b / 3 holds in byte 13 + b % 3 of its first piece
-    const int sb = 16 * q + n, src = (sb * 171) >> 9, pos = sb - 3 * src;   // src = sb / 3 for sb < 160
-    const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)r.p[0][3]);
-    const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : r.p[0][q - 8];
-    const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, e8m0_to_f32((sw >> (8 + 8 * pos)) & 0xffu)),
-                                     f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-    const float v = (dd[0] + dd[1]) + dd[2];
-    const unsigned row = (unsigned)(rt * 16 + n);
-    const unsigned owner = (unsigned)(((float)row + 0.5f) * sh.inv_r);
-    if (tok) st_coherent(pdst + (owner * ostride + (row - owner * (unsigned)R)), tagged(tag, __float_as_uint(wt * v)));
+  for (int q0 = 0; q0 < kDnTpw; q0 += T) {
+    float vt[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int q = q0 + t;
+      if (q < kDnTpw) {
+        // this lane's down scale (tile q, row n) is held by lane n + 16 (q / 3), in byte
+        // 13 + q % 3 of its first piece
+        const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
+        const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : (q == 8 ? dn8 : dn9);
+        const float dsc = e8m0_normal_to_f32((sw >> (8 + 8 * (q % 3))) & 0xffu);
+        const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, dsc), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+        vt[t] = (dd[0] + dd[1]) + dd[2];
+      } else {
+        vt[t] = 0.0f;
+      }
+    }
+    float v = vt[0];
+    if constexpr (T == 2) {
+      v = __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[1]), false, false)[0]);
+    } else if constexpr (T == 4) {
+      const uint32_t lo = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[2]), false, false)[0];
+      const uint32_t hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[1]), __float_as_uint(vt[3]), false, false)[0];
+      v = __uint_as_float(__builtin_amdgcn_permlane16_swap(lo, hi, false, false)[0]);
+    }
+    const int q = q0 + g / MP, rt = wave + kWaves * q;
+    if (tok && q < kDnTpw && rt < ntile) st_coherent(pdst + rowoff[rt * 16 + n], tagged(tag, __float_as_uint(wt * v)));
   }
+  if (nrec) task_load<kPieces - 2, kPieces>(nrec, r);
   __syncthreads();  // gu_s is rewritten by the next task
 }
 
@@ -532,35 +559,38 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
     stamp(w, l, 12);
     if (wave == 0) {
       // union in first-occurrence order over (token, rank); slot 0 is the shared expert (if any).
-      // Lane j holds selection (j / K, j % K).
-      const int n = M * K;
-      const int mj = lane < n ? lane / K : 0, rj = lane - mj * K;
-      const int e = lane < n ? s_idx[mj][rj] : -1;
-      const float wj = lane < n ? s_w[mj][rj] : 0.0f;
-      bool first = lane < n;
+      // Lane j < M * kMaxK holds selection (j / kMaxK, j % kMaxK) when that rank is < K; every lane
+      // compares its expert with all selections (broadcast LDS reads, no serial lane loop).
+      constexpr int N = M * kMaxK;
+      const int mj = lane / kMaxK, rj = lane % kMaxK;
+      const bool valid = lane < N && rj < K;
+      const int e = valid ? s_idx[mj][rj] : -1;
+      bool first = valid;
       unsigned mask = 0;
       float wsum[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
-      for (int i = 0; i < n; ++i) {
-        const int ei = __builtin_amdgcn_readlane(e, i);
-        const int mi = i / K;
-        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i));
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int mi = i / kMaxK, ri = i % kMaxK;
+        const int ei = ri < K ? s_idx[mi][ri] : -2;
         if (ei == e) {
           if (i < lane) first = false;
           mask |= 1u << mi;
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            if (m == mi) wsum[m] += wi;
+          wsum[mi] += s_w[mi][ri];
         }
       }
       const unsigned long long firsts = __ballot(first);
-      const int cnt = first ? __popc(mask) : 0;
-      int pair0 = ns * M;
-      for (int i = 0; i < n; ++i) {
-        const int ci = __builtin_amdgcn_readlane(cnt, i);
-        pair0 += i < lane ? ci : 0;
+      const int cnt = first ? __popc(mask) : 0;   // this slot's (slot, token) pairs: at most M < 8
+      // exclusive prefix sum of cnt over the lanes, and its total, from three bit planes
+      int before = 0, total = ns * M;
+#pragma unroll
+      for (int bit = 0; bit < 3; ++bit) {
+        const unsigned long long bb = __ballot((cnt >> bit) & 1);
+        before += __popcll(bb & lt) << bit;
+        total += __popcll(bb) << bit;
       }
+      const int pair0 = ns * M + before;
       const int slot = ns + __popcll(firsts & lt);
       if (first) {
         un.id[slot] = e;
@@ -586,8 +616,6 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
 #pragma unroll
           for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
         }
-        int total = ns * M;
-        for (int i = 0; i < n; ++i) total += __builtin_amdgcn_readlane(cnt, i);
         un.n = __popcll(firsts) + ns;
         un.n_pairs = total;
       }
@@ -620,6 +648,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   __shared__ float s_w[kMaxM][kMaxK];
   __shared__ uint32_t s_sel[kMaxM][kMaxK];
   __shared__ float s_y[kMaxM][kMaxRows];
+  __shared__ uint32_t s_rowoff[kHMax];   // row -> its word in the owner's partial region
   __shared__ __attribute__((aligned(16))) unsigned long long s_desc[2][kDescWords];
   __shared__ unsigned long long s_launch;
 
@@ -656,6 +685,13 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     for (int i = tid; i < sh.y_stride; i += kThreads) st_coherent(w.ytag + (size_t)b * sh.y_stride + i, 0ull);
     if (tid < kLine) st_coherent(w.done + (size_t)b * kLine + tid, 0ull);
     grid_sync(w, sync);
+  }
+
+  // row r's offset in its owner's region [pairs][J][kLine] of the partial sums (owner = r / R);
+  // first read after the first task's __syncthreads
+  for (int r = tid; r < H; r += kThreads) {
+    const int owner = r / R;
+    s_rowoff[r] = (uint32_t)(owner * sh.P * J * kLine + (r - owner * R));
   }
 
   // router rows of layer 0 -> LDS (asynchronous; this wave waits for them before its dots)
@@ -778,8 +814,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       TaskRegs sreg;
-      task_load(L, sh, E, b - (G - J), tid, sreg);
-      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, red, tid, tag_pt);
+      task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
+      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, red, s_rowoff, tid, tag_pt, nullptr);
     }
     stamp(w, l, 3);
 
@@ -797,12 +833,19 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 4: routed tasks
     {
+      // tasks q = b, b + G, ...: each one's loads are issued during the previous one's compute
       const int n_rt = (un.n - ns) * J;
-      for (int q = b; q < n_rt; q += G) {
+      int q = b;
+      if (q < n_rt) {
         TaskRegs cur;
-        const int u = ns + q / J;
-        task_load(L, sh, un.id[u], q % J, tid, cur);
-        task_compute<M>(sh, w, cur, un, u, q % J, xs, red, tid, tag_pt);
+        task_load<0, kPieces>(task_rec(L, sh, un.id[ns + q / J], q % J, tid), cur);
+        for (;;) {
+          const int qn = q + G;
+          const uint8_t* nrec = qn < n_rt ? task_rec(L, sh, un.id[ns + qn / J], qn % J, tid) : nullptr;
+          task_compute<M>(sh, w, cur, un, ns + q / J, q % J, xs, red, s_rowoff, tid, tag_pt, nrec);
+          if (!nrec) break;
+          q = qn;
+        }
       }
     }
     // the next layer's router rows -> LDS, after this layer's task loads: an LDS DMA pending among
@@ -937,9 +980,9 @@ __global__ void pack_tasks_kernel(const uint8_t* __restrict__ gq, const uint8_t*
         tail[t] = c < nch ? gs[grow * gu_srow + c] : 0;
       }
       for (int k = 0; k < 3; ++k) {
-        const int sb = 3 * lane + k;   // byte [q][i'] of the wave's 160 down scales
-        const int row = 16 * (w + kWaves * (sb >> 4)) + (sb & 15);
-        tail[5 + k] = (sb < 16 * kDnTpw && row < H) ? ds[(e * H + row) * dn_srow + j] : 0;
+        const int q = 3 * g + k;       // down scale of tile q, row i
+        const int row = 16 * (w + kWaves * q) + i;
+        tail[5 + k] = (q < kDnTpw && row < H) ? ds[(e * H + row) * dn_srow + j] : 0;
       }
       for (int b = 0; b < 8; ++b) v[2 + (b >> 2)] |= (uint32_t)tail[b] << (8 * (b & 3));
     } else if (p <= kGuCpl) {

@@ -39,6 +39,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+// E8M0 byte 1 .. 254 -> 2^(s-127) in one shift (the scales a bank may hold); byte 0 gives 0.0,
+// which the task-major records use as padding next to zero codes.
+__device__ __forceinline__ float e8m0_normal_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
 // Two e2m1 nibbles of byte `B` of `w`, times `scale`, as bf16x2 / float2 (element order: low
 // nibble first). gfx950 converts in one VALU op.
 template <int B>

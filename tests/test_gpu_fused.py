@@ -67,9 +67,9 @@ def _task_major(bank: dict, n: int, H: int, I: int) -> np.ndarray:
                 else:
                     out[e, j, 0, :, :, 4 * (q - 8):4 * (q - 8) + 4] = word
             for k in range(3):
-                sb = 3 * lane + k
-                row = 16 * (w + 16 * (sb >> 4)) + (sb & 15)
-                ok = (sb < 160) & (row < H)
+                q = 3 * g + k
+                row = 16 * (w + 16 * q) + i
+                ok = (q < 10) & (row < H)
                 out[e, j, 0, :, :, 13 + k] = np.where(ok, ds[e][np.minimum(row, H - 1), j], 0)
     return out.reshape(n, J, 8 * 16 * 64 * 16)
 
