@@ -61,15 +61,8 @@ constexpr int kMaxRows = 16;    // output rows owned by one workgroup
 constexpr int kMaxGrid = 512;
 constexpr int kPollBatch = 8;   // tagged words per thread in flight while reading partials
 constexpr int kLine = 16;       // 64-bit words per 128-byte line: hand-off words of one writer share no line
-constexpr int kBlkLanes = 8;   // lanes of a row-sum group that read one block's partial lines
-// Lanes that share one (token, row) output sum in the combine: fewer tokens, wider groups.
-template <int M>
-__host__ __device__ constexpr int sum_lanes() { return M == 1 ? 32 : (M == 2 ? 16 : 8); }
 static_assert(kMaxRows <= kLine, "an owner's rows of one (pair, block) share one line");
 static_assert(kMaxM <= kLine, "an expert's logits of all tokens share one line");
-static_assert(sum_lanes<1>() * kMaxRows <= 512 && 2 * sum_lanes<2>() * kMaxRows <= 512 &&
-                  3 * sum_lanes<3>() * kMaxRows <= 512 && 4 * sum_lanes<4>() * kMaxRows <= 512,
-              "combine groups exceed the workgroup");
 constexpr int kSyncCounters = 16;
 constexpr int kSyncStride = 16;             // 64-bit words: 128 bytes apart
 constexpr unsigned kSpinLimit = 1u << 20;   // polls before a wait gives up (~1 s)
@@ -129,8 +122,7 @@ struct Union {
   int pair0[kMaxSlots];          // first (slot, token) pair index of the slot
   float w[kMaxSlots][kMaxM];     // gate weight of (slot, token)
   int n_pairs;
-  int tok_n[kMaxM];              // pairs of each token, in slot order
-  int tok_pair[kMaxM][kMaxSlots];
+  int ptok[kMaxPairs];           // token of each (slot, token) pair (M > 1)
 };
 
 __device__ __forceinline__ void stamp(const Work& w, int l, int k) {
@@ -538,7 +530,6 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
         un.mask[slot] = 1u;
         un.pair0[slot] = slot;
         un.w[slot][0] = wr;
-        un.tok_pair[0][slot] = slot;
       }
       if (lane == 0) {
         if (ns) {
@@ -546,11 +537,9 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
           un.mask[0] = 1u;
           un.pair0[0] = 0;
           un.w[0][0] = 1.0f;
-          un.tok_pair[0][0] = 0;
         }
         un.n = ns + K;
         un.n_pairs = ns + K;
-        un.tok_n[0] = ns + K;
       }
     }
   }
@@ -601,12 +590,8 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const unsigned long long bm = __ballot(first && ((mask >> m) & 1u));
-        if (first && ((mask >> m) & 1u)) un.tok_pair[m][ns + __popcll(bm & lt)] = pair0 + __popc(mask & ((1u << m) - 1u));
-        if (lane == 0) {
-          un.tok_n[m] = ns + __popcll(bm);
-          if (ns) un.tok_pair[m][0] = m;
-        }
+        if (first && ((mask >> m) & 1u)) un.ptok[pair0 + __popc(mask & ((1u << m) - 1u))] = m;
+        if (ns && lane == 0) un.ptok[m] = m;
       }
       if (lane == 0) {
         if (ns) {
@@ -662,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
   // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates [M][E]
   // u64, then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
-  // then this workgroup's partial sums [pairs][J][kLine] fp32
+  // then the combine's per-wave row sums [waves][M][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
   unsigned char* scratch = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
@@ -865,50 +850,60 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 5: combine owned rows
     if (my_rows > 0) {
-      // slot (pair, block, row) at (p * J + j) * kLine + row: lane group tid / kLine takes one
-      // (pair, block) per batch step, lanes with row >= my_rows idle
-      const int n_slots = un.n_pairs * J * kLine;
+      // line (pair p, block j) = p * J + j of this owner's region holds its rows. Thread t polls
+      // row t % 16 of lines t / 16 + 64 k and sums them per token in registers (k ascending), then
+      // the four lanes of a wave with that row, then the 16 waves: a fixed order (deterministic)
+      constexpr int kStep = kThreads / kLine;
+      const int n_lines = un.n_pairs * J;
       const unsigned long long* src = w.partial + (size_t)b * sh.P * J * kLine;
-      const bool my_row = (tid % kLine) < my_rows;
-      for (int base = 0; base < n_slots; base += kPollBatch * kThreads) {
+      const int r = tid % kLine, L0 = tid / kLine;
+      const bool my_row = r < my_rows;
+      const float inv_j = 1.0f / (float)J;
+      float acc[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+      for (int k0 = 0; k0 * kStep < n_lines; k0 += kPollBatch) {
         int idx[kPollBatch];
         unsigned long long v[kPollBatch];
 #pragma unroll
         for (int q = 0; q < kPollBatch; ++q) {
-          const int i = base + tid + q * kThreads;
-          idx[q] = i < n_slots && my_row ? i : -1;
+          const int Lq = L0 + (k0 + q) * kStep;
+          idx[q] = Lq < n_lines && my_row ? Lq * kLine + r : -1;
         }
         poll_tagged<kPollBatch>(w, src, idx, tag_pt, v);
 #pragma unroll
-        for (int q = 0; q < kPollBatch; ++q)
-          if (idx[q] >= 0) red[idx[q]] = __uint_as_float((uint32_t)v[q]);
-      }
-      __syncthreads();
-      stamp(w, l, 7);
-      // y[m][row] = sum over token m's pairs and blocks. sum_lanes<M>() lanes share a (m, row): lane s
-      // takes blocks j = s % 8 (mod 8) of pairs i = s / 8 (mod lanes / 8), in a fixed order; then a
-      // fixed-order DPP reduction (deterministic)
-      {
-        constexpr int W = sum_lanes<M>(), WP = W / kBlkLanes;
-        const int grp = tid / W, s = tid % W;
-        const int m = grp / kMaxRows, rl = grp % kMaxRows;
-        const int sp = s / kBlkLanes, sj = s % kBlkLanes;
-        float acc = 0.0f;
-        if (m < M && rl < my_rows) {
-          const int npm = un.tok_n[m];
-          for (int i = sp; i < npm; i += WP) {
-            const float* rp = red + (size_t)un.tok_pair[m][i] * J * kLine + rl;
+        for (int q = 0; q < kPollBatch; ++q) {
+          if (idx[q] >= 0) {
+            const float x = __uint_as_float((uint32_t)v[q]);
+            if constexpr (M == 1) {
+              acc[0] += x;
+            } else {
+              const int Lq = L0 + (k0 + q) * kStep;
+              const int mt = un.ptok[(int)(((float)Lq + 0.5f) * inv_j)];   // pair Lq / J
 #pragma unroll
-            for (int jj = 0; jj < kIMax / kBlk / kBlkLanes; ++jj) {
-              const int j = sj + jj * kBlkLanes;
-              if (j < J) acc += rp[j * kLine];
+              for (int m = 0; m < M; ++m) acc[m] += m == mt ? x : 0.0f;
             }
           }
         }
-        acc = row8_sum(acc);
-        if constexpr (W >= 16) acc = row16_sum_of_row8(acc);
-        if constexpr (W >= 32) acc += __shfl_xor(acc, 16, kWave);
-        if (s == 0 && m < M && rl < my_rows) s_y[m][rl] = acc;
+      }
+      float* wsum = red;   // [wave][M][kLine]
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float x = acc[m];
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        if (lane < kLine) wsum[(wave * M + m) * kLine + lane] = x;
+      }
+      __syncthreads();
+      stamp(w, l, 7);
+      if (tid < M * kLine) {
+        const int m = tid / kLine, rr = tid % kLine;
+        float y = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) y += wsum[(wv * M + m) * kLine + rr];
+        if (rr < my_rows) s_y[m][rr] = y;
       }
       __syncthreads();
       stamp(w, l, 13);
@@ -1005,7 +1000,10 @@ size_t g_trace_bytes[64];
 constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
-  const size_t sel = (size_t)M * E * 8, comb = (size_t)P * J * kLine * 4, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  // scratch: selection keys, then a task's gate/up sums and activation parts, then the combine's
+  // per-wave row sums
+  const size_t sel = (size_t)M * E * 8, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  const size_t comb = (size_t)kWaves * M * kLine * 4;
   const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
   return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
 }
