@@ -99,6 +99,7 @@ struct Shape {
   float inv_r;     // 1 / R: owner of a row = floor((row + 0.5) / R) without an integer division
   int y_stride;    // tagged y words per row owner (M * R / 2, padded to whole lines)
   int x_fresh;  // no layer's x is written by this launch: x of layer l+1 is fetched during layer l's barrier
+  int jg;       // partial lines per routed pair (J / blocks per task group); set per layer
 };
 
 struct Work {
@@ -292,6 +293,11 @@ __device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
 constexpr int kGuCpk = 4 * kGuCpl;            // chunks of a row per k-slice: H <= 4 * 20 * 32
 constexpr int kDnTpw = kHMax / 16 / kWaves;   // down-projection row tiles (16 rows) per wave
 constexpr int kPieces = 8;                    // 16-byte pieces per lane of a task record
+// At M = 1 the shared expert's J tasks run before selection on the last J workgroups (the routed
+// tasks leave them idle). With more tokens the union needs most workgroups for several tasks, so
+// the shared expert joins the grouped task pool after selection instead.
+template <int M>
+constexpr bool kEarlyShared = M == 1;
 constexpr int kTaskBytes = kPieces * kThreads * 16;
 static_assert(kTaskBytes == QWS_TASK_BYTES, "task record size");
 static_assert(kGuCpl == 5 && kDnTpw == 10, "piece layout: 5 gate/up chunks + 10 down words + scales per lane");
@@ -321,8 +327,9 @@ __device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
 // k-slice sums of gate/up and the activation parts.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
-                                             int u, int j, const uint16_t* xs, float* gu_s, const uint32_t* rowoff,
-                                             unsigned tid, uint32_t tag, const uint8_t* nrec) {
+                                             int u, const uint16_t* xs, float* gu_s, const uint32_t* rowoff,
+                                             unsigned tid, uint32_t tag, const uint8_t* nrec, int line_shared,
+                                             int line_routed, bool first, bool last, float (&outv)[kDnTpw]) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
   const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
@@ -403,7 +410,10 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
   const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
   const float wt = un.w[u][min(mt, M - 1)];
   const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
-  unsigned long long* pdst = w.partial + (size_t)(pm * J + j) * kLine;
+  // partial line of (pair pm, this task's block or block group): at M = 1 the shared slot's pairs
+  // (run early) come first with one line per block, then the other pairs with one line per group
+  const int nsm = kEarlyShared<M> && sh.has_shared ? M : 0;
+  unsigned long long* pdst = w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * kLine;
   const int ntile = H >> 4;
 #pragma unroll
   for (int q0 = 0; q0 < kDnTpw; q0 += T) {
@@ -431,8 +441,12 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
       const uint32_t hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[1]), __float_as_uint(vt[3]), false, false)[0];
       v = __uint_as_float(__builtin_amdgcn_permlane16_swap(lo, hi, false, false)[0]);
     }
+    // a workgroup's tasks of one group (same slot, consecutive blocks) add up in registers and
+    // store once, after the last
+    outv[q0 / T] = first ? v : outv[q0 / T] + v;
     const int q = q0 + g / MP, rt = wave + kWaves * q;
-    if (tok && q < kDnTpw && rt < ntile) st_coherent(pdst + rowoff[rt * 16 + n], tagged(tag, __float_as_uint(wt * v)));
+    if (last && tok && q < kDnTpw && rt < ntile)
+      st_coherent(pdst + rowoff[rt * 16 + n], tagged(tag, __float_as_uint(wt * outv[q0 / T])));
   }
   if (nrec) task_load<kPieces - 2, kPieces>(nrec, r);
   __syncthreads();  // gu_s is rewritten by the next task
@@ -453,23 +467,54 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
   const int E = sh.E, K = sh.K;
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int ns = sh.has_shared ? 1 : 0;
-  (void)tid;
-  if (wave < M) {
-    const int m = wave;
-    uint32_t key[kQ];
-    {
+  uint32_t key[kQ];
+  if constexpr (M == 1) {
+    if (wave == 0) {
       int idx[kQ];
       unsigned long long v[kQ];
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
         const int e = lane + kWave * q;
-        idx[q] = e < E ? e * kLine + m : -1;
+        idx[q] = e < E ? e * kLine : -1;
       }
       poll_tagged<kQ>(w, w.logits, idx, tag, v);
       stamp(w, l, 4);
 #pragma unroll
       for (int q = 0; q < kQ; ++q) key[q] = idx[q] >= 0 ? sel_key(__uint_as_float((uint32_t)v[q])) : 0u;
     }
+  } else {
+    // every thread polls: word i = (expert i / M, token i % M) of the logits, so the M words of a
+    // line are read by adjacent lanes of one instruction and every line is requested once; keys
+    // go to LDS [m][e] for the token waves
+    uint32_t* keys = reinterpret_cast<uint32_t*>(cand + M * E);
+    {
+      constexpr int N = (M * kQ * kWave + kThreads - 1) / kThreads;
+      int idx[N];
+      unsigned long long v[N];
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        const int i = tid + kThreads * k, e = i / M, m = i - e * M;
+        idx[k] = e < E ? e * kLine + m : -1;
+      }
+      poll_tagged<N>(w, w.logits, idx, tag, v);
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        const int i = tid + kThreads * k, e = i / M, m = i - e * M;
+        if (e < E) keys[m * E + e] = sel_key(__uint_as_float((uint32_t)v[k]));
+      }
+    }
+    __syncthreads();
+    stamp(w, l, 4);
+    if (wave < M) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int e = lane + kWave * q;
+        key[q] = e < E ? keys[wave * E + e] : 0u;
+      }
+    }
+  }
+  if (wave < M) {
+    const int m = wave;
     // threshold: maxima of the 8-lane groups (a group holds experts 8g .. 8g+7 + 64 q)
     uint32_t lm = key[0];
 #pragma unroll
@@ -609,6 +654,14 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
 }
 
 // ------------------------------------------------------------------------------ the kernel
+// Blocks per task group: the smallest divisor of J for which the nsr routed slots' groups fit in
+// G workgroups (1 when every task has a workgroup of its own).
+__device__ __forceinline__ int group_size(int nsr, int J, int G) {
+  for (int k = 1; k < J; ++k)
+    if (J % k == 0 && nsr * (J / k) <= G) return k;
+  return J;
+}
+
 __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
@@ -646,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int J = I / kBlk;
 
   // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates [M][E]
-  // u64, then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
+  // u64 (+ keys [M][E] u32 when M > 1), then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
   // then the combine's per-wave row sums [waves][M][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
@@ -704,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     const int ns = sh.has_shared ? 1 : 0;
     const int row0 = b * R;
     const int my_rows = max(0, min(R, H - row0));
-    const bool shared_task = sh.has_shared && b >= G - J;
+    const bool shared_task = kEarlyShared<M> && sh.has_shared && b >= G - J;
     const int r_row = b + G * wave;                       // this wave's router row
     const bool is_router = wave < sh.nrw && r_row < E;
     // descriptor of layer l: layer 0 from the kernel arguments, later ones from the LDS copy made
@@ -799,8 +852,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       TaskRegs sreg;
+      float sout[kDnTpw];
       task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
-      task_compute<M>(sh, w, sreg, un, 0, b - (G - J), xs, red, s_rowoff, tid, tag_pt, nullptr);
+      task_compute<M>(sh, w, sreg, un, 0, xs, red, s_rowoff, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
     }
     stamp(w, l, 3);
 
@@ -818,18 +872,32 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 4: routed tasks
     {
-      // tasks q = b, b + G, ...: each one's loads are issued during the previous one's compute
-      const int n_rt = (un.n - ns) * J;
-      int q = b;
-      if (q < n_rt) {
+      // groups of kg consecutive blocks of one slot (kg = the smallest divisor of J that leaves at
+      // most G groups): workgroup b takes groups b, b + G, ...; a group's partials add up in
+      // registers and are stored once. Each task's loads are issued during the previous one's
+      // compute.
+      const int s0 = kEarlyShared<M> ? ns : 0;   // first slot of the pool
+      const int nsr = un.n - s0, kg = group_size(nsr, J, G), jg = J / kg, n_gr = nsr * jg;
+      sh.jg = jg;
+      int gi = b;
+      if (gi < n_gr) {
         TaskRegs cur;
-        task_load<0, kPieces>(task_rec(L, sh, un.id[ns + q / J], q % J, tid), cur);
+        float outv[kDnTpw];
+        int t = 0;
+        task_load<0, kPieces>(task_rec(L, sh, un.id[s0 + gi / jg], (gi % jg) * kg, tid), cur);
         for (;;) {
-          const int qn = q + G;
-          const uint8_t* nrec = qn < n_rt ? task_rec(L, sh, un.id[ns + qn / J], qn % J, tid) : nullptr;
-          task_compute<M>(sh, w, cur, un, ns + q / J, q % J, xs, red, s_rowoff, tid, tag_pt, nrec);
+          int gn = gi, tn = t + 1;
+          if (tn == kg) {
+            gn = gi + G;
+            tn = 0;
+          }
+          const uint8_t* nrec =
+              gn < n_gr ? task_rec(L, sh, un.id[s0 + gn / jg], (gn % jg) * kg + tn, tid) : nullptr;
+          task_compute<M>(sh, w, cur, un, s0 + gi / jg, xs, red, s_rowoff, tid, tag_pt, nrec, 0,
+                          s0 * M * J + gi % jg, t == 0, t == kg - 1, outv);
           if (!nrec) break;
-          q = qn;
+          gi = gn;
+          t = tn;
         }
       }
     }
@@ -853,8 +921,11 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       // line (pair p, block j) = p * J + j of this owner's region holds its rows. Thread t polls
       // row t % 16 of lines t / 16 + 64 k and sums them per token in registers (k ascending), then
       // the four lanes of a wave with that row, then the 16 waves: a fixed order (deterministic)
+      // lines: the shared slot's pairs x J blocks, then the routed pairs x jg block groups
       constexpr int kStep = kThreads / kLine;
-      const int n_lines = un.n_pairs * J;
+      const int nsm = kEarlyShared<M> ? ns * M : 0, n_sh = nsm * J;
+      const int n_lines = n_sh + (un.n_pairs - nsm) * sh.jg;
+      const float inv_jg = 1.0f / (float)sh.jg;
       const unsigned long long* src = w.partial + (size_t)b * sh.P * J * kLine;
       const int r = tid % kLine, L0 = tid / kLine;
       const bool my_row = r < my_rows;
@@ -879,7 +950,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
               acc[0] += x;
             } else {
               const int Lq = L0 + (k0 + q) * kStep;
-              const int mt = un.ptok[(int)(((float)Lq + 0.5f) * inv_j)];   // pair Lq / J
+              const int pq = Lq < n_sh ? (int)(((float)Lq + 0.5f) * inv_j)
+                                       : nsm + (int)(((float)(Lq - n_sh) + 0.5f) * inv_jg);
+              const int mt = un.ptok[pq];
 #pragma unroll
               for (int m = 0; m < M; ++m) acc[m] += m == mt ? x : 0.0f;
             }
@@ -1002,7 +1075,7 @@ constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
   // scratch: selection keys, then a task's gate/up sums and activation parts, then the combine's
   // per-wave row sums
-  const size_t sel = (size_t)M * E * 8, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  const size_t sel = (size_t)M * E * (M > 1 ? 12 : 8), gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
   const size_t comb = (size_t)kWaves * M * kLine * 4;
   const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
   return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
@@ -1143,7 +1216,7 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
     }
   }
   const Shape sh{E, K, H, I, hs, R, P, chained ? 1 : 0, nrw, 1.0f / (float)R, line_words(M * R / 2),
-                 x_fresh ? 1 : 0};
+                 x_fresh ? 1 : 0, J};
   const Layer first = to_layer(host[0]);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (M) {
