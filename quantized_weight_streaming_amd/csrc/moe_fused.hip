@@ -766,11 +766,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     if (l > 0) L = desc_from_lds(s_desc[l & 1]);
     // tags never 0: a zero-filled workspace holds tag 0
     const uint32_t tag_lg = tag_base + 4u * (uint32_t)l + 1u, tag_pt = tag_lg + 1u, tag_y = tag_lg + 2u;
-    // the next layer's descriptor -> registers now, LDS after the router (its load has landed by then)
-    unsigned long long next_desc = 0;
     const bool has_next = l + 1 < n_layers;
-    if (has_next && wave == kWaves - 1 && lane < kDescWords)
-      next_desc = ldg(reinterpret_cast<const unsigned long long*>(rest + (l + 1)) + lane);
     stamp(w, l, 0);
 
     // ------------------------------------------------------------------ 1: x
@@ -802,6 +798,11 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     }
     __syncthreads();
     stamp(w, l, 1);
+    // the next layer's descriptor -> registers now (after the x wait: a load issued before it would
+    // hold up this layer's x), LDS after the router
+    unsigned long long next_desc = 0;
+    if (has_next && wave == kWaves - 1 && lane < kDescWords)
+      next_desc = ldg(reinterpret_cast<const unsigned long long*>(rest + (l + 1)) + lane);
 
     // ------------------------------------------------------------------ 2: router, shared task
     if (is_router) {
