@@ -126,9 +126,29 @@ struct Union {
   int ptok[kMaxPairs];           // token of each (slot, token) pair (M > 1)
 };
 
+// Trace stamps go to LDS and reach memory in one store per layer, issued where the workgroup waits
+// for its stores anyway: a store per stamp would put its acknowledgement into the next wait for a
+// load and stretch the phase it marks. Stamps 8, 9 and 14 are taken after that store and leave with
+// the next layer's (the last layer's at the end of the kernel).
+__shared__ unsigned long long s_stamp[kTracePoints];
+constexpr unsigned kLateStamps = (1u << 8) | (1u << 9) | (1u << 14);
+
 __device__ __forceinline__ void stamp(const Work& w, int l, int k) {
-  if (w.trace && threadIdx.x == 0)
-    w.trace[((size_t)l * gridDim.x + blockIdx.x) * kTracePoints + k] = wall_clock64();
+  (void)l;
+  if (w.trace && threadIdx.x == 0) s_stamp[k] = wall_clock64();
+}
+// Lanes 0 .. kTracePoints-1 of wave 0 (the wave that takes the stamps): layer l's early stamps and
+// layer l-1's late ones (only the late ones when `late_only`); a slot is cleared once written.
+__device__ __forceinline__ void flush_stamps(const Work& w, int l, bool late_only) {
+  const int k = threadIdx.x;
+  if (w.trace && k < kTracePoints) {
+    const bool late = (kLateStamps >> k) & 1u;
+    const int layer = late ? (late_only ? l : l - 1) : l;
+    if ((late || !late_only) && layer >= 0) {
+      w.trace[((size_t)layer * gridDim.x + blockIdx.x) * kTracePoints + k] = s_stamp[k];
+      s_stamp[k] = 0ull;
+    }
+  }
 }
 
 __device__ __forceinline__ unsigned long long tagged(uint32_t tag, uint32_t v) {
@@ -710,6 +730,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int r_row0 = b + G * wave;                      // this wave's router row
   SyncState sync{0ull, false};
 
+  if (tid < kTracePoints) s_stamp[tid] = 0ull;
   // launch number -> this launch's tag base (every workgroup adds 1 per launch)
   if (tid == 0)
     s_launch = __hip_atomic_fetch_add(w.launches, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / (unsigned)G;
@@ -999,6 +1020,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           st_coherent(w.ytag + (size_t)b * sh.y_stride + m * (R / 2) + rp, tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
       }
     }
+    flush_stamps(w, l, false);
     stamp(w, l, 8);
     if (!sh.chained && l + 1 < n_layers) {
       // layer l's output is written before layer l+1 starts
@@ -1011,6 +1033,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer
     }
   }
+  flush_stamps(w, n_layers - 1, true);
 }
 
 // ------------------------------------------------------------------------------ task-major pack
