@@ -147,14 +147,17 @@ class MoeLayer:
         return len({int(e) for e in self.idx.cpu().reshape(-1).tolist()})
 
 
-def probe_ceiling(qws, dev):
+def probe_ceiling(qws, dev, probe="probe_read"):
+    """Best read rate over a few grid sizes for 4 GiB: `probe_read` (ordinary grid-strided loads)
+    or `probe_read_nt` (non-temporal loads, one contiguous share per workgroup)."""
     import torch
     buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    fn = getattr(qws, probe)
     best = {}
     for blocks in (1024, 2048, 4096, 8192):
-        r = time_cold(lambda: qws.probe_read(buf, sink, blocks), dev, iters=10, warm=2)
+        r = time_cold(lambda: fn(buf, sink, blocks), dev, iters=10, warm=2)
         best[blocks] = buf.numel() / (r["median_us"] * 1e-6) / 1e9
     del buf
     b = max(best, key=best.get)
@@ -341,6 +344,8 @@ def main():
     if not args.no_breakdown:
         breakdown["probe_read_ceiling"] = probe_ceiling(qws, dev)
         log("probe", breakdown["probe_read_ceiling"])
+        breakdown["probe_read_nt_ceiling"] = probe_ceiling(qws, dev, "probe_read_nt")
+        log("probe nt", breakdown["probe_read_nt_ceiling"])
         wsf = {1: qws.moe_layer_workspace(1, K_TOP, 512, 2560, 768, dev),
                4: qws.moe_layer_workspace(4, K_TOP, 512, 2560, 768, dev)}
         wsr1 = qws.route_workspace(1, 512, dev)

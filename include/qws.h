@@ -291,6 +291,13 @@ int qws_debug_trace_buffer(void* buf, size_t bytes);
  * device's practical read bandwidth.                                                        */
 int qws_probe_read(const void* buf, size_t bytes, unsigned* sink, int blocks, qws_stream_t stream);
 
+/* Non-temporal streaming-read probe: same arguments and errors as qws_probe_read. Workgroup b
+ * reads its own contiguous share (bytes / blocks, rounded up to 16-byte words; the last share
+ * ends at the buffer's end) with non-temporal 128-bit loads and writes the XOR of the share's
+ * 32-bit words into sink[b] (0 for an empty share). The faster streaming shape; its lines are not
+ * kept in the caches, so unlike qws_probe_read it is no cache flush.                          */
+int qws_probe_read_nt(const void* buf, size_t bytes, unsigned* sink, int blocks, qws_stream_t stream);
+
 /* Copy probe: copies `bytes` (multiple of 16; both buffers 16-byte aligned, not overlapping) from
  * `src` to `dst` with 128-bit loads and stores, grid-strided over `blocks` workgroups (<= 65536).
  * A kernel of known traffic (reads and writes `bytes` each) against which HBM traffic counters

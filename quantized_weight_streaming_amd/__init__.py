@@ -28,7 +28,7 @@ __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "debug_dequant_mxfp4", "debug_dequant_fp8",
-           "probe_read", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
+           "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
 
 def lib():
@@ -346,6 +346,11 @@ def debug_trace_buffer(buf) -> None:
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
     check("qws_probe_read", lib().qws_probe_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), blocks,
                                                  _stream(buf.device)))
+
+
+def probe_read_nt(buf: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    check("qws_probe_read_nt", lib().qws_probe_read_nt(_p(buf), buf.numel() * buf.element_size(), _p(sink), blocks,
+                                                       _stream(buf.device)))
 
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int) -> None:

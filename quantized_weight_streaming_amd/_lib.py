@@ -67,6 +67,7 @@ SIGNATURES = {
     "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),
     "qws_debug_dequant_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _P]),
     "qws_probe_read": (_I, [_P, _SZ, _P, _I, _P]),
+    "qws_probe_read_nt": (_I, [_P, _SZ, _P, _I, _P]),
     "qws_probe_copy": (_I, [_P, _P, _SZ, _I, _P]),
     "qws_debug_trace_buffer": (_I, [_P, _SZ]),
 }

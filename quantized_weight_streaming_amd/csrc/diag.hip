@@ -163,6 +163,35 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4_t* __restri
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Non-temporal read probe: workgroup b reads share b (contiguous, 1/gridDim of the buffer), each
+// wave 4 consecutive KB per step with non-temporal loads. Measured on MI355X this is the access
+// shape that streams fastest (~7.0 TB/s over 4 GiB, against ~5.9 TB/s for the grid-strided
+// ordinary loads above).
+__global__ __launch_bounds__(256) void probe_read_nt_kernel(const u32x4_t* __restrict__ buf, size_t n16,
+                                                            unsigned* __restrict__ sink) {
+  __shared__ unsigned part[4];
+  constexpr int kU = 4;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n16 ? b0 + per : n16;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t acc = 0;
+  for (size_t base = b0 + (size_t)wave * kU * kWave; base < b1; base += (size_t)4 * kU * kWave) {
+    u32x4_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t i = base + (size_t)u * kWave + lane;
+      v[u] = i < b1 ? __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)(buf + i)) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 // --------------------------------------------------------------------------- copy probe
 // A plain copy of known size: the reference point that turns the HBM traffic counters of other
 // kernels into bytes (read and write both equal `bytes` here).
@@ -285,6 +314,15 @@ extern "C" int qws_probe_read(const void* buf, size_t bytes, unsigned* sink, int
   if (bytes == 0 || bytes % 16 || blocks < 1 || blocks > 65536) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(buf)) return QWS_ERR_ALIGN;
   hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4_t*>(buf), bytes / 16, sink);
+  return qws_host::check_launch();
+}
+
+extern "C" int qws_probe_read_nt(const void* buf, size_t bytes, unsigned* sink, int blocks, qws_stream_t stream) {
+  if (!buf || !sink) return QWS_ERR_ARG;
+  if (bytes == 0 || bytes % 16 || blocks < 1 || blocks > 65536) return QWS_ERR_SHAPE;
+  if (!qws_host::aligned16(buf)) return QWS_ERR_ALIGN;
+  hipLaunchKernelGGL(probe_read_nt_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4_t*>(buf), bytes / 16, sink);
   return qws_host::check_launch();
 }

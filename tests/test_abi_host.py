@@ -152,6 +152,10 @@ def test_diagnostics_validation(lib):
     assert lib.qws_probe_read(A, 100, A, 4, None) == _lib.QWS_ERR_SHAPE
     assert lib.qws_probe_read(A, 1024, A, 0, None) == _lib.QWS_ERR_SHAPE
     assert lib.qws_probe_read(None, 1024, A, 4, None) == _lib.QWS_ERR_ARG
+    assert lib.qws_probe_read_nt(A, 100, A, 4, None) == _lib.QWS_ERR_SHAPE
+    assert lib.qws_probe_read_nt(A, 1024, A, 70000, None) == _lib.QWS_ERR_SHAPE
+    assert lib.qws_probe_read_nt(None, 1024, A, 4, None) == _lib.QWS_ERR_ARG
+    assert lib.qws_probe_read_nt(MIS, 1024, A, 4, None) == _lib.QWS_ERR_ALIGN
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):

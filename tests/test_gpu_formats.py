@@ -103,3 +103,20 @@ def test_probe_read_checksum():
     qws.probe_read(buf, sink, 64)
     torch.cuda.synchronize()
     assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(a)
+
+
+@pytest.mark.parametrize("n_words,blocks", [(1 << 20, 64), (4 * 1000 + 12, 7), (8, 5)])
+def test_probe_read_nt_checksum_per_share(n_words, blocks):
+    """Workgroup b's word is the XOR of its contiguous share of 16-byte words (empty shares: 0)."""
+    say(f"probe read nt words={n_words} blocks={blocks}")
+    rng = np.random.default_rng(4)
+    a = rng.integers(0, 2**32, n_words, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(a.view(np.int32)).cuda()
+    sink = torch.full((blocks,), -1, dtype=torch.int32, device="cuda")
+    qws.probe_read_nt(buf, sink, blocks)
+    torch.cuda.synchronize()
+    n16 = n_words // 4
+    per = -(-n16 // blocks)
+    want = [np.bitwise_xor.reduce(a[4 * min(b * per, n16):4 * min((b + 1) * per, n16)]) if b * per < n16 else 0
+            for b in range(blocks)]
+    assert [int(v) for v in sink.cpu().numpy().view(np.uint32)] == [int(w) for w in want]
