@@ -274,10 +274,9 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
 // Selection key: order-preserving float -> uint32 (larger float, larger key; -0 == +0; NaN ranks
 // as -inf). Every logit maps to >= 0x007fffff; 0 marks an absent entry.
 __device__ __forceinline__ uint32_t sel_key(float f) {
-  if (f != f) f = -__builtin_inff();
-  if (f == 0.0f) f = 0.0f;
+  f = f != f ? -__builtin_inff() : f + 0.0f;   // -0 + 0 = +0 (round to nearest)
   const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: ~u, else u | sign bit
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -474,38 +473,132 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
 
 // ------------------------------------------------------------------------------ top-K + union
 // Every workgroup selects the top-K of each token from the tagged logits (the same result in every
-// workgroup), with one wave per token and no workgroup barrier: fewer polling waves make the
-// logits exchange faster, and the serial part stays short. Lane l holds experts l + 64 q. A
-// candidate must reach T = the smallest of the maxima of the 8 lane groups (lanes 8g .. 8g+7)
-// when at least K groups hold experts (then >= K logits reach T, so all of the top K do);
-// otherwise T admits every expert. A candidate's rank is the number of candidates that beat it
-// (larger logit, or equal logit and lower index); ranks < K are the selection, in order.
+// workgroup). A lane holds experts lane + 64 q. A candidate must reach T = the smallest of the
+// maxima of the 8 lane groups (lanes 8g .. 8g+7) when at least K groups hold experts (then >= K
+// logits reach T, so all of the top K do); otherwise T admits every expert. A candidate's rank is
+// the number of candidates that beat it (larger logit, or equal logit and lower index); ranks < K
+// are the selection, in order.
+
+// One token: wave 0 polls the logits (fewer polling waves make the exchange faster), finds T and
+// writes the candidates to LDS in (q, lane) order with straight-line code; then every wave ranks
+// its share of the candidates (one ballot per 64 of them) and enters the selected ones into the
+// union (the shared expert, then the selection in rank order). The gate weights come last, from
+// wave 0 after the final barrier: a task reads them only after its own first barrier, so the other
+// waves issue their task loads meanwhile.
+template <int kQ>
+__device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, uint32_t tag, int wave, int lane,
+                                               unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
+                                               float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK], int l) {
+  const int E = sh.E, K = sh.K;
+  const int ns = sh.has_shared ? 1 : 0;
+  // LDS: candidates [0, nc), then one slot per lane for the lanes without one, then the count
+  unsigned long long* const n_slot = cand + E + kWave;
+  if (wave == 0) {
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int idx[kQ];
+    unsigned long long v[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int e = lane + kWave * q;
+      idx[q] = e < E ? e * kLine : -1;
+    }
+    poll_tagged<kQ>(w, w.logits, idx, tag, v);
+    stamp(w, l, 4);
+    // absent experts (past E) get key 0 by a mask rather than a branch per q
+    uint32_t key[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      key[q] = sel_key(__uint_as_float((uint32_t)v[q])) & (0u - (uint32_t)(lane + kWave * q < E));
+    // T: group maxima (quad swaps, half-row mirror), then their minimum by lane moves (groups 8
+    // lanes apart within a row, then across rows and half-waves). A group without experts has
+    // maximum 0, which admits every expert; T >= 1 keeps absent ones out.
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int q = 1; q < kQ; ++q) lm = max(lm, key[q]);
+    lm = max(lm, dpp<0xB1>(lm));
+    lm = max(lm, dpp<0x4E>(lm));
+    lm = max(lm, dpp<0x141>(lm));
+    uint32_t t = min(lm, dpp<0x128>(lm));
+    const auto h16 = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+    t = min((uint32_t)h16[0], (uint32_t)h16[1]);
+    const auto h32 = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+    t = min((uint32_t)h32[0], (uint32_t)h32[1]);
+    const uint32_t T = max((uint32_t)__builtin_amdgcn_readfirstlane(t), 1u);
+    stamp(w, l, 10);
+    // every lane writes: a lane without a candidate to a slot of its own past the table
+    int nc = 0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const bool f = key[q] >= T;
+      const unsigned long long bl = __ballot(f);
+      cand[f ? nc + __popcll(bl & lt) : E + lane] = rank_key(key[q], lane + kWave * q);
+      nc += __popcll(bl);
+    }
+    if (lane == 0) {
+      *n_slot = (unsigned long long)nc;
+      if (ns) {
+        un.id[0] = E;
+        un.mask[0] = 1u;
+        un.pair0[0] = 0;
+        un.w[0][0] = 1.0f;
+      }
+      un.n = ns + K;
+      un.n_pairs = ns + K;
+    }
+    stamp(w, l, 11);
+  }
+  __syncthreads();
+  {
+    // candidate c = wave + 16 k: its rank counts the candidates above it, 64 per ballot (stopping
+    // once it is known to be outside the top K)
+    const int nc = (int)*n_slot;
+    const unsigned long long o0 = lane < nc ? cand[lane] : 0ull;
+    for (int c = wave; c < nc; c += kWaves) {
+      const unsigned long long cc = cand[c];
+      int rank = __popcll(__ballot(o0 > cc));
+      for (int j0 = kWave; j0 < nc && rank < K; j0 += kWave) {
+        const unsigned long long o = j0 + lane < nc ? cand[j0 + lane] : 0ull;
+        rank += __popcll(__ballot(o > cc));
+      }
+      if (rank < K && lane == 0) {
+        const int e = (int)(0xffffffffu - (uint32_t)cc), slot = ns + rank;
+        s_sel[0][rank] = (uint32_t)(cc >> 32);
+        s_idx[0][rank] = e;
+        un.id[slot] = e;
+        un.mask[slot] = 1u;
+        un.pair0[slot] = slot;
+      }
+    }
+  }
+  __syncthreads();
+  stamp(w, l, 12);
+  if (wave == 0) {
+    // softmax over the K selected logits, summed in rank order (the same sum in every lane)
+    const float z = lane < K ? expf(key_to_float(s_sel[0][lane]) - key_to_float(s_sel[0][0])) : 0.0f;
+    float sum = 0.0f;
+    for (int r = 0; r < K; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), r));
+    const float wr = z / sum;
+    if (lane < K) {
+      s_w[0][lane] = wr;
+      un.w[ns + lane][0] = wr;
+    }
+  }
+}
+
+// Several tokens: every thread polls (word i = (expert i / M, token i % M) of the logits, so the
+// M words of a line are read by adjacent lanes of one instruction and every line is requested
+// once) and the keys go to LDS [m][e]; then wave m selects token m's top K, and wave 0 forms the
+// union.
 template <int M, int kQ>
 __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint32_t tag, int tid, int wave, int lane,
                                             unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
                                             float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK], int l) {
+  static_assert(M > 1, "one token: select_top_one");
   const int E = sh.E, K = sh.K;
   const unsigned long long lt = (1ull << lane) - 1ull;
   const int ns = sh.has_shared ? 1 : 0;
   uint32_t key[kQ];
-  if constexpr (M == 1) {
-    if (wave == 0) {
-      int idx[kQ];
-      unsigned long long v[kQ];
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const int e = lane + kWave * q;
-        idx[q] = e < E ? e * kLine : -1;
-      }
-      poll_tagged<kQ>(w, w.logits, idx, tag, v);
-      stamp(w, l, 4);
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) key[q] = idx[q] >= 0 ? sel_key(__uint_as_float((uint32_t)v[q])) : 0u;
-    }
-  } else {
-    // every thread polls: word i = (expert i / M, token i % M) of the logits, so the M words of a
-    // line are read by adjacent lanes of one instruction and every line is requested once; keys
-    // go to LDS [m][e] for the token waves
+  {
     uint32_t* keys = reinterpret_cast<uint32_t*>(cand + M * E);
     {
       constexpr int N = (M * kQ * kWave + kThreads - 1) / kThreads;
@@ -580,35 +673,14 @@ __device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint
         s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)mine);
       }
     }
-    stamp(w, l, 12);
     // softmax over the K selected logits, summed in rank order (the same sum in every lane)
     const float z = lane < K ? expf(key_to_float(s_sel[m][lane]) - key_to_float(s_sel[m][0])) : 0.0f;
     float sum = 0.0f;
     for (int r = 0; r < K; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), r));
     const float wr = z / sum;
     if (lane < K) s_w[m][lane] = wr;
-    if constexpr (M == 1) {
-      // one token: the union is the shared expert, then the selection in rank order
-      if (lane < K) {
-        const int slot = ns + lane;
-        un.id[slot] = s_idx[0][lane];
-        un.mask[slot] = 1u;
-        un.pair0[slot] = slot;
-        un.w[slot][0] = wr;
-      }
-      if (lane == 0) {
-        if (ns) {
-          un.id[0] = E;
-          un.mask[0] = 1u;
-          un.pair0[0] = 0;
-          un.w[0][0] = 1.0f;
-        }
-        un.n = ns + K;
-        un.n_pairs = ns + K;
-      }
-    }
   }
-  if constexpr (M > 1) {
+  {
     __syncthreads();
     stamp(w, l, 12);
     if (wave == 0) {
@@ -719,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int J = I / kBlk;
 
   // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates [M][E]
-  // u64 (+ keys [M][E] u32 when M > 1), then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
+  // u64 (+ 65 u64 when M = 1; + keys [M][E] u32 when M > 1), then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
   // then the combine's per-wave row sums [waves][M][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
@@ -882,14 +954,25 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 3: top-K and union
     // a lane holds experts lane + 64 q for q < kQ: 8 registers suffice up to 512 experts
-    if (E <= 8 * kWave) select_topk<M, 8>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-    else select_topk<M, kMaxE / kWave>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-    if (b == 0 && tid < M * sh.K) {
-      const int m = tid / sh.K, r = tid - m * sh.K;
-      if (L.topk_idx) stg(L.topk_idx + tid, s_idx[m][r]);
-      if (L.topk_w) stg(L.topk_w + tid, s_w[m][r]);
+    if constexpr (M == 1) {
+      if (E <= 8 * kWave) select_top_one<8>(sh, w, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      else select_top_one<kMaxE / kWave>(sh, w, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      // no barrier: the gate weights (wave 0, just formed) are read only past a task's first
+      // barrier; wave 0 wrote s_idx and s_w itself
+      if (b == 0 && tid < sh.K) {
+        if (L.topk_idx) stg(L.topk_idx + tid, s_idx[0][tid]);
+        if (L.topk_w) stg(L.topk_w + tid, s_w[0][tid]);
+      }
+    } else {
+      if (E <= 8 * kWave) select_topk<M, 8>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      else select_topk<M, kMaxE / kWave>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      if (b == 0 && tid < M * sh.K) {
+        const int m = tid / sh.K, r = tid - m * sh.K;
+        if (L.topk_idx) stg(L.topk_idx + tid, s_idx[m][r]);
+        if (L.topk_w) stg(L.topk_w + tid, s_w[m][r]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     stamp(w, l, 5);
 
     // ------------------------------------------------------------------ 4: routed tasks
@@ -1099,7 +1182,8 @@ constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
   // scratch: selection keys, then a task's gate/up sums and activation parts, then the combine's
   // per-wave row sums
-  const size_t sel = (size_t)M * E * (M > 1 ? 12 : 8), gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  // (one token: 64 more candidate slots, written by the lanes without a candidate, and the count)
+  const size_t sel = M > 1 ? (size_t)M * E * 12 : (size_t)(E + kWave + 1) * 8, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
   const size_t comb = (size_t)kWaves * M * kLine * 4;
   const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
   return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
