@@ -900,28 +900,36 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     // ------------------------------------------------------------------ 2: router, shared task
     if (is_router) {
       wait_mem();   // this wave's router-row copy into LDS has landed
-      const uint16_t* wrow = wr_s + (size_t)wave * H;
-      float acc[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-#pragma unroll
-      for (int t = 0; t < kRtCpl; ++t) {
-        const int c = lane + t * kWave;
-        if (c < (H >> 3)) {
-          const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(wrow + c * 8);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + m * H + c * 8);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(rv[d]), as_bf16x2(xv[d]), acc[m]);
-          }
-        }
-      }
-      // bias loaded before any store: a wait for a load between the stores would also wait for the
-      // previous store's acknowledgement, slow while other workgroups poll these lines
+      // bias loads first (their latency overlaps the dot products), and before any store: a wait
+      // for a load between the stores would also wait for the previous store's acknowledgement,
+      // slow while other workgroups poll these lines
       float bias[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) bias[m] = L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f;
+      // every operand read is issued before the first product: chunks past the row end read the
+      // last chunk and use a zero router operand (their products add exact zeros, so the sum and
+      // its order equal those of the two-call router kernel)
+      const uint16_t* wrow = wr_s + (size_t)wave * H;
+      const int nrc = H >> 3;
+      u32x4_t rv[kRtCpl], xv[M][kRtCpl];
+#pragma unroll
+      for (int t = 0; t < kRtCpl; ++t) {
+        const int c = lane + t * kWave, cc = min(c, nrc - 1);
+        const uint32_t keep = 0u - (uint32_t)(c < nrc);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wrow + cc * 8);
+        rv[t] = u32x4_t{v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep};
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m][t] = *reinterpret_cast<const u32x4_t*>(xs + m * H + cc * 8);
+      }
+      float acc[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        acc[m] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kRtCpl; ++t)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(rv[t][d]), as_bf16x2(xv[m][t][d]), acc[m]);
+      }
       float lg[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) lg[m] = wave_sum(acc[m]) + bias[m];
