@@ -112,7 +112,7 @@ struct Work {
   unsigned long long* logits;    // [E][kLine] tagged logits: expert e, token m at e*kLine + m (one line per router row)
   unsigned long long* ytag;      // [G][y_stride] tagged bf16 pairs of y (chained sequences): owner b, token m, pair q at b*y_stride + m*R/2 + q
   unsigned long long* done;      // [G][kLine] tagged "layer finished" words (layers that are not chained)
-  unsigned long long* partial;   // [G][P][J][kLine] tagged, gate-weighted partial sums: owner, pair, block, row - owner*R
+  unsigned long long* partial;   // [P * J][H] tagged, gate-weighted partial sums: line (pair, block or block group), row
 };
 
 // Routing of the current layer, shared by the workgroup (LDS).
@@ -346,7 +346,7 @@ __device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
 // k-slice sums of gate/up and the activation parts.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
-                                             int u, const uint16_t* xs, float* gu_s, const uint32_t* rowoff,
+                                             int u, const uint16_t* xs, float* gu_s,
                                              unsigned tid, uint32_t tag, const uint8_t* nrec, int line_shared,
                                              int line_routed, bool first, bool last, float (&outv)[kDnTpw]) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
@@ -432,7 +432,9 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
   // partial line of (pair pm, this task's block or block group): at M = 1 the shared slot's pairs
   // (run early) come first with one line per block, then the other pairs with one line per group
   const int nsm = kEarlyShared<M> && sh.has_shared ? M : 0;
-  unsigned long long* pdst = w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * kLine;
+  // (a line is one row-contiguous vector of H tagged words: a store of 16 rows fills a 128-byte
+  // line of memory, and a row owner reads its R consecutive words of every line)
+  unsigned long long* pdst = w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
   const int ntile = H >> 4;
 #pragma unroll
   for (int q0 = 0; q0 < kDnTpw; q0 += T) {
@@ -465,7 +467,7 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
     outv[q0 / T] = first ? v : outv[q0 / T] + v;
     const int q = q0 + g / MP, rt = wave + kWaves * q;
     if (last && tok && q < kDnTpw && rt < ntile)
-      st_coherent(pdst + rowoff[rt * 16 + n], tagged(tag, __float_as_uint(wt * outv[q0 / T])));
+      st_coherent(pdst + rt * 16 + n, tagged(tag, __float_as_uint(wt * outv[q0 / T])));
   }
   if (nrec) task_load<kPieces - 2, kPieces>(nrec, r);
   __syncthreads();  // gu_s is rewritten by the next task
@@ -778,7 +780,6 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   __shared__ float s_w[kMaxM][kMaxK];
   __shared__ uint32_t s_sel[kMaxM][kMaxK];
   __shared__ float s_y[kMaxM][kMaxRows];
-  __shared__ uint32_t s_rowoff[kHMax];   // row -> its word in the owner's partial region
   __shared__ __attribute__((aligned(16))) unsigned long long s_desc[2][kDescWords];
   __shared__ unsigned long long s_launch;
 
@@ -810,19 +811,12 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const uint32_t tag_base = (uint32_t)(s_launch * kTagsPerLaunch);
   if (s_launch > 0 && tag_base == 0) {
     // tags repeat from here on: clear every tagged word (tag 0 is never valid) before any use
-    const size_t own = (size_t)sh.P * J * kLine;
-    for (size_t i = tid; i < own; i += kThreads) st_coherent(w.partial + (size_t)b * own + i, 0ull);
+    const size_t n_part = (size_t)sh.P * J * H;
+    for (size_t i = (size_t)b * kThreads + tid; i < n_part; i += (size_t)G * kThreads) st_coherent(w.partial + i, 0ull);
     for (int i = b * kThreads + tid; i < E * kLine; i += G * kThreads) st_coherent(w.logits + i, 0ull);
     for (int i = tid; i < sh.y_stride; i += kThreads) st_coherent(w.ytag + (size_t)b * sh.y_stride + i, 0ull);
     if (tid < kLine) st_coherent(w.done + (size_t)b * kLine + tid, 0ull);
     grid_sync(w, sync);
-  }
-
-  // row r's offset in its owner's region [pairs][J][kLine] of the partial sums (owner = r / R);
-  // first read after the first task's __syncthreads
-  for (int r = tid; r < H; r += kThreads) {
-    const int owner = r / R;
-    s_rowoff[r] = (uint32_t)(owner * sh.P * J * kLine + (r - owner * R));
   }
 
   // router rows of layer 0 -> LDS (asynchronous; this wave waits for them before its dots)
@@ -956,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       TaskRegs sreg;
       float sout[kDnTpw];
       task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
-      task_compute<M>(sh, w, sreg, un, 0, xs, red, s_rowoff, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
+      task_compute<M>(sh, w, sreg, un, 0, xs, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
     }
     stamp(w, l, 3);
 
@@ -1006,7 +1000,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           }
           const uint8_t* nrec =
               gn < n_gr ? task_rec(L, sh, un.id[s0 + gn / jg], (gn % jg) * kg + tn, tid) : nullptr;
-          task_compute<M>(sh, w, cur, un, s0 + gi / jg, xs, red, s_rowoff, tid, tag_pt, nrec, 0,
+          task_compute<M>(sh, w, cur, un, s0 + gi / jg, xs, red, tid, tag_pt, nrec, 0,
                           s0 * M * J + gi % jg, t == 0, t == kg - 1, outv);
           if (!nrec) break;
           gi = gn;
@@ -1031,15 +1025,15 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 5: combine owned rows
     if (my_rows > 0) {
-      // line (pair p, block j) = p * J + j of this owner's region holds its rows. Thread t polls
-      // row t % 16 of lines t / 16 + 64 k and sums them per token in registers (k ascending), then
-      // the four lanes of a wave with that row, then the 16 waves: a fixed order (deterministic)
+      // this owner's rows are words row0 .. row0 + my_rows - 1 of every line. Thread t polls row
+      // t % 16 of lines t / 16 + 64 k and sums them per token in registers (k ascending), then the
+      // four lanes of a wave with that row, then the 16 waves: a fixed order (deterministic)
       // lines: the shared slot's pairs x J blocks, then the routed pairs x jg block groups
       constexpr int kStep = kThreads / kLine;
       const int nsm = kEarlyShared<M> ? ns * M : 0, n_sh = nsm * J;
       const int n_lines = n_sh + (un.n_pairs - nsm) * sh.jg;
       const float inv_jg = 1.0f / (float)sh.jg;
-      const unsigned long long* src = w.partial + (size_t)b * sh.P * J * kLine;
+      const unsigned long long* src = w.partial + row0;
       const int r = tid % kLine, L0 = tid / kLine;
       const bool my_row = r < my_rows;
       const float inv_j = 1.0f / (float)J;
@@ -1052,7 +1046,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 #pragma unroll
         for (int q = 0; q < kPollBatch; ++q) {
           const int Lq = L0 + (k0 + q) * kStep;
-          idx[q] = Lq < n_lines && my_row ? Lq * kLine + r : -1;
+          idx[q] = Lq < n_lines && my_row ? Lq * H + r : -1;
         }
         poll_tagged<kPollBatch>(w, src, idx, tag_pt, v);
 #pragma unroll
@@ -1203,13 +1197,13 @@ constexpr int line_words(int n) { return (n + kLine - 1) / kLine * kLine; }
 size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
   const size_t sync = qws_host::align256(kSyncCounters * kSyncStride * 8);
   const size_t misc = 256;   // launch counter, error count
-  // sized for the largest grid and per-workgroup strides (kWaves router rows, kMaxRows owned rows)
+  // sized for the largest grid and per-workgroup strides (kWaves router rows, kMaxRows owned
+  // rows); the partial sums for every (pair, block) line of H rows
   (void)E;
-  (void)H;
   const size_t lg = qws_host::align256((size_t)kMaxE * kLine * 8);
   const size_t yt = qws_host::align256((size_t)kMaxGrid * line_words(M * kMaxRows / 2) * 8);
   const size_t dn = qws_host::align256((size_t)kMaxGrid * kLine * 8);
-  const size_t part = qws_host::align256((size_t)kMaxGrid * M * (K + 1) * (I / kBlk) * kLine * 8);
+  const size_t part = qws_host::align256((size_t)M * (K + 1) * (I / kBlk) * H * 8);
   if (w) {
     w->trace = nullptr;
     w->sync = reinterpret_cast<unsigned long long*>(base);
