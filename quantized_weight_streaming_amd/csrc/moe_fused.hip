@@ -243,11 +243,21 @@ __device__ void grid_sync(const Work& w, SyncState& st) {
   __syncthreads();
 }
 
+// One wave copies a router row (H bf16) into LDS with 16-byte DMA loads.
+__device__ __forceinline__ void router_row_to_lds(const uint16_t* row, uint16_t* dst, int H, int lane) {
+  for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
+    if (c0 + lane < (H >> 3))
+      __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
+                                       (__attribute__((address_space(3))) void*)(dst + c0 * 8), 16, 0, 0);
+}
+
 // Between layers that are not chained: every workgroup publishes a tagged word once all of its
 // stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
-// round trip to a counter before the wait starts.
+// round trip to a counter before the wait starts. Meanwhile the router waves copy the next
+// layer's router rows (next_row: this wave's row, or NULL) into LDS and the last wave polls: it
+// issues none of these copies, which a wait for its loads would also wait for.
 __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, const uint16_t* next_x, uint16_t* xs,
-                               int n_x) {
+                               int n_x, const uint16_t* next_row, uint16_t* row_dst, int H) {
   wait_mem();
   __syncthreads();
   stamp(w, l, 14);
@@ -260,12 +270,14 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
         __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(next_x + (size_t)(c + lane) * 8),
                                          (__attribute__((address_space(3))) void*)(xs + (size_t)c * 8), 16, 0, 0);
   }
-  if (tid < kWave) {
+  if (next_row) router_row_to_lds(next_row, row_dst, H, tid % kWave);
+  if (tid >= kThreads - kWave) {
     constexpr int kPer = kMaxGrid / kWave;
+    const int lane = tid - (kThreads - kWave);
     int idx[kPer];
     unsigned long long v[kPer];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) idx[q] = tid + q * kWave < (int)gridDim.x ? (tid + q * kWave) * kLine : -1;
+    for (int q = 0; q < kPer; ++q) idx[q] = lane + q * kWave < (int)gridDim.x ? (lane + q * kWave) * kLine : -1;
     poll_tagged<kPer>(w, w.done, idx, tag, v);
   }
   __syncthreads();
@@ -820,14 +832,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   }
 
   // router rows of layer 0 -> LDS (asynchronous; this wave waits for them before its dots)
-  if (wave < sh.nrw && r_row0 < E) {
-    const uint16_t* row = first.wr + (size_t)r_row0 * H;
-    for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
-      if (c0 + lane < (H >> 3))
-        __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
-                                         (__attribute__((address_space(3))) void*)(wr_s + (size_t)wave * H + c0 * 8),
-                                         16, 0, 0);
-  }
+  if (wave < sh.nrw && r_row0 < E) router_row_to_lds(first.wr + (size_t)r_row0 * H, wr_s + (size_t)wave * H, H, lane);
 
   for (int l = 0; l < n_layers; ++l) {
     // opaque copies of the thread index and the shape per layer: values derived from them are
@@ -1008,18 +1013,15 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
         }
       }
     }
-    // the next layer's router rows -> LDS, after this layer's task loads: an LDS DMA pending among
-    // them would make every wait for a task load wait for all of them
-    if (has_next && is_router) {
-      const uint16_t* nwr = reinterpret_cast<const uint16_t*>(
-          uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8]));
-      const uint16_t* row = nwr + (size_t)r_row * H;
-      for (int c0 = 0; c0 < (H >> 3); c0 += kWave)
-        if (c0 + lane < (H >> 3))
-          __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(row + (c0 + lane) * 8),
-                                           (__attribute__((address_space(3))) void*)(wr_s + (size_t)wave * H + c0 * 8),
-                                           16, 0, 0);
-    }
+    // the next layer's router rows -> LDS: chained layers (no barrier) here, after this layer's task
+    // loads (an LDS DMA pending among them would make every wait for a task load wait for it);
+    // otherwise during the barrier, where the router waves are idle
+    const uint16_t* next_row = nullptr;
+    if (has_next && is_router)
+      next_row = reinterpret_cast<const uint16_t*>(
+                     uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8])) +
+                 (size_t)r_row * H;
+    if (next_row && sh.chained) router_row_to_lds(next_row, wr_s + (size_t)wave * H, H, lane);
 
     stamp(w, l, 6);
 
@@ -1112,7 +1114,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       const uint16_t* next_x = nullptr;
       if (sh.x_fresh)
         next_x = reinterpret_cast<const uint16_t*>(uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, x_bf16) / 8]));
-      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H);
+      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H, next_row, wr_s + (size_t)wave * H, H);
       stamp(w, l, 9);
     } else {
       __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer
