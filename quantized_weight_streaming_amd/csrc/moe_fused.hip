@@ -124,6 +124,7 @@ struct Union {
   float w[kMaxSlots][kMaxM];     // gate weight of (slot, token)
   int n_pairs;
   int ptok[kMaxPairs];           // token of each (slot, token) pair (M > 1)
+  int sel_slot[kMaxM * kMaxK];   // slot of selection (token, rank) at token * kMaxK + rank (M > 1)
 };
 
 // Trace stamps go to LDS and reach memory in one store per layer, issued where the workgroup waits
@@ -351,20 +352,19 @@ __device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
   for (int q = P0; q < P1; ++q) r.p[q] = ld16_stream(rec + (size_t)q * kThreads * 16);
 }
 
-// Computes task (slot u: tokens in un.mask[u], pairs un.pair0[u] + rank, gate weights un.w[u][m],
+// Computes task (slot u: tokens in `mask` (un.mask[u]), pairs un.pair0[u] + rank, gate weights un.w[u][m],
 // block j) from its loaded registers, and stores
 // partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every row, tagged, at the row's
 // offset in its owner's region. gu_s (LDS: 4 x M x 64 floats, then M x 4 x 32 bf16) takes the
 // k-slice sums of gate/up and the activation parts.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
-                                             int u, const uint16_t* xs, float* gu_s,
+                                             int u, unsigned mask, const uint16_t* xs, float* gu_s,
                                              unsigned tid, uint32_t tag, const uint8_t* nrec, int line_shared,
                                              int line_routed, bool first, bool last, float (&outv)[kDnTpw]) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
   const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
-  const unsigned mask = un.mask[u];
   // gate/up: B column i is token i, read from LDS by the lanes of this slot's tokens only (one
   // exec mask per chunk); other columns are zero. Two accumulators (s even / odd) halve the chain
   // of dependent MFMAs.
@@ -599,164 +599,198 @@ __device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, u
   }
 }
 
+// Several tokens: the union, per lane and the same in every wave. Lane j < M * kMaxK holds
+// selection (token j / kMaxK, rank j % kMaxK): its expert, whether it is that expert's first
+// selection in (token, rank) order (the one that owns the slot), the slot, and where first the
+// slot's token mask and first pair. Slot 0 is the shared expert (if any), then the routed
+// experts in first-occurrence order.
+struct UnionLane {
+  int e;            // expert of the selection (-1: no selection)
+  bool first;
+  int slot;
+  unsigned mask;    // where first
+  int pair0;        // where first
+  int n, n_pairs;   // slots and (slot, token) pairs, wave-uniform
+};
+
+template <int M>
+__device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int K, int ns, int lane) {
+  constexpr int N = M * kMaxK;
+  static_assert(N <= kWave, "one wave holds every selection");
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int rj = lane % kMaxK;
+  const bool valid = lane < N && rj < K;
+  UnionLane u;
+  u.e = valid ? s_idx[lane / kMaxK][rj] : -1;
+  // every selection against every other, from registers (descending: fl ends at the first lane
+  // with this expert)
+  unsigned mask = 0u;
+  int fl = lane;
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) {
+    const int ei = __builtin_amdgcn_readlane(u.e, i);
+    const bool same = valid && ei == u.e;
+    mask |= same ? 1u << (i / kMaxK) : 0u;
+    fl = same ? i : fl;
+  }
+  u.first = valid && fl == lane;
+  const unsigned long long firsts = __ballot(u.first);
+  u.slot = __builtin_amdgcn_ds_bpermute(fl << 2, ns + (int)__popcll(firsts & lt));
+  u.mask = mask;
+  // exclusive prefix sum of the first lanes' token counts (at most M <= 4: three bit planes)
+  const int cnt = u.first ? __popc(mask) : 0;
+  int before = 0, total = ns * M;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const unsigned long long bb = __ballot((cnt >> bit) & 1);
+    before += __popcll(bb & lt) << bit;
+    total += __popcll(bb) << bit;
+  }
+  u.pair0 = ns * M + before;
+  u.n = ns + __popcll(firsts);
+  u.n_pairs = total;
+  return u;
+}
 // Several tokens: every thread polls (word i = (expert i / M, token i % M) of the logits, so the
 // M words of a line are read by adjacent lanes of one instruction and every line is requested
-// once) and the keys go to LDS [m][e]; then wave m selects token m's top K, and wave 0 forms the
-// union.
+// once) and the keys go to LDS; wave m < M then finds token m's T and writes its candidates as in
+// the one-token case (token m's region: E candidates, 64 slots for the lanes without one, the
+// count); every wave ranks its share of all tokens' candidates; then wave 0 forms the union while
+// wave 1 + m forms token m's weights, and a barrier publishes both (the weights go into the union
+// after it: a task reads them only past its own first barrier).
 template <int M, int kQ>
-__device__ __forceinline__ void select_topk(const Shape& sh, const Work& w, uint32_t tag, int tid, int wave, int lane,
-                                            unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
-                                            float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK], int l) {
-  static_assert(M > 1, "one token: select_top_one");
+__device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, const Layer& L, uint32_t tag, int tid,
+                                             int wave, int lane, unsigned long long* cand, Union& un,
+                                             int (*s_idx)[kMaxK], float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK],
+                                             int l) {
+  static_assert(M > 1 && M + 1 <= kWaves, "one token: select_top_one");
   const int E = sh.E, K = sh.K;
-  const unsigned long long lt = (1ull << lane) - 1ull;
   const int ns = sh.has_shared ? 1 : 0;
-  uint32_t key[kQ];
+  const int stride = E + kWave + 1;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(cand + (size_t)M * stride);   // [M][E]
   {
-    uint32_t* keys = reinterpret_cast<uint32_t*>(cand + M * E);
-    {
-      constexpr int N = (M * kQ * kWave + kThreads - 1) / kThreads;
-      int idx[N];
-      unsigned long long v[N];
+    constexpr int N = (M * kQ * kWave + kThreads - 1) / kThreads;
+    int idx[N];
+    unsigned long long v[N];
 #pragma unroll
-      for (int k = 0; k < N; ++k) {
-        const int i = tid + kThreads * k, e = i / M, m = i - e * M;
-        idx[k] = e < E ? e * kLine + m : -1;
-      }
-      poll_tagged<N>(w, w.logits, idx, tag, v);
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        const int i = tid + kThreads * k, e = i / M, m = i - e * M;
-        if (e < E) keys[m * E + e] = sel_key(__uint_as_float((uint32_t)v[k]));
-      }
+    for (int k = 0; k < N; ++k) {
+      const int i = tid + kThreads * k, e = i / M, m = i - e * M;
+      idx[k] = e < E ? e * kLine + m : -1;
     }
-    __syncthreads();
-    stamp(w, l, 4);
-    if (wave < M) {
+    poll_tagged<N>(w, w.logits, idx, tag, v);
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const int e = lane + kWave * q;
-        key[q] = e < E ? keys[wave * E + e] : 0u;
-      }
+    for (int k = 0; k < N; ++k) {
+      const int i = tid + kThreads * k, e = i / M, m = i - e * M;
+      if (e < E) keys[m * E + e] = sel_key(__uint_as_float((uint32_t)v[k]));
     }
   }
+  __syncthreads();
+  stamp(w, l, 4);
   if (wave < M) {
     const int m = wave;
-    // threshold: maxima of the 8-lane groups (a group holds experts 8g .. 8g+7 + 64 q)
+    unsigned long long* cm = cand + (size_t)m * stride;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    uint32_t key[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int e = lane + kWave * q;
+      key[q] = keys[m * E + min(e, E - 1)] & (0u - (uint32_t)(e < E));
+    }
     uint32_t lm = key[0];
 #pragma unroll
     for (int q = 1; q < kQ; ++q) lm = max(lm, key[q]);
     lm = max(lm, dpp<0xB1>(lm));
     lm = max(lm, dpp<0x4E>(lm));
     lm = max(lm, dpp<0x141>(lm));
-    const int ngroups = min(kWave / 8, (E + 7) / 8);
-    uint32_t T = 0u;
-    if (ngroups >= K) {
-      T = 0xffffffffu;
-#pragma unroll
-      for (int g = 0; g < kWave / 8; ++g)
-        if (g < ngroups) T = min(T, (uint32_t)__builtin_amdgcn_readlane((int)lm, 8 * g));
-    }
+    uint32_t t = min(lm, dpp<0x128>(lm));
+    const auto h16 = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+    t = min((uint32_t)h16[0], (uint32_t)h16[1]);
+    const auto h32 = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+    t = min((uint32_t)h32[0], (uint32_t)h32[1]);
+    const uint32_t T = max((uint32_t)__builtin_amdgcn_readfirstlane(t), 1u);
     stamp(w, l, 10);
-    // candidates -> LDS in (q, lane) order
-    unsigned long long* cm = cand + m * E;
     int nc = 0;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const bool f = key[q] != 0u && key[q] >= T;
+      const bool f = key[q] >= T;
       const unsigned long long bl = __ballot(f);
-      if (f) cm[nc + __popcll(bl & lt)] = rank_key(key[q], lane + kWave * q);
+      cm[f ? nc + __popcll(bl & lt) : E + lane] = rank_key(key[q], lane + kWave * q);
       nc += __popcll(bl);
     }
+    if (lane == 0) cm[E + kWave] = (unsigned long long)nc;
     stamp(w, l, 11);
-    // ranks (this wave's LDS writes above are visible to its reads: one wave's LDS operations run
-    // in order)
-    for (int j0 = 0; j0 < nc; j0 += kWave) {
-      const int j = j0 + lane;
-      const unsigned long long mine = j < nc ? cm[j] : 0ull;
-      int rank = 0;
-      if (nc <= 2 * kWave) {
-#pragma unroll 4
-        for (int q = 0; q < nc; ++q) rank += cm[q] > mine ? 1 : 0;
-      } else {
-        // many equal logits: stop counting once a candidate is known to be outside the top K
-        for (int q = 0; q < nc && rank < K; ++q) rank += cm[q] > mine ? 1 : 0;
-      }
-      if (j < nc && rank < K) {
-        s_sel[m][rank] = (uint32_t)(mine >> 32);
-        s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)mine);
+  }
+  __syncthreads();
+  {
+    // every token's count and first 64 candidates are read before any ballot
+    int nc[M];
+    unsigned long long o0[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) nc[m] = (int)cand[(size_t)m * stride + E + kWave];
+#pragma unroll
+    for (int m = 0; m < M; ++m) o0[m] = lane < nc[m] ? cand[(size_t)m * stride + lane] : 0ull;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const unsigned long long* cm = cand + (size_t)m * stride;
+      for (int c = wave; c < nc[m]; c += kWaves) {
+        const unsigned long long cc = cm[c];
+        int rank = __popcll(__ballot(o0[m] > cc));
+        for (int j0 = kWave; j0 < nc[m] && rank < K; j0 += kWave) {
+          const unsigned long long o = j0 + lane < nc[m] ? cm[j0 + lane] : 0ull;
+          rank += __popcll(__ballot(o > cc));
+        }
+        if (rank < K && lane == 0) {
+          s_sel[m][rank] = (uint32_t)(cc >> 32);
+          s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)cc);
+        }
       }
     }
-    // softmax over the K selected logits, summed in rank order (the same sum in every lane)
+  }
+  __syncthreads();
+  stamp(w, l, 12);
+  float wr = 0.0f;
+  if (wave == 0) {
+    const UnionLane u = union_lanes<M>(s_idx, K, ns, lane);
+    if (u.first) {
+      un.id[u.slot] = u.e;
+      un.mask[u.slot] = u.mask;
+      un.pair0[u.slot] = u.pair0;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if ((u.mask >> m) & 1u) un.ptok[u.pair0 + __popc(u.mask & ((1u << m) - 1u))] = m;
+    }
+    if (u.e >= 0) un.sel_slot[lane] = u.slot;   // slot of selection (lane / kMaxK, lane % kMaxK)
+    if (lane == 0) {
+      if (ns) {
+        un.id[0] = E;
+        un.mask[0] = (1u << M) - 1u;
+        un.pair0[0] = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          un.w[0][m] = 1.0f;
+          un.ptok[m] = m;
+        }
+      }
+      un.n = u.n;
+      un.n_pairs = u.n_pairs;
+    }
+  } else if (wave <= M) {
+    // softmax over token m's K selections, summed in rank order
+    const int m = wave - 1;
     const float z = lane < K ? expf(key_to_float(s_sel[m][lane]) - key_to_float(s_sel[m][0])) : 0.0f;
     float sum = 0.0f;
     for (int r = 0; r < K; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), r));
-    const float wr = z / sum;
-    if (lane < K) s_w[m][lane] = wr;
-  }
-  {
-    __syncthreads();
-    stamp(w, l, 12);
-    if (wave == 0) {
-      // union in first-occurrence order over (token, rank); slot 0 is the shared expert (if any).
-      // Lane j < M * kMaxK holds selection (j / kMaxK, j % kMaxK) when that rank is < K; every lane
-      // compares its expert with all selections (broadcast LDS reads, no serial lane loop).
-      constexpr int N = M * kMaxK;
-      const int mj = lane / kMaxK, rj = lane % kMaxK;
-      const bool valid = lane < N && rj < K;
-      const int e = valid ? s_idx[mj][rj] : -1;
-      bool first = valid;
-      unsigned mask = 0;
-      float wsum[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) wsum[m] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int mi = i / kMaxK, ri = i % kMaxK;
-        const int ei = ri < K ? s_idx[mi][ri] : -2;
-        if (ei == e) {
-          if (i < lane) first = false;
-          mask |= 1u << mi;
-          wsum[mi] += s_w[mi][ri];
-        }
-      }
-      const unsigned long long firsts = __ballot(first);
-      const int cnt = first ? __popc(mask) : 0;   // this slot's (slot, token) pairs: at most M < 8
-      // exclusive prefix sum of cnt over the lanes, and its total, from three bit planes
-      int before = 0, total = ns * M;
-#pragma unroll
-      for (int bit = 0; bit < 3; ++bit) {
-        const unsigned long long bb = __ballot((cnt >> bit) & 1);
-        before += __popcll(bb & lt) << bit;
-        total += __popcll(bb) << bit;
-      }
-      const int pair0 = ns * M + before;
-      const int slot = ns + __popcll(firsts & lt);
-      if (first) {
-        un.id[slot] = e;
-        un.mask[slot] = mask;
-        un.pair0[slot] = pair0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) un.w[slot][m] = wsum[m];
-      }
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        if (first && ((mask >> m) & 1u)) un.ptok[pair0 + __popc(mask & ((1u << m) - 1u))] = m;
-        if (ns && lane == 0) un.ptok[m] = m;
-      }
-      if (lane == 0) {
-        if (ns) {
-          un.id[0] = E;
-          un.mask[0] = (1u << M) - 1u;
-          un.pair0[0] = 0;
-#pragma unroll
-          for (int m = 0; m < M; ++m) un.w[0][m] = 1.0f;
-        }
-        un.n = __popcll(firsts) + ns;
-        un.n_pairs = total;
+    wr = z / sum;
+    if (lane < K) {
+      s_w[m][lane] = wr;
+      if (blockIdx.x == 0) {
+        if (L.topk_idx) stg(L.topk_idx + m * K + lane, s_idx[m][lane]);
+        if (L.topk_w) stg(L.topk_w + m * K + lane, wr);
       }
     }
   }
+  __syncthreads();
+  if (wave >= 1 && wave <= M && lane < K) un.w[un.sel_slot[(wave - 1) * kMaxK + lane]][wave - 1] = wr;
 }
 
 // ------------------------------------------------------------------------------ the kernel
@@ -804,7 +838,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   const int J = I / kBlk;
 
   // dynamic LDS: x [M][H] bf16 | router rows [nrw][H] bf16 | scratch: selection candidates [M][E]
-  // u64 (+ 65 u64 when M = 1; + keys [M][E] u32 when M > 1), then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
+  // u64 (+ 65 u64 per token; + keys [M][E] u32 when M > 1), then a task's gate/up k-slice sums [4][M][64] fp32 and activation parts [M][4][32] bf16,
   // then the combine's per-wave row sums [waves][M][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
@@ -955,7 +989,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       TaskRegs sreg;
       float sout[kDnTpw];
       task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
-      task_compute<M>(sh, w, sreg, un, 0, xs, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
+      task_compute<M>(sh, w, sreg, un, 0, (1u << M) - 1u, xs, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
     }
     stamp(w, l, 3);
 
@@ -971,14 +1005,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
         if (L.topk_w) stg(L.topk_w + tid, s_w[0][tid]);
       }
     } else {
-      if (E <= 8 * kWave) select_topk<M, 8>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-      else select_topk<M, kMaxE / kWave>(sh, w, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-      if (b == 0 && tid < M * sh.K) {
-        const int m = tid / sh.K, r = tid - m * sh.K;
-        if (L.topk_idx) stg(L.topk_idx + tid, s_idx[m][r]);
-        if (L.topk_w) stg(L.topk_w + tid, s_w[m][r]);
-      }
-      __syncthreads();
+      // the union is in LDS (its weights are read only past a task's first barrier)
+      if (E <= 8 * kWave) select_multi<M, 8>(sh, w, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      else select_multi<M, kMaxE / kWave>(sh, w, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
     }
     stamp(w, l, 5);
 
@@ -1005,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           }
           const uint8_t* nrec =
               gn < n_gr ? task_rec(L, sh, un.id[s0 + gn / jg], (gn % jg) * kg + tn, tid) : nullptr;
-          task_compute<M>(sh, w, cur, un, s0 + gi / jg, xs, red, tid, tag_pt, nrec, 0,
+          task_compute<M>(sh, w, cur, un, s0 + gi / jg, un.mask[s0 + gi / jg], xs, red, tid, tag_pt, nrec, 0,
                           s0 * M * J + gi % jg, t == 0, t == kg - 1, outv);
           if (!nrec) break;
           gi = gn;
@@ -1186,8 +1215,9 @@ constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
   // scratch: selection keys, then a task's gate/up sums and activation parts, then the combine's
   // per-wave row sums
-  // (one token: 64 more candidate slots, written by the lanes without a candidate, and the count)
-  const size_t sel = M > 1 ? (size_t)M * E * 12 : (size_t)(E + kWave + 1) * 8, gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
+  // (per token: E candidates, 64 slots written by the lanes without a candidate, and the count;
+  // several tokens: then their keys [M][E] u32)
+  const size_t sel = (size_t)M * (E + kWave + 1) * 8 + (M > 1 ? (size_t)M * E * 4 : 0), gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
   const size_t comb = (size_t)kWaves * M * kLine * 4;
   const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
   return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
