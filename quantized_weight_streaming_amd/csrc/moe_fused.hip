@@ -1318,17 +1318,21 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   if (st != QWS_OK) return st;
   const int J = I / kBlk;
   const int nrw = (E + G - 1) / G;
-  const int R = ((H + G - 1) / G + 1) & ~1;   // even, so a thread writes a bf16 pair of one token
-  if (G > kMaxGrid || G < J || nrw > kWaves || R > kMaxRows) return QWS_ERR_SHAPE;
+  // rows per owner: even, so that a thread writes a bf16 pair of one token
+  const int R_all = ((H + G - 1) / G + 1) & ~1;   // every workgroup owns rows
+  if (G > kMaxGrid || G < J || nrw > kWaves || R_all > kMaxRows) return QWS_ERR_SHAPE;
   const int P = M * (K + 1);
   const size_t lds = lds_bytes(M, E, H, P, J, nrw);
   if (lds > kMaxDynLds) return QWS_ERR_SHAPE;
   // Chained: layer l+1 reads y of layer l. Then the layers need no barrier, provided every
   // workgroup computes router rows and owns output rows, so that no workgroup can fall a layer
   // behind the others (each layer waits for every workgroup's logits and every owner's y).
-  bool chained = n_layers > 1 && E >= G && (size_t)(G - 1) * R < (size_t)H;
+  bool chained = n_layers > 1 && E >= G && (size_t)(G - 1) * R_all < (size_t)H;
   for (int l = 0; chained && l + 1 < n_layers; ++l)
     chained = host[l].y_bf16 != nullptr && host[l + 1].x_bf16 == host[l].y_bf16;
+  // Otherwise an owner takes one whole 128-byte line of every partial-sum vector (kLine rows,
+  // when the grid has owners for all of them): it reads no line another owner also reads.
+  const int R = !chained && (size_t)G * kLine >= (size_t)H ? kLine : R_all;
   Work w;
   ws_layout(M, K, E, H, I, static_cast<char*>(workspace), &w);
   {
