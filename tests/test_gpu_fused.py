@@ -120,6 +120,46 @@ def test_fused_window_m4(regime, union):
         assert len(set(L.topk_idx.cpu().numpy().reshape(-1).tolist())) == union
 
 
+def _zero_router(layer: Layer) -> Layer:
+    layer.wr = np.zeros_like(layer.wr)
+    layer.wr_t = torch.zeros_like(layer.wr_t)
+    return layer
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_fused_all_logits_tied(M):
+    """Zero router weights: every logit is 0.0 and all 512 experts tie (far more candidates than
+    one wave holds), so the selection is experts 0 .. K-1 (ties go to the lower index) with
+    weights 1/K, and y follows the oracle."""
+    say("fused all tied", M)
+    layer = _zero_router(Layer(0, 0, synth.LayerShape(), M))
+    L = _fused(layer)
+    K = layer.shape.topk
+    ridx, rw, _ = layer.oracle_route()
+    assert np.array_equal(ridx, np.tile(np.arange(K), (M, 1)))
+    assert L.topk_idx.cpu().numpy().tolist() == ridx.tolist()
+    assert np.all(L.topk_w.cpu().numpy() == np.float32(1.0 / K))
+    assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"all tied M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_fused_many_tied_candidates(M):
+    """Zero router weights and a bias of 1.0 on 100 seeded experts: those 100 tie above the rest
+    (two waves' worth of candidates) and the K lowest indices among them are selected."""
+    say("fused 100 tied", M)
+    shape = synth.LayerShape()
+    top = np.random.default_rng(11).choice(shape.n_routed, 100, replace=False)
+    bias = np.zeros(shape.n_routed, dtype=np.float32)
+    bias[top] = 1.0
+    layer = _zero_router(Layer(0, 0, shape, M, bias=bias))
+    L = _fused(layer)
+    ridx, rw, _ = layer.oracle_route()
+    want = np.sort(top)[:shape.topk]
+    assert np.array_equal(ridx, np.tile(want, (M, 1)))
+    assert L.topk_idx.cpu().numpy().tolist() == ridx.tolist()
+    assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"100 tied M={M}")
+
+
 def test_fused_matches_two_call_routing():
     say("fused vs two-call")
     layer = Layer(8, 0, synth.LayerShape(), 4)
