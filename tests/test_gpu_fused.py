@@ -103,6 +103,15 @@ def test_fused_layer_m1(E):
     _check_layer(Layer(0, 0, synth.LayerShape(n_routed=E), 1), _fused(Layer(0, 0, synth.LayerShape(n_routed=E), 1)))
 
 
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_fused_layer_1024_experts(M):
+    """More than 512 routed experts: a lane holds 16 logits in the selection and a workgroup
+    computes four router rows."""
+    say("fused layer E=1024 M", M)
+    layer = Layer(3, 0, synth.LayerShape(hidden=256, inter=64, n_routed=1024), M)
+    _check_layer(layer, _fused(layer))
+
+
 def test_fused_layer_zipf():
     say("fused layer zipf")
     layer = Layer(1, 0, synth.LayerShape(), 1, bias=synth.zipf_bias(1, 0, 512))
