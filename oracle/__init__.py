@@ -18,9 +18,14 @@ Inference Optimizations NVIDIA Measured on DGX Spark"):
 * ``lmhead``   -- online per-row FP8 quantisation of the bf16 head and the head GEMV in FP8 and
   bf16 (posts/593 paragraph 3; Netics "Online FP8 quantization halves the LM head weight reads").
 
+* ``verify``   -- the verification epilogue of a speculative window after the head: per-position
+  argmax, greedy prefix acceptance of the drafts, and top-k / top-p sampling at a temperature
+  with the caller's uniform draw (signal/190 and the Netics post on speculative decoding).
+
 Pins (all in ``tests/test_oracle_*.py``): closed forms of the formats, exhaustive comparison with
 torch's float8_e4m3fn, brute force in pure-Python loops at tiny shapes, the one-hot routing that
 reduces the layer to a single dense FFN, x = 0 routing, exact ties, one-hot LM-head inputs, and
-the pages' printed byte counts. No function here is "parity unpinned".
+the pages' printed byte counts, hand-worked verification windows, closed forms of the sampling
+distribution and its inversion checked by frequency. No function here is "parity unpinned".
 """
-from . import formats, lmhead, moe  # noqa: F401
+from . import formats, lmhead, moe, verify  # noqa: F401
