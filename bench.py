@@ -377,9 +377,20 @@ def main():
             reg: round(layer_bytes(breakdown[f"moe_layer_m4_{reg}"]["union"], 4) / layer_bytes(K_TOP, 1), 3)
             for reg in synth.REGIMES}
         xh = step.xh
+        # a verification window of four positions: the head GEMV alone, and with the greedy
+        # epilogue fused (targets, accepted prefix of three synthetic drafts; logits still written)
+        x4 = _bf16(synth.token_vectors(0, 1001, 4), dev)
+        lg4 = torch.empty((4, head8.rows), dtype=torch.float32, device=dev)
+        ws_v = qws.verify_workspace(4, dev)
+        draft = torch.tensor([1, 2, 3], dtype=torch.int32, device=dev)
+        vout = qws.lmhead_verify_greedy_fp8(head8, x4, draft, ws_v, logits=lg4)
         for name, fn, nb in (("lmhead_fp8_m1", lambda: qws.lmhead_gemv_fp8(head8, xh, out=step.logits), head_bytes(1)),
                              ("lmhead_bf16_m1", lambda: qws.lmhead_gemv_bf16(head_bf16, xh, out=step.logits),
-                              head_bytes(1, fp8=False))):
+                              head_bytes(1, fp8=False)),
+                             ("lmhead_fp8_m4", lambda: qws.lmhead_gemv_fp8(head8, x4, out=lg4), head_bytes(4)),
+                             ("lmhead_verify_greedy_fp8_m4",
+                              lambda: qws.lmhead_verify_greedy_fp8(head8, x4, draft, ws_v, logits=lg4, out=vout),
+                              head_bytes(4))):
             t = time_cold(fn, dev, flush=flush)
             t.update({"bytes": nb, "GBps": round(nb / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)

@@ -257,6 +257,25 @@ int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long cols,
 int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
                     qws_stream_t stream);
 
+/* Greedy verification of a speculative window after the FP8 head. The configuration drafts
+ * three tokens and verifies a four-position window at once, accepting the correct prefix
+ * (runbyai.xyz/signal/190, the paragraph on speculative decoding; Netics post, "Speculative
+ * decoding reduces the number of steps"); greedy decoding is the pages' synthetic run.
+ *   x_bf16 [M, cols], 1 <= M <= 4 (the window's positions); draft [M - 1] int32 (NULL allowed
+ *   when M = 1); logits_out NULL or fp32 [M, rows] (the same values as lmhead_gemv_fp8);
+ *   target_out [M]: each position's argmax (ties to the lower row; NaN below every number);
+ *   emitted_out [M] and n_out [1]: draft i (i < M - 1) is accepted while it equals target i, then
+ *   the target of the first position not accepted: emitted[0 .. n) with n in 1 .. M, emitted[i]
+ *   = -1 for i >= n. All of these are device memory owned by the caller.
+ *   workspace: lmhead_verify_workspace_bytes(M) bytes, 16-byte aligned, zero-filled before its
+ *   first use and left ready for the next call; calls that share it must not overlap.
+ * Errors: QWS_ERR_FORMAT for a head that is not FP8-tagged, QWS_ERR_ARG for a missing pointer,
+ * QWS_ERR_SHAPE for M outside 1 .. 4, QWS_ERR_WORKSPACE / QWS_ERR_ALIGN as elsewhere. */
+size_t lmhead_verify_workspace_bytes(int M);
+int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                             float* logits_out, int* target_out, int* emitted_out, int* n_out,
+                             void* workspace, size_t workspace_bytes, qws_stream_t stream);
+
 /* logits[m, r] = sum_k W[r, k] * x[m, k]   (head must be BF16-tagged; an FP8 head is refused
  * with QWS_ERR_FORMAT instead of being read as bf16). Same shapes as lmhead_gemv_fp8.       */
 int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,

@@ -27,7 +27,8 @@ from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
-           "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "debug_dequant_mxfp4", "debug_dequant_fp8",
+           "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_verify_greedy_fp8",
+           "verify_workspace", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
 
@@ -319,6 +320,32 @@ def lmhead_gemv_fp8(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
 
 def lmhead_gemv_bf16(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
     return _gemv("lmhead_gemv_bf16", head, x, out)
+
+
+def verify_workspace(M: int, device) -> torch.Tensor:
+    """Zero-filled workspace of lmhead_verify_greedy_fp8 for windows of up to M positions."""
+    n = int(lib().lmhead_verify_workspace_bytes(M))
+    if n == 0:
+        raise QwsError("lmhead_verify_workspace_bytes", _lib.QWS_ERR_SHAPE)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def lmhead_verify_greedy_fp8(head: LMHead, x: torch.Tensor, draft: torch.Tensor | None, workspace: torch.Tensor,
+                             logits: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """Greedy verification of an M-position window: {"target": int32 [M], "emitted": int32 [M],
+    "n": int32 [1]} (device tensors; reused from `out` when given), logits into `logits` if given."""
+    _need(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = {k: torch.empty(n, dtype=torch.int32, device=dev) for k, n in (("target", M), ("emitted", M), ("n", 1))}
+    if draft is not None and (draft.dtype != torch.int32 or draft.numel() != M - 1 or draft.device != dev):
+        raise ValueError("draft: int32 [M - 1] on the device of x")
+    st = lib().lmhead_verify_greedy_fp8(C.byref(head.desc), _p(x), M, None if draft is None else _p(draft),
+                                        None if logits is None else _p(logits), _p(out["target"]), _p(out["emitted"]),
+                                        _p(out["n"]), _p(workspace), workspace.numel(), _stream(dev))
+    check("lmhead_verify_greedy_fp8", st)
+    return out
 
 
 # ----------------------------------------------------------------------------------- diagnostics

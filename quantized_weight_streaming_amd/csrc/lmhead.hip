@@ -81,6 +81,40 @@ __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const uint16_t* __
 }
 
 // --------------------------------------------------------------------------- FP8 GEMV
+// This lane's share of x: chunks j + 32 t (16 bf16 each) of every token.
+template <int M>
+__device__ __forceinline__ void fp8_load_x(const uint16_t* __restrict__ x, int cols, int j, u32x4_t (&xr)[M][kCpl][2]) {
+  const int nch = cols >> 4;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int t = 0; t < kCpl; ++t) {
+      const int c = j + 32 * t;
+      xr[m][t][0] = c < nch ? ld16(x + (size_t)m * cols + c * 16) : u32x4_t{0, 0, 0, 0};
+      xr[m][t][1] = c < nch ? ld16(x + (size_t)m * cols + c * 16 + 8) : u32x4_t{0, 0, 0, 0};
+    }
+}
+// This lane's partial dot products of one row (its 5 chunks of 16 codes) with the M tokens.
+template <int M>
+__device__ __forceinline__ void fp8_row_dots(const u32x4_t (&w)[kCpl], const u32x4_t (&xr)[M][kCpl][2], float (&acc)[M]) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kCpl; ++t) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x2_t lo = fp8x2_to_bf16x2<false>(w[t][d]);
+      const bf16x2_t hi = fp8x2_to_bf16x2<true>(w[t][d]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        // codes 4d..4d+3 of the chunk pair with bf16 elements 4d..4d+3: x dwords 2d, 2d+1
+        acc[m] = dot2(lo, as_bf16x2(xr[m][t][d >> 1][(2 * d) & 3]), acc[m]);
+        acc[m] = dot2(hi, as_bf16x2(xr[m][t][d >> 1][(2 * d + 1) & 3]), acc[m]);
+      }
+    }
+  }
+}
+
 template <int M>
 __global__ __launch_bounds__(kBlock) void gemv_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scale,
                                                           long long rows, int cols, const uint16_t* __restrict__ x,
@@ -94,14 +128,7 @@ __global__ __launch_bounds__(kBlock) void gemv_fp8_kernel(const uint8_t* __restr
   if (p >= npairs) return;
 
   u32x4_t xr[M][kCpl][2];
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int t = 0; t < kCpl; ++t) {
-      const int c = j + 32 * t;
-      xr[m][t][0] = c < nch ? ld16(x + (size_t)m * cols + c * 16) : u32x4_t{0, 0, 0, 0};
-      xr[m][t][1] = c < nch ? ld16(x + (size_t)m * cols + c * 16 + 8) : u32x4_t{0, 0, 0, 0};
-    }
+  fp8_load_x<M>(x, cols, j, xr);
 
   auto load = [&](long long pp, u32x4_t (&wq)[kCpl]) {
     const long long row = 2 * pp + half;
@@ -116,22 +143,7 @@ __global__ __launch_bounds__(kBlock) void gemv_fp8_kernel(const uint8_t* __restr
   for (; p < npairs; p += nwaves) {
     if (p + nwaves < npairs) load(p + nwaves, nxt);
     float acc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kCpl; ++t) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x2_t lo = fp8x2_to_bf16x2<false>(cur[t][d]);
-        const bf16x2_t hi = fp8x2_to_bf16x2<true>(cur[t][d]);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          // codes 4d..4d+3 of the chunk pair with bf16 elements 4d..4d+3: x dwords 2d, 2d+1
-          acc[m] = dot2(lo, as_bf16x2(xr[m][t][d >> 1][(2 * d) & 3]), acc[m]);
-          acc[m] = dot2(hi, as_bf16x2(xr[m][t][d >> 1][(2 * d + 1) & 3]), acc[m]);
-        }
-      }
-    }
+    fp8_row_dots<M>(cur, xr, acc);
     const long long row = 2 * p + half;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -140,6 +152,114 @@ __global__ __launch_bounds__(kBlock) void gemv_fp8_kernel(const uint8_t* __restr
     }
 #pragma unroll
     for (int t = 0; t < kCpl; ++t) cur[t] = nxt[t];
+  }
+}
+
+// --------------------------------------------------------------------------- greedy verification
+// The FP8 GEMV of a verification window (M positions) with the epilogue fused: each wave keeps,
+// per position, the largest (logit, lower row) key of its rows; a workgroup stores the maximum of
+// its waves; the last workgroup to arrive (two-level arrival) reduces them to each position's
+// target token and forms the accepted prefix of the M - 1 draft tokens.
+template <int M>
+__global__ __launch_bounds__(kBlock) void verify_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scale,
+                                                            long long rows, int cols, const uint16_t* __restrict__ x,
+                                                            float* __restrict__ out, const int* __restrict__ draft,
+                                                            int* __restrict__ target_out, int* __restrict__ emitted_out,
+                                                            int* __restrict__ n_out, unsigned long long* __restrict__ keys,
+                                                            unsigned* __restrict__ counters) {
+  __shared__ unsigned long long s_best[kWavesPerBlock][M];
+  __shared__ bool s_last;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int half = lane >> 5, j = lane & 31;
+  const int nch = cols >> 4;
+  const long long npairs = (rows + 1) >> 1;
+  const long long nwaves = (long long)gridDim.x * kWavesPerBlock;
+  long long p = (long long)blockIdx.x * kWavesPerBlock + wave;
+  unsigned long long best[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) best[m] = 0ull;   // below every key
+
+  if (p < npairs) {   // no early return: every workgroup arrives below
+    u32x4_t xr[M][kCpl][2];
+    fp8_load_x<M>(x, cols, j, xr);
+    auto load = [&](long long pp, u32x4_t (&wq)[kCpl]) {
+      const long long row = 2 * pp + half;
+#pragma unroll
+      for (int t = 0; t < kCpl; ++t) {
+        const int c = j + 32 * t;
+        wq[t] = (row < rows && c < nch) ? ld16_weights(q + row * cols + c * 16) : u32x4_t{0, 0, 0, 0};
+      }
+    };
+    u32x4_t cur[kCpl], nxt[kCpl];
+    load(p, cur);
+    for (; p < npairs; p += nwaves) {
+      if (p + nwaves < npairs) load(p + nwaves, nxt);
+      float acc[M];
+      fp8_row_dots<M>(cur, xr, acc);
+      const long long row = 2 * p + half;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = scale[row < rows ? row : rows - 1] * group_sum<32>(acc[m]);
+        if (out && j == 0 && row < rows) out[(size_t)m * rows + row] = v;
+        const unsigned long long k = row < rows ? rank_key(sel_key(v), (int)row) : 0ull;
+        best[m] = k > best[m] ? k : best[m];
+      }
+#pragma unroll
+      for (int t = 0; t < kCpl; ++t) cur[t] = nxt[t];
+    }
+  }
+  // the two half-waves' rows, then the waves of the workgroup
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const unsigned long long o = __shfl_xor(best[m], 32, kWave);
+    best[m] = o > best[m] ? o : best[m];
+    if (lane == 0) s_best[wave][m] = best[m];
+  }
+  __syncthreads();
+  if (threadIdx.x < M) {
+    unsigned long long k = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) k = s_best[w][threadIdx.x] > k ? s_best[w][threadIdx.x] : k;
+    st_coherent(keys + (size_t)blockIdx.x * M + threadIdx.x, k);
+  }
+  if (!arrive_last_grid(counters, &s_last)) return;
+
+  // last workgroup: every workgroup's keys (device-coherent loads), then the window
+#pragma unroll
+  for (int m = 0; m < M; ++m) best[m] = 0ull;
+  for (unsigned g = threadIdx.x; g < gridDim.x; g += kBlock)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const unsigned long long k = ld_coherent(keys + (size_t)g * M + m);
+      best[m] = k > best[m] ? k : best[m];
+    }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long k = __shfl_xor(best[m], o, kWave);
+      best[m] = k > best[m] ? k : best[m];
+    }
+    if (lane == 0) s_best[wave][m] = best[m];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int target[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) k = s_best[w][m] > k ? s_best[w][m] : k;
+      target[m] = (int)(0xffffffffu - (uint32_t)k);
+      target_out[m] = target[m];
+    }
+    // draft i is accepted while it equals the target of position i; then the target of the first
+    // position not accepted
+    int a = 0;
+    while (a < M - 1 && draft[a] == target[a]) ++a;
+#pragma unroll
+    for (int i = 0; i < M; ++i) emitted_out[i] = i < a ? draft[i] : (i == a ? target[a] : -1);
+    *n_out = a + 1;
   }
 }
 
@@ -191,11 +311,12 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_kernel(const uint16_t* __res
   }
 }
 
+// 16 workgroups per CU; each wave loops over the rest (4096 .. 8192 workgroups measured best on
+// MI355X for the 157,184-row head, ~3% ahead of 2048 and ~10% ahead of one unit per wave)
+constexpr int kHeadGrid = 4096;
 int grid_for(long long units) {
-  // 16 workgroups per CU; each wave loops over the rest (4096 .. 8192 workgroups measured best
-  // on MI355X for the 157,184-row head, ~3% ahead of 2048 and ~10% ahead of one unit per wave)
   long long blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  return (int)(blocks < 4096 ? blocks : 4096);
+  return (int)(blocks < kHeadGrid ? blocks : kHeadGrid);
 }
 
 int check_head(const qws_lmhead* h, unsigned fmt) {
@@ -247,6 +368,42 @@ extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M
     case 3: hipLaunchKernelGGL(gemv_fp8_kernel<3>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
     default: hipLaunchKernelGGL(gemv_fp8_kernel<4>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
   }
+  return qws_host::check_launch();
+}
+
+extern "C" size_t lmhead_verify_workspace_bytes(int M) {
+  if (M < 1 || M > 4) return 0;
+  return qws_host::align256((size_t)kHeadGrid * M * 8) + (size_t)(kArriveGroups + 1) * kCounterStride * 4;
+}
+
+extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                                        float* logits_out, int* target_out, int* emitted_out, int* n_out,
+                                        void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  if (st != QWS_OK) return st;
+  if (!x_bf16 || !target_out || !emitted_out || !n_out || (M > 1 && !draft)) return QWS_ERR_ARG;
+  if (M < 1 || M > 4) return QWS_ERR_SHAPE;
+  if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
+  if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
+  const uint8_t* q = static_cast<const uint8_t*>(head->w);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const int cols = (int)head->cols;
+  unsigned long long* keys = static_cast<unsigned long long*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                                   qws_host::align256((size_t)kHeadGrid * M * 8));
+  dim3 grid(grid_for((head->rows + 1) / 2)), block(kBlock);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define QWS_VERIFY(MM)                                                                                            \
+  hipLaunchKernelGGL(verify_fp8_kernel<MM>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out, \
+                     draft, target_out, emitted_out, n_out, keys, counters)
+  switch (M) {
+    case 1: QWS_VERIFY(1); break;
+    case 2: QWS_VERIFY(2); break;
+    case 3: QWS_VERIFY(3); break;
+    default: QWS_VERIFY(4); break;
+  }
+#undef QWS_VERIFY
   return qws_host::check_launch();
 }
 

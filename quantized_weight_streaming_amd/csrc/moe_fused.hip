@@ -284,21 +284,6 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
   __syncthreads();
 }
 
-// Selection key: order-preserving float -> uint32 (larger float, larger key; -0 == +0; NaN ranks
-// as -inf). Every logit maps to >= 0x007fffff; 0 marks an absent entry.
-__device__ __forceinline__ uint32_t sel_key(float f) {
-  f = f != f ? -__builtin_inff() : f + 0.0f;   // -0 + 0 = +0 (round to nearest)
-  const uint32_t u = __float_as_uint(f);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: ~u, else u | sign bit
-}
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-// Total order of the selection: larger key first, then lower expert index.
-__device__ __forceinline__ unsigned long long rank_key(uint32_t key, int e) {
-  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
-}
-
 // Non-temporal 16-byte load of weights that are read once per step.
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);

@@ -161,6 +161,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// ------------------------------------------------------------------------------ selection keys
+// Order-preserving float -> uint32 (larger float, larger key; -0 == +0; NaN ranks as -inf).
+// Every number maps to >= 0x007fffff, so 0 can mark an absent entry.
+__device__ __forceinline__ uint32_t sel_key(float f) {
+  f = f != f ? -__builtin_inff() : f + 0.0f;   // -0 + 0 = +0 (round to nearest)
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: ~u, else u | sign bit
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Total order of a selection: larger key first, then lower index (the maximum is the winner).
+__device__ __forceinline__ unsigned long long rank_key(uint32_t key, int i) {
+  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+}
+
 // ------------------------------------------------------------------------------ sync
 // Cross-workgroup hand-off inside one kernel, without an agent-scope fence. On gfx950 such a
 // fence writes back the whole L2 of the XCD and invalidates it, and every wave that executes one

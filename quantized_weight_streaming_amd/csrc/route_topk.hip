@@ -14,18 +14,6 @@ constexpr int kRouteCpl = 5;            // 16-byte chunks per lane: H <= 64 * 5 
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;
 
-// Order-preserving map float -> uint32 (larger float, larger key); -0 equals +0; NaN ranks as
-// -inf (ties with it go to the lower index, as for any equal logits).
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-  if (f != f) f = -__builtin_inff();
-  if (f == 0.0f) f = 0.0f;
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -45,7 +33,7 @@ __device__ void select_topk(const float* __restrict__ lg, int E, int K, int* __r
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     int e = lane + i * kWave;
-    key[i] = e < E ? ((unsigned long long)ordered_key(ld_coherent(lg + e)) << 32) | (0xffffffffu - (unsigned)e) : 0ull;
+    key[i] = e < E ? ((unsigned long long)sel_key(ld_coherent(lg + e)) << 32) | (0xffffffffu - (unsigned)e) : 0ull;
   }
   float sel_v[8];
   int sel_i[8];

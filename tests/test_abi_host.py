@@ -145,6 +145,30 @@ def test_lmhead_desc_and_quantize_validation(lib):
     assert lib.lmhead_quantize_fp8(A, 10, 64, MIS, A, C.byref(d), None) == _lib.QWS_ERR_ALIGN
 
 
+def test_verify_validation(lib):
+    bf = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, 100, 64, A, None))
+    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 100, 64, A, A))
+    wsb = lib.lmhead_verify_workspace_bytes(4)
+    assert wsb > 0 and lib.lmhead_verify_workspace_bytes(0) == 0 and lib.lmhead_verify_workspace_bytes(5) == 0
+    ok = dict(head=fp8, x=A, M=4, draft=A, lg=None, t=A, e=A, n=A, ws=A, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lmhead_verify_greedy_fp8(a["head"], a["x"], a["M"], a["draft"], a["lg"], a["t"], a["e"], a["n"],
+                                            a["ws"], a["wsb"], None)
+    assert call(head=bf) == _lib.QWS_ERR_FORMAT
+    assert call(x=None) == _lib.QWS_ERR_ARG
+    assert call(draft=None) == _lib.QWS_ERR_ARG
+    assert call(t=None) == _lib.QWS_ERR_ARG
+    assert call(n=None) == _lib.QWS_ERR_ARG
+    assert call(M=0) == _lib.QWS_ERR_SHAPE
+    assert call(M=5) == _lib.QWS_ERR_SHAPE
+    assert call(x=MIS) == _lib.QWS_ERR_ALIGN
+    assert call(ws=MIS) == _lib.QWS_ERR_ALIGN
+    assert call(wsb=wsb - 1) == _lib.QWS_ERR_WORKSPACE
+    assert call(ws=None) == _lib.QWS_ERR_WORKSPACE
+
+
 def test_diagnostics_validation(lib):
     assert lib.qws_debug_dequant_mxfp4(A, A, 4, 64, 2, A, None) == _lib.QWS_ERR_ARG
     assert lib.qws_debug_dequant_mxfp4(A, A, 4, 48, 0, A, None) == _lib.QWS_ERR_SHAPE
