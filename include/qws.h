@@ -226,9 +226,14 @@ int moe_workspace_errors(const void* workspace, int M, int K, int E, int inter, 
  * every generated token reads all of it: ~805 MB per token in bf16, half in FP8 (posts/593
  * paragraph 3).
  *   format QWS_FMT_BF16:                w = bf16 [rows, cols], row_scale NULL.
- *   format QWS_FMT_FP8_E4M3FN_ROWSCALE: w = E4M3 codes u8 [rows, cols], row_scale fp32 [rows];
- *                                       weight[r, k] = e4m3(w[r, k]) * row_scale[r].
+ *   format QWS_FMT_FP8_E4M3FN_ROWSCALE: w = E4M3 codes u8, tile-major (below), row_scale fp32
+ *                                       [rows]; weight[r, k] = e4m3(q[r, k]) * row_scale[r].
  * rows >= 1; cols multiple of 32, 32 .. 2560.
+ * Tile-major FP8 codes (lmhead_fp8_codes_bytes(rows, cols) bytes): the rows in tiles of 16, the
+ * last one padded with zero-code rows; tile t starts at byte 16 t cols; inside it, the 16 codes
+ * q[16 t + i, 16 c .. 16 c + 15] (chunk c of tile row i) are at byte 16 (16 c + i). A wave of the
+ * GEMV then reads 1 KB of consecutive bytes per load instruction: 4 chunks of 16 rows, the
+ * operand of one matrix-core product each.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   unsigned format;
@@ -246,14 +251,22 @@ int lmhead_bf16_desc(const void* w_bf16, long long rows, long long cols, qws_lmh
  *   s_r = fl32(max_k |W[r, k]| / 448)  (s_r = 1 for an all-zero row)
  *   q[r, k] = E4M3(fl32(W[r, k] / s_r)), round to nearest even, saturating at +-448
  * Both divisions are IEEE float32 round-to-nearest-even.
- *   w_bf16 [rows, cols] in; codes_out u8 [rows, cols] and row_scale_out fp32 [rows] out.
- *   desc_out (host memory) is filled with an FP8-tagged descriptor of the outputs.         */
+ *   w_bf16 [rows, cols] in; codes_out u8, lmhead_fp8_codes_bytes(rows, cols) bytes (tile-major,
+ *   pad rows written as zero codes) and row_scale_out fp32 [rows] out, all device memory owned by
+ *   the caller. desc_out (host memory) is filled with an FP8-tagged descriptor of the outputs.
+ * Errors: QWS_ERR_ARG for a missing pointer, QWS_ERR_SHAPE for rows or cols out of range,
+ * QWS_ERR_ALIGN for w_bf16 or codes_out not 16-byte aligned.                                 */
 int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long cols,
                         unsigned char* codes_out, float* row_scale_out, qws_lmhead* desc_out,
                         qws_stream_t stream);
 
+/* Bytes of the tile-major FP8 codes of a rows x cols head: ceil(rows / 16) * 16 * cols; 0 for
+ * rows or cols out of range. */
+size_t lmhead_fp8_codes_bytes(long long rows, long long cols);
+
 /* logits[m, r] = row_scale[r] * sum_k e4m3(q[r, k]) * x[m, k]   (head must be FP8-tagged)
- *   x_bf16 [M, cols], 1 <= M <= 4; logits_out fp32 [M, rows].                              */
+ *   x_bf16 [M, cols], 1 <= M <= 4; logits_out fp32 [M, rows]. Each token gets the same logits,
+ *   bit for bit, whatever M and its place in the window.                                    */
 int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
                     qws_stream_t stream);
 
@@ -291,7 +304,8 @@ int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* l
 int qws_debug_dequant_mxfp4(const unsigned char* q, const unsigned char* s, long long rows,
                             int cols, int path, float* out, qws_stream_t stream);
 
-/* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for an FP8-tagged head, fp32 [rows, cols].  */
+/* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for an FP8-tagged head (tile-major codes),
+ * fp32 [rows, cols] row-major.                                                              */
 int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t stream);
 
 /* Tracing of the fused MoE launches on the current device: while `buf` is registered (device

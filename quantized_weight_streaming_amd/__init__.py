@@ -27,7 +27,8 @@ from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
-           "lmhead_quantize_fp8", "lmhead_gemv_fp8", "lmhead_gemv_bf16", "lmhead_verify_greedy_fp8",
+           "lmhead_quantize_fp8", "lmhead_fp8_codes_bytes", "fp8_codes_rowmajor", "lmhead_gemv_fp8", "lmhead_gemv_bf16",
+           "lmhead_verify_greedy_fp8",
            "verify_workspace", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
@@ -290,18 +291,40 @@ def lmhead_bf16(w: torch.Tensor) -> LMHead:
     return LMHead(w, None, d)
 
 
+def lmhead_fp8_codes_bytes(rows: int, cols: int) -> int:
+    """Bytes of the tile-major FP8 codes of a rows x cols head (rows padded to a multiple of 16)."""
+    n = int(lib().lmhead_fp8_codes_bytes(rows, cols))
+    if n == 0:
+        raise QwsError("lmhead_fp8_codes_bytes", _lib.QWS_ERR_SHAPE)
+    return n
+
+
 def lmhead_quantize_fp8(w: torch.Tensor, codes=None, row_scale=None) -> LMHead:
-    """Online per-row FP8 quantisation of a bf16 head (done once, at construction)."""
+    """Online per-row FP8 quantisation of a bf16 head (done once, at construction). The codes are
+    a flat uint8 tensor in the tile-major layout of the library (fp8_codes_rowmajor undoes it)."""
     _need(w, "w", torch.bfloat16, 2)
     rows, cols = w.shape
+    n = lmhead_fp8_codes_bytes(rows, cols)
     if codes is None:
-        codes = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+        codes = torch.empty(n, dtype=torch.uint8, device=w.device)
+    elif codes.dtype != torch.uint8 or not codes.is_contiguous() or codes.numel() < n:
+        raise ValueError(f"codes must be contiguous uint8 with at least {n} elements")
     if row_scale is None:
         row_scale = torch.empty(rows, dtype=torch.float32, device=w.device)
     d = LMHeadDesc()
     st = lib().lmhead_quantize_fp8(_p(w), rows, cols, _p(codes), _p(row_scale), C.byref(d), _stream(w.device))
     check("lmhead_quantize_fp8", st)
     return LMHead(codes, row_scale, d)
+
+
+def fp8_codes_rowmajor(head: LMHead) -> torch.Tensor:
+    """The E4M3 codes of an FP8 head as uint8 [rows, cols], row-major (a copy, on the head's
+    device): tile t of 16 rows starts at byte 16 t cols and holds chunk c (16 codes) of its row i
+    at byte 16 (16 c + i)."""
+    rows, cols = head.desc.rows, head.desc.cols
+    tiles = (rows + 15) // 16
+    t = head.w[:tiles * 16 * cols].view(tiles, cols // 16, 16, 16)   # tile, chunk, row, byte
+    return t.permute(0, 2, 1, 3).reshape(tiles * 16, cols)[:rows].contiguous()
 
 
 def _gemv(fn: str, head: LMHead, x: torch.Tensor, out):

@@ -62,6 +62,7 @@ SIGNATURES = {
     "moe_workspace_errors": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_uint), _P]),
     "lmhead_bf16_desc": (_I, [_P, _LL, _LL, C.POINTER(LMHeadDesc)]),
     "lmhead_quantize_fp8": (_I, [_P, _LL, _LL, _P, _P, C.POINTER(LMHeadDesc), _P]),
+    "lmhead_fp8_codes_bytes": (_SZ, [_LL, _LL]),
     "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "lmhead_verify_workspace_bytes": (_SZ, [_I]),
     "lmhead_verify_greedy_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -129,7 +129,8 @@ __global__ void dequant_fp8_kernel(const uint8_t* __restrict__ q, const float* _
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
     const long long r = i / nch;
     const int c = (int)(i % nch);
-    const u32x4_t w = ld16(q + r * cols + (size_t)c * 16);
+    // tile-major codes: tile r / 16 at byte 16 (r / 16) cols, chunk c of tile row r % 16 at 16 (16c + r % 16)
+    const u32x4_t w = ld16(q + (r >> 4) * 16 * (long long)cols + (16ll * c + (r & 15)) * 16);
     const float sc = scale[r];
     float4* o = reinterpret_cast<float4*>(out + r * cols + (size_t)c * 16);
 #pragma unroll

@@ -2,15 +2,17 @@
 // head GEMV in FP8 and in bf16, for M <= 4 token vectors, float32 logits.
 // The head is 157,184 x 2,560 and every token reads all of it: ~805 MB in bf16, half in FP8
 // (runbyai.xyz/posts/593 paragraph 3; Netics, "Online FP8 quantization halves the LM head weight
-// reads"). At M = 1 the GEMV is a pure HBM stream, so the kernels are built around keeping many
+// reads"). For M <= 4 the GEMV is a pure HBM stream, so the kernels are built around keeping many
 // 128-bit loads in flight per lane, and the weights are read with non-temporal loads (measured on
 // MI355X over the 402 MB FP8 head: 63.6 us against 71.4 us with ordinary loads, whose lines are
 // kept in the caches that a read-once stream never revisits):
-//  - FP8: half a wave (32 lanes) per row, 5 x 16 B per lane; x (bf16) stays in VGPRs for the whole
-//    grid-stride loop, the next row pair's loads are issued before the current pair is reduced.
-//    E4M3 -> bf16 is exact and one VALU op per pair; bf16 dot2 accumulates in fp32; the row scale
-//    multiplies the reduced sum once.
-//  - bf16: one wave per row, 5 x 16 B per lane, same structure.
+//  - FP8: the quantiser writes the codes tile-major (16-row tiles) and the GEMV runs each tile on
+//    the matrix cores, with x in LDS: the code registers a wave needs do not grow with M (x held
+//    in registers for every token did, and the M = 4 GEMV ran at half speed for want of waves).
+//    E4M3 -> bf16 is exact and one VALU op per pair; the products accumulate in fp32; the row
+//    scale multiplies the reduced sum once.
+//  - bf16: one wave per row, 5 x 16 B per lane, x in registers, the next row's loads issued
+//    before the current row is reduced.
 #include "qws_common.hpp"
 
 namespace {
@@ -34,20 +36,29 @@ __device__ __forceinline__ float group_max64(float v) {
 }
 
 // --------------------------------------------------------------------------- quantise
-// One wave per row: absmax, s = fl32(absmax / 448), codes = E4M3_RNE(fl32(w / s)).
+// Byte offset of codes (row r, columns 16c .. 16c+15) in the tile-major FP8 layout: tiles of 16
+// rows, tile t at byte 16 t cols; inside a tile, chunk c of tile row r at byte 16 (16c + r).
+__host__ __device__ __forceinline__ long long tile_byte(long long r, int c, int cols) {
+  return (r >> 4) * 16 * (long long)cols + (16ll * c + (r & 15)) * 16;
+}
+
+// One wave per row: absmax, s = fl32(absmax / 448), codes = E4M3_RNE(fl32(w / s)), written
+// tile-major; the rows that pad the last tile get zero codes.
 __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const uint16_t* __restrict__ w, long long rows,
                                                               int cols, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
   const int lane = threadIdx.x % kWave;
   const long long nwaves = (long long)gridDim.x * kWavesPerBlock;
+  const long long rows_pad = (rows + 15) & ~15ll;
   const int nch = cols >> 3;  // chunks of 8 bf16
-  for (long long row = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; row < rows; row += nwaves) {
+  for (long long row = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; row < rows_pad; row += nwaves) {
+    const bool real = row < rows;
     const uint16_t* src = w + row * cols;
     u32x4_t v[kCpl];
 #pragma unroll
     for (int t = 0; t < kCpl; ++t) {
       const int c = lane + t * kWave;
-      v[t] = c < nch ? ld16(src + c * 8) : u32x4_t{0, 0, 0, 0};
+      v[t] = real && c < nch ? ld16(src + c * 8) : u32x4_t{0, 0, 0, 0};
     }
     float amax = 0.0f;
 #pragma unroll
@@ -59,10 +70,9 @@ __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const uint16_t* __
       }
     amax = group_max64(amax);
     const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-    uint8_t* dst = codes + row * cols;
 #pragma unroll
     for (int t = 0; t < kCpl; ++t) {
-      const int c = lane + t * kWave;
+      const int c = lane + t * kWave;   // 8 codes: half c % 2 of 16-byte chunk c / 2
       if (c < nch) {
         u32x2_t out;
 #pragma unroll
@@ -73,193 +83,174 @@ __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const uint16_t* __
           const float a3 = __fdiv_rn(bf16_bits_to_f32(v[t][2 * h + 1] >> 16), s);
           out[h] = f32x2_to_e4m3x2<true>(a2, a3, f32x2_to_e4m3x2<false>(a0, a1, 0u));
         }
-        *reinterpret_cast<u32x2_t*>(dst + c * 8) = out;
+        *reinterpret_cast<u32x2_t*>(codes + tile_byte(row, c >> 1, cols) + 8 * (c & 1)) = out;
       }
     }
-    if (lane == 0) scales[row] = s;
+    if (real && lane == 0) scales[row] = s;
   }
 }
 
 // --------------------------------------------------------------------------- FP8 GEMV
-// This lane's share of x: chunks j + 32 t (16 bf16 each) of every token.
-template <int M>
-__device__ __forceinline__ void fp8_load_x(const uint16_t* __restrict__ x, int cols, int j, u32x4_t (&xr)[M][kCpl][2]) {
-  const int nch = cols >> 4;
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int t = 0; t < kCpl; ++t) {
-      const int c = j + 32 * t;
-      xr[m][t][0] = c < nch ? ld16(x + (size_t)m * cols + c * 16) : u32x4_t{0, 0, 0, 0};
-      xr[m][t][1] = c < nch ? ld16(x + (size_t)m * cols + c * 16 + 8) : u32x4_t{0, 0, 0, 0};
-    }
-}
-// This lane's partial dot products of one row (its 5 chunks of 16 codes) with the M tokens.
-template <int M>
-__device__ __forceinline__ void fp8_row_dots(const u32x4_t (&w)[kCpl], const u32x4_t (&xr)[M][kCpl][2], float (&acc)[M]) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-#pragma unroll
-  for (int t = 0; t < kCpl; ++t) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const bf16x2_t lo = fp8x2_to_bf16x2<false>(w[t][d]);
-      const bf16x2_t hi = fp8x2_to_bf16x2<true>(w[t][d]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        // codes 4d..4d+3 of the chunk pair with bf16 elements 4d..4d+3: x dwords 2d, 2d+1
-        acc[m] = dot2(lo, as_bf16x2(xr[m][t][d >> 1][(2 * d) & 3]), acc[m]);
-        acc[m] = dot2(hi, as_bf16x2(xr[m][t][d >> 1][(2 * d + 1) & 3]), acc[m]);
-      }
-    }
-  }
-}
+// The head's rows in tiles of 16 on the matrix cores: D (16 rows x 16 columns) += A (16 rows x 32
+// codes, E4M3 -> bf16, exact) x B (32 columns of x x 16 tokens; tokens M .. 15 are zero), fp32
+// accumulation. The codes are stored tile-major (see tile_byte) so that the 64 lanes of a wave
+// load 1 KB of consecutive bytes per instruction: chunk c of tile row i is what lane
+// (g = c % 4, i) needs for k-block c / 4. A row-major head read this way moves 16 rows x 64 B per
+// instruction and measured ~25% slower on MI355X.
+// A workgroup takes one tile at a time; its kHeadWaves waves split the tile's columns, the next
+// tile's codes load while the current one is multiplied, and the waves' partial sums meet in LDS.
+// Every token's column is computed the same way whatever M is, so a window of M tokens gives each
+// token the logits it would get alone, bit for bit.
+constexpr int kHeadWaves = 8;
+constexpr int kKbw = kMaxCols / 64 / kHeadWaves;  // k-blocks (64 columns) per wave
+constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x (bf16 elements)
+constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
 
-template <int M>
-__global__ __launch_bounds__(kBlock) void gemv_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scale,
-                                                          long long rows, int cols, const uint16_t* __restrict__ x,
-                                                          float* __restrict__ out) {
-  const int lane = threadIdx.x % kWave;
-  const int half = lane >> 5, j = lane & 31;
-  const int nch = cols >> 4;  // chunks of 16 codes
-  const long long npairs = (rows + 1) >> 1;
-  const long long nwaves = (long long)gridDim.x * kWavesPerBlock;
-  long long p = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (p >= npairs) return;
-
-  u32x4_t xr[M][kCpl][2];
-  fp8_load_x<M>(x, cols, j, xr);
-
-  auto load = [&](long long pp, u32x4_t (&wq)[kCpl]) {
-    const long long row = 2 * pp + half;
-#pragma unroll
-    for (int t = 0; t < kCpl; ++t) {
-      const int c = j + 32 * t;
-      wq[t] = (row < rows && c < nch) ? ld16_weights(q + row * cols + c * 16) : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  u32x4_t cur[kCpl], nxt[kCpl];
-  load(p, cur);
-  for (; p < npairs; p += nwaves) {
-    if (p + nwaves < npairs) load(p + nwaves, nxt);
-    float acc[M];
-    fp8_row_dots<M>(cur, xr, acc);
-    const long long row = 2 * p + half;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float v = group_sum<32>(acc[m]);
-      if (j == 0 && row < rows) out[(size_t)m * rows + row] = scale[row] * v;
-    }
-#pragma unroll
-    for (int t = 0; t < kCpl; ++t) cur[t] = nxt[t];
-  }
-}
-
-// --------------------------------------------------------------------------- greedy verification
-// The FP8 GEMV of a verification window (M positions) with the epilogue fused: each wave keeps,
-// per position, the largest (logit, lower row) key of its rows; a workgroup stores the maximum of
-// its waves; the last workgroup to arrive (two-level arrival) reduces them to each position's
-// target token and forms the accepted prefix of the M - 1 draft tokens.
-template <int M>
-__global__ __launch_bounds__(kBlock) void verify_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scale,
-                                                            long long rows, int cols, const uint16_t* __restrict__ x,
-                                                            float* __restrict__ out, const int* __restrict__ draft,
-                                                            int* __restrict__ target_out, int* __restrict__ emitted_out,
-                                                            int* __restrict__ n_out, unsigned long long* __restrict__ keys,
-                                                            unsigned* __restrict__ counters) {
-  __shared__ unsigned long long s_best[kWavesPerBlock][M];
+template <int M, bool kVerify>
+__global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ scale, long long rows, int cols,
+    const uint16_t* __restrict__ x, float* __restrict__ out, const int* __restrict__ draft,
+    int* __restrict__ target_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
+    unsigned long long* __restrict__ keys, unsigned* __restrict__ counters) {
+  __shared__ __align__(16) uint16_t xs[M * kXsStride];
+  __shared__ __align__(16) float red[2][kHeadWaves][M][16];
   __shared__ bool s_last;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int half = lane >> 5, j = lane & 31;
-  const int nch = cols >> 4;
-  const long long npairs = (rows + 1) >> 1;
-  const long long nwaves = (long long)gridDim.x * kWavesPerBlock;
-  long long p = (long long)blockIdx.x * kWavesPerBlock + wave;
-  unsigned long long best[M];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1), g = lane >> 4, i = lane & 15;
+  const long long ntiles = (rows + 15) >> 4;   // the grid never exceeds it
+  const int ncs = cols >> 4;                   // 16-byte chunks per row
+  const int kb0 = wave * kKbw;
+  // this wave's codes of a tile: k-blocks kb0 .. kb0 + kKbw - 1, 1 KB each (chunks past the row
+  // end are not loaded and add zeros)
+  auto load = [&](long long tl, u32x4_t (&w)[kKbw]) {
+    const uint8_t* p = q + tl * 16 * (long long)cols + lane * 16;
 #pragma unroll
-  for (int m = 0; m < M; ++m) best[m] = 0ull;   // below every key
-
-  if (p < npairs) {   // no early return: every workgroup arrives below
-    u32x4_t xr[M][kCpl][2];
-    fp8_load_x<M>(x, cols, j, xr);
-    auto load = [&](long long pp, u32x4_t (&wq)[kCpl]) {
-      const long long row = 2 * pp + half;
+    for (int t = 0; t < kKbw; ++t)
+      w[t] = 4 * (kb0 + t) + g < ncs ? ld16_weights(p + (kb0 + t) * 1024) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  long long tile = blockIdx.x;
+  u32x4_t cur[kKbw], nxt[kKbw];
+  load(tile, cur);
+  // epilogue thread: tile row er of token em
+  const int er = tid & 15, em = tid >> 4;
+  const bool ep = tid < 16 * M;
+  float sc = ep ? scale[min(tile * 16 + er, rows - 1)] : 0.0f;
+  unsigned long long best = 0ull;   // below every key
+  // x (bf16) into LDS, zero past the row end
+  for (int e = tid; e < M * (kXsStride / 8); e += kHeadWaves * kWave) {
+    const int m = e / (kXsStride / 8), c = (e % (kXsStride / 8)) * 8;
+    *reinterpret_cast<u32x4_t*>(xs + m * kXsStride + c) =
+        c < cols ? ld16(x + (size_t)m * cols + c) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  int buf = 0;
+  for (; tile < ntiles; tile += gridDim.x) {
+    const long long tn = tile + gridDim.x;
+    if (tn < ntiles) load(tn, nxt);
+    const float scn = ep && tn < ntiles ? scale[min(tn * 16 + er, rows - 1)] : 0.0f;
+    f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
 #pragma unroll
-      for (int t = 0; t < kCpl; ++t) {
-        const int c = j + 32 * t;
-        wq[t] = (row < rows && c < nch) ? ld16_weights(q + row * cols + c * 16) : u32x4_t{0, 0, 0, 0};
+    for (int t = 0; t < kKbw; ++t) {
+      // lane (g, i) holds codes 16c .. 16c+15 of tile row i (c = 4 kb + g): the first 8 go with
+      // x columns 16c .. 16c+7 in one product, the last 8 with 16c+8 .. 16c+15 in the other
+      u32x4_t xa = {0u, 0u, 0u, 0u}, xb = xa;
+      if (i < M) {
+        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs + i * kXsStride + 64 * (kb0 + t) + 16 * g);
+        xa = xp[0];
+        xb = xp[1];
       }
-    };
-    u32x4_t cur[kCpl], nxt[kCpl];
-    load(p, cur);
-    for (; p < npairs; p += nwaves) {
-      if (p + nwaves < npairs) load(p + nwaves, nxt);
-      float acc[M];
-      fp8_row_dots<M>(cur, xr, acc);
-      const long long row = 2 * p + half;
+      const u32x4_t w = cur[t];
+      const u32x4_t alo = {__builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[0])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[0])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[1])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[1]))};
+      const u32x4_t ahi = {__builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[2])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[2])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[3])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[3]))};
+      d0 = mfma_16x16x32(alo, xa, d0);
+      d1 = mfma_16x16x32(ahi, xb, d1);
+    }
+    // lane (g, i < M) holds token i's partial sums of tile rows 4g .. 4g+3
+    if (i < M) *reinterpret_cast<f32x4_t*>(&red[buf][wave][i][4 * g]) = d0 + d1;
+    __syncthreads();   // red[buf] is rewritten two tiles later, after the next barrier
+    if (ep) {
+      float v = red[buf][0][em][er];
+#pragma unroll
+      for (int w = 1; w < kHeadWaves; ++w) v += red[buf][w][em][er];
+      v *= sc;
+      const long long row = tile * 16 + er;
+      if (row < rows) {
+        if (!kVerify || out) out[(size_t)em * rows + row] = v;
+        if constexpr (kVerify) {
+          const unsigned long long k = rank_key(sel_key(v), (int)row);
+          best = k > best ? k : best;
+        }
+      }
+    }
+    sc = scn;
+    buf ^= 1;
+#pragma unroll
+    for (int t = 0; t < kKbw; ++t) cur[t] = nxt[t];
+  }
+  if constexpr (kVerify) {
+    // Greedy verification epilogue: the workgroup's largest (logit, lower row) key per token, then
+    // the last workgroup to arrive (two-level arrival) reduces all of them to each position's
+    // target token and forms the accepted prefix of the M - 1 draft tokens.
+    __shared__ unsigned long long s_best[kHeadWaves][M];
+    const unsigned G = gridDim.x;
+    if (ep) {   // tokens' epilogue threads are the 16-lane groups of wave 0
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const unsigned long long k = __shfl_xor(best, o, kWave);
+        best = k > best ? k : best;
+      }
+      if (er == 0) st_coherent(keys + (size_t)em * G + blockIdx.x, best);   // token-major
+    }
+    if (!arrive_last_grid(counters, &s_last)) return;
+    // every thread of the last workgroup loads its share of all keys at once (device-coherent
+    // loads, independent of each other), then the maxima meet in registers and LDS
+    constexpr int kPer = (kHeadGrid + kHeadWaves * kWave - 1) / (kHeadWaves * kWave);
+    unsigned long long kk[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) kk[m] = 0ull;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      // past the grid: the last key again (no branch, so the loads issue together)
+      const unsigned b = min(tid + j * kHeadWaves * kWave, G - 1);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float v = scale[row < rows ? row : rows - 1] * group_sum<32>(acc[m]);
-        if (out && j == 0 && row < rows) out[(size_t)m * rows + row] = v;
-        const unsigned long long k = row < rows ? rank_key(sel_key(v), (int)row) : 0ull;
-        best[m] = k > best[m] ? k : best[m];
+        const unsigned long long k = ld_coherent(keys + (size_t)m * G + b);
+        kk[m] = k > kk[m] ? k : kk[m];
       }
-#pragma unroll
-      for (int t = 0; t < kCpl; ++t) cur[t] = nxt[t];
     }
-  }
-  // the two half-waves' rows, then the waves of the workgroup
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const unsigned long long o = __shfl_xor(best[m], 32, kWave);
-    best[m] = o > best[m] ? o : best[m];
-    if (lane == 0) s_best[wave][m] = best[m];
-  }
-  __syncthreads();
-  if (threadIdx.x < M) {
-    unsigned long long k = 0ull;
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) k = s_best[w][threadIdx.x] > k ? s_best[w][threadIdx.x] : k;
-    st_coherent(keys + (size_t)blockIdx.x * M + threadIdx.x, k);
-  }
-  if (!arrive_last_grid(counters, &s_last)) return;
-
-  // last workgroup: every workgroup's keys (device-coherent loads), then the window
-#pragma unroll
-  for (int m = 0; m < M; ++m) best[m] = 0ull;
-  for (unsigned g = threadIdx.x; g < gridDim.x; g += kBlock)
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const unsigned long long k = ld_coherent(keys + (size_t)g * M + m);
-      best[m] = k > best[m] ? k : best[m];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long ko = __shfl_xor(kk[m], o, kWave);
+        kk[m] = ko > kk[m] ? ko : kk[m];
+      }
+      if (lane == 0) s_best[wave][m] = kk[m];
     }
+    __syncthreads();
+    if (tid == 0) {
+      int target[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
+      for (int m = 0; m < M; ++m) {
+        unsigned long long k = s_best[0][m];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long k = __shfl_xor(best[m], o, kWave);
-      best[m] = k > best[m] ? k : best[m];
+        for (int w = 1; w < kHeadWaves; ++w) k = s_best[w][m] > k ? s_best[w][m] : k;
+        target[m] = (int)(0xffffffffu - (uint32_t)k);
+        target_out[m] = target[m];
+      }
+      // draft i is accepted while it equals the target of position i; then the target of the
+      // first position not accepted
+      int a = 0;
+      while (a < M - 1 && draft[a] == target[a]) ++a;
+#pragma unroll
+      for (int m = 0; m < M; ++m) emitted_out[m] = m < a ? draft[m] : (m == a ? target[a] : -1);
+      *n_out = a + 1;
     }
-    if (lane == 0) s_best[wave][m] = best[m];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int target[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      unsigned long long k = 0ull;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) k = s_best[w][m] > k ? s_best[w][m] : k;
-      target[m] = (int)(0xffffffffu - (uint32_t)k);
-      target_out[m] = target[m];
-    }
-    // draft i is accepted while it equals the target of position i; then the target of the first
-    // position not accepted
-    int a = 0;
-    while (a < M - 1 && draft[a] == target[a]) ++a;
-#pragma unroll
-    for (int i = 0; i < M; ++i) emitted_out[i] = i < a ? draft[i] : (i == a ? target[a] : -1);
-    *n_out = a + 1;
   }
 }
 
@@ -312,11 +303,11 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_kernel(const uint16_t* __res
 }
 
 // 16 workgroups per CU; each wave loops over the rest (4096 .. 8192 workgroups measured best on
-// MI355X for the 157,184-row head, ~3% ahead of 2048 and ~10% ahead of one unit per wave)
-constexpr int kHeadGrid = 4096;
+// MI355X for the bf16 head, ~3% ahead of 2048 and ~10% ahead of one unit per wave)
+constexpr int kGemvGrid = 4096;
 int grid_for(long long units) {
   long long blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  return (int)(blocks < kHeadGrid ? blocks : kHeadGrid);
+  return (int)(blocks < kGemvGrid ? blocks : kGemvGrid);
 }
 
 int check_head(const qws_lmhead* h, unsigned fmt) {
@@ -350,6 +341,44 @@ extern "C" int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long
   return st;
 }
 
+namespace {
+// One launch of head_fp8_kernel: M tokens, greedy epilogue when `verify`.
+int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out, bool verify,
+                    const int* draft, int* target_out, int* emitted_out, int* n_out, unsigned long long* keys,
+                    unsigned* counters, hipStream_t s) {
+  const uint8_t* q = static_cast<const uint8_t*>(head->w);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  const int cols = (int)head->cols;
+  const long long ntiles = (head->rows + 15) / 16;
+  dim3 grid((unsigned)(ntiles < kHeadGrid ? ntiles : kHeadGrid)), block(kHeadWaves * kWave);
+#define QWS_HEAD(MM, VV)                                                                                        \
+  hipLaunchKernelGGL((head_fp8_kernel<MM, VV>), grid, block, 0, s, q, head->row_scale, head->rows, cols, x,     \
+                     logits_out, draft, target_out, emitted_out, n_out, keys, counters)
+  if (verify) {
+    switch (M) {
+      case 1: QWS_HEAD(1, true); break;
+      case 2: QWS_HEAD(2, true); break;
+      case 3: QWS_HEAD(3, true); break;
+      default: QWS_HEAD(4, true); break;
+    }
+  } else {
+    switch (M) {
+      case 1: QWS_HEAD(1, false); break;
+      case 2: QWS_HEAD(2, false); break;
+      case 3: QWS_HEAD(3, false); break;
+      default: QWS_HEAD(4, false); break;
+    }
+  }
+#undef QWS_HEAD
+  return qws_host::check_launch();
+}
+}  // namespace
+
+extern "C" size_t lmhead_fp8_codes_bytes(long long rows, long long cols) {
+  if (rows < 1 || rows > (1ll << 31) || cols < 32 || cols > kMaxCols || cols % 32) return 0;
+  return (size_t)((rows + 15) / 16 * 16) * (size_t)cols;
+}
+
 extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
                                qws_stream_t stream) {
   int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
@@ -357,18 +386,8 @@ extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M
   if (!x_bf16 || !logits_out) return QWS_ERR_ARG;
   if (M < 1 || M > 4) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
-  const uint8_t* q = static_cast<const uint8_t*>(head->w);
-  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  const int cols = (int)head->cols;
-  dim3 grid(grid_for((head->rows + 1) / 2)), block(kBlock);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (M) {
-    case 1: hipLaunchKernelGGL(gemv_fp8_kernel<1>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
-    case 2: hipLaunchKernelGGL(gemv_fp8_kernel<2>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
-    case 3: hipLaunchKernelGGL(gemv_fp8_kernel<3>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
-    default: hipLaunchKernelGGL(gemv_fp8_kernel<4>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out); break;
-  }
-  return qws_host::check_launch();
+  return launch_head_fp8(head, x_bf16, M, logits_out, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t lmhead_verify_workspace_bytes(int M) {
@@ -386,25 +405,11 @@ extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf
   if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
   if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
   if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
-  const uint8_t* q = static_cast<const uint8_t*>(head->w);
-  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  const int cols = (int)head->cols;
   unsigned long long* keys = static_cast<unsigned long long*>(workspace);
   unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
                                                    qws_host::align256((size_t)kHeadGrid * M * 8));
-  dim3 grid(grid_for((head->rows + 1) / 2)), block(kBlock);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-#define QWS_VERIFY(MM)                                                                                            \
-  hipLaunchKernelGGL(verify_fp8_kernel<MM>, grid, block, 0, s, q, head->row_scale, head->rows, cols, x, logits_out, \
-                     draft, target_out, emitted_out, n_out, keys, counters)
-  switch (M) {
-    case 1: QWS_VERIFY(1); break;
-    case 2: QWS_VERIFY(2); break;
-    case 3: QWS_VERIFY(3); break;
-    default: QWS_VERIFY(4); break;
-  }
-#undef QWS_VERIFY
-  return qws_host::check_launch();
+  return launch_head_fp8(head, x_bf16, M, logits_out, true, draft, target_out, emitted_out, n_out, keys, counters,
+                         static_cast<hipStream_t>(stream));
 }
 
 extern "C" int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,

@@ -115,3 +115,20 @@ class Layer:
         experts = {e: self.expert(e) for e in set(np.asarray(idx).reshape(-1).tolist()) | {self.shape.n_routed}
                    if 0 <= e <= self.shape.n_routed}
         return OM.moe_layer(self.x, idx, w, experts, self.shape.n_routed, self.shape.has_shared)
+
+
+def fp8_tile_major(codes: np.ndarray) -> np.ndarray:
+    """Row-major E4M3 codes [rows, cols] -> the library's tile-major bytes, from the header's
+    definition: rows padded with zero codes to a multiple of 16; tile t at byte 16 t cols; chunk c
+    (columns 16c .. 16c+15) of tile row i at byte 16 (16 c + i) of its tile."""
+    rows, cols = codes.shape
+    pad = (rows + 15) // 16 * 16
+    full = np.zeros((pad, cols), dtype=np.uint8)
+    full[:rows] = codes
+    out = np.empty(pad * cols, dtype=np.uint8)
+    for t in range(pad // 16):
+        for c in range(cols // 16):
+            for i in range(16):
+                o = t * 16 * cols + (16 * c + i) * 16
+                out[o:o + 16] = full[16 * t + i, 16 * c:16 * c + 16]
+    return out

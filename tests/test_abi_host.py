@@ -145,6 +145,16 @@ def test_lmhead_desc_and_quantize_validation(lib):
     assert lib.lmhead_quantize_fp8(A, 10, 64, MIS, A, C.byref(d), None) == _lib.QWS_ERR_ALIGN
 
 
+def test_fp8_codes_bytes(lib):
+    # rows padded to whole 16-row tiles; 0 for shapes the head refuses
+    assert lib.lmhead_fp8_codes_bytes(157184, 2560) == 157184 * 2560
+    assert lib.lmhead_fp8_codes_bytes(1, 32) == 16 * 32
+    assert lib.lmhead_fp8_codes_bytes(17, 96) == 32 * 96
+    assert lib.lmhead_fp8_codes_bytes(0, 2560) == 0
+    assert lib.lmhead_fp8_codes_bytes(10, 48) == 0
+    assert lib.lmhead_fp8_codes_bytes(10, 2592) == 0
+
+
 def test_verify_validation(lib):
     bf = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, 100, 64, A, None))
     fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 100, 64, A, A))
@@ -267,3 +277,4 @@ def test_pack_bytes(lib):
 ])
 def test_pack_validation(lib, kw, status):
     assert _pack(lib, **kw) == status
+

@@ -58,7 +58,7 @@ def _quant_case(w_bits: np.ndarray, what: str):
     say("fp8 quantize", what, w_bits.shape)
     head = qws.lmhead_quantize_fp8(bf16(w_bits))
     torch.cuda.synchronize()
-    codes = head.w.cpu().numpy()
+    codes = qws.fp8_codes_rowmajor(head).cpu().numpy()
     scales = head.row_scale.cpu().numpy()
     rc, rs = OL.fp8_rowquant(w_bits)
     assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)), f"{what}: scales differ"

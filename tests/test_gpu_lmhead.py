@@ -9,7 +9,7 @@ import quantized_weight_streaming_amd as qws
 import synth
 from oracle import lmhead as OL
 
-from .helpers import assert_close, bf16, check_argmax, say
+from .helpers import assert_close, bf16, check_argmax, fp8_tile_major, say
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,20 @@ def test_gemv_small(M, rows, cols):
     codes, scales = OL.fp8_rowquant(w)
     assert_close(l8, OL.lmhead_fp8(codes, scales, x), what="fp8 head")
     assert_close(lb, OL.lmhead_bf16(w, x), what="bf16 head")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (17, 96), (999, 544), (64, 2560)])
+def test_quantize_writes_the_tile_major_layout(rows, cols):
+    """The device codes, byte for byte, are the oracle's codes placed as the header defines (zero
+    codes in the rows that pad the last tile)."""
+    say("fp8 tile-major layout", rows, cols)
+    w = synth.bf16_normal(8, 0, synth.HEAD, rows + cols, (rows, cols), 0.02)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    codes, _ = OL.fp8_rowquant(w)
+    got = h8.w.cpu().numpy()
+    assert got.size == qws.lmhead_fp8_codes_bytes(rows, cols) == (rows + 15) // 16 * 16 * cols
+    assert np.array_equal(got, fp8_tile_major(codes))
+    assert np.array_equal(qws.fp8_codes_rowmajor(h8).cpu().numpy(), codes)
 
 
 def test_gemv_one_hot_columns():
@@ -73,7 +87,7 @@ def test_full_head_quantize_bit_exact(full_head):
     w, wt, h8, codes, scales = full_head
     say("full head codes/scales")
     assert np.array_equal(h8.row_scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
-    assert np.array_equal(h8.w.cpu().numpy(), codes)
+    assert np.array_equal(qws.fp8_codes_rowmajor(h8).cpu().numpy(), codes)
 
 
 def test_full_head_gemv(full_head):
