@@ -384,12 +384,18 @@ def main():
         ws_v = qws.verify_workspace(4, dev)
         draft = torch.tensor([1, 2, 3], dtype=torch.int32, device=dev)
         vout = qws.lmhead_verify_greedy_fp8(head8, x4, draft, ws_v, logits=lg4)
+        # the sampled run's settings (temperature 0.6, top_k 29, top_p 0.95) with seeded uniforms
+        u4 = torch.tensor(np.random.default_rng(1002).random(4), dtype=torch.float32, device=dev)
+        sout = qws.lmhead_verify_sample_fp8(head8, x4, draft, u4, ws_v, logits=lg4)
         for name, fn, nb in (("lmhead_fp8_m1", lambda: qws.lmhead_gemv_fp8(head8, xh, out=step.logits), head_bytes(1)),
                              ("lmhead_bf16_m1", lambda: qws.lmhead_gemv_bf16(head_bf16, xh, out=step.logits),
                               head_bytes(1, fp8=False)),
                              ("lmhead_fp8_m4", lambda: qws.lmhead_gemv_fp8(head8, x4, out=lg4), head_bytes(4)),
                              ("lmhead_verify_greedy_fp8_m4",
                               lambda: qws.lmhead_verify_greedy_fp8(head8, x4, draft, ws_v, logits=lg4, out=vout),
+                              head_bytes(4)),
+                             ("lmhead_verify_sample_fp8_m4",
+                              lambda: qws.lmhead_verify_sample_fp8(head8, x4, draft, u4, ws_v, out=sout),
                               head_bytes(4))):
             t = time_cold(fn, dev, flush=flush)
             t.update({"bytes": nb, "GBps": round(nb / (t["median_us"] * 1e-6) / 1e9, 1)})

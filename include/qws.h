@@ -289,6 +289,30 @@ int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, 
                              float* logits_out, int* target_out, int* emitted_out, int* n_out,
                              void* workspace, size_t workspace_bytes, qws_stream_t stream);
 
+/* Sampled verification of a speculative window after the FP8 head, for the pages' sampled run
+ * (temperature 0.6, top_p 0.95, top_k 29: Netics post, "GSM8K measured a 42.5% throughput gain").
+ * Per position m: the logits divided by the temperature, the top_k largest (ties to the lower row;
+ * NaN below every number), their softmax, the shortest prefix of that order whose probability
+ * reaches top_p, and token[m] = the first of that prefix whose running probability exceeds
+ * u[m] times the prefix's total (the last of it when none does). Draft i is accepted while it
+ * equals token[i]; emitted / n as for lmhead_verify_greedy_fp8. (The pages give no acceptance rule
+ * for sampled drafts and no draft probabilities, so a draft counts when it is the token the target
+ * samples with the caller's uniform; u[m] is drawn by the caller, in [0, 1).)
+ *   x_bf16 [M, cols], 1 <= M <= 4; draft [M - 1] int32 (NULL allowed when M = 1);
+ *   temperature > 0, finite; 1 <= top_k <= 32; 0 < top_p <= 1; u fp32 [M] (device);
+ *   logits_out fp32 [M, rows] (required: the same values as lmhead_gemv_fp8); token_out int32 [M];
+ *   topk_out NULL or int32 [M, top_k]: the rows of the top_k in order (-1 past min(top_k, rows));
+ *   emitted_out int32 [M], n_out int32 [1]; all device memory owned by the caller.
+ *   workspace: lmhead_verify_workspace_bytes(M) bytes, shared with lmhead_verify_greedy_fp8 (the
+ *   same conditions: zero-filled before first use, calls that share it must not overlap).
+ * Two launches: the head GEMV (logits and per-workgroup maxima), then one workgroup per position.
+ * Errors: as lmhead_verify_greedy_fp8, plus QWS_ERR_ARG for u or logits_out missing, temperature or
+ * top_p out of range, QWS_ERR_SHAPE for top_k outside 1 .. 32 or more than 262,144 rows. */
+int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                             float temperature, int top_k, float top_p, const float* u,
+                             float* logits_out, int* token_out, int* topk_out, int* emitted_out,
+                             int* n_out, void* workspace, size_t workspace_bytes, qws_stream_t stream);
+
 /* logits[m, r] = sum_k W[r, k] * x[m, k]   (head must be BF16-tagged; an FP8 head is refused
  * with QWS_ERR_FORMAT instead of being read as bf16). Same shapes as lmhead_gemv_fp8.       */
 int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,

@@ -28,7 +28,7 @@ __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_fp8_codes_bytes", "fp8_codes_rowmajor", "lmhead_gemv_fp8", "lmhead_gemv_bf16",
-           "lmhead_verify_greedy_fp8",
+           "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8",
            "verify_workspace", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
@@ -368,6 +368,37 @@ def lmhead_verify_greedy_fp8(head: LMHead, x: torch.Tensor, draft: torch.Tensor 
                                         None if logits is None else _p(logits), _p(out["target"]), _p(out["emitted"]),
                                         _p(out["n"]), _p(workspace), workspace.numel(), _stream(dev))
     check("lmhead_verify_greedy_fp8", st)
+    return out
+
+
+def lmhead_verify_sample_fp8(head: LMHead, x: torch.Tensor, draft: torch.Tensor | None, u: torch.Tensor,
+                             workspace: torch.Tensor, temperature: float = 0.6, top_k: int = 29, top_p: float = 0.95,
+                             logits: torch.Tensor | None = None, topk: bool = False, out: dict | None = None) -> dict:
+    """Sampled verification of an M-position window with one uniform u[m] in [0, 1) per position:
+    {"token": int32 [M], "emitted": int32 [M], "n": int32 [1], "logits": fp32 [M, rows] and, with
+    topk=True, "topk": int32 [M, top_k] (rows in order)} (device tensors; reused from `out`)."""
+    _need(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = {k: torch.empty(n, dtype=torch.int32, device=dev) for k, n in (("token", M), ("emitted", M), ("n", 1))}
+        if topk:
+            out["topk"] = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+    if logits is None:
+        logits = out.get("logits")
+    if logits is None:
+        logits = torch.empty((M, head.rows), dtype=torch.float32, device=dev)
+    out["logits"] = logits
+    if draft is not None and (draft.dtype != torch.int32 or draft.numel() != M - 1 or draft.device != dev):
+        raise ValueError("draft: int32 [M - 1] on the device of x")
+    if u.dtype != torch.float32 or u.numel() != M or u.device != dev:
+        raise ValueError("u: float32 [M] on the device of x")
+    tk = out.get("topk")
+    st = lib().lmhead_verify_sample_fp8(C.byref(head.desc), _p(x), M, None if draft is None else _p(draft),
+                                        float(temperature), int(top_k), float(top_p), _p(u), _p(logits),
+                                        _p(out["token"]), None if tk is None else _p(tk), _p(out["emitted"]),
+                                        _p(out["n"]), _p(workspace), workspace.numel(), _stream(dev))
+    check("lmhead_verify_sample_fp8", st)
     return out
 
 

@@ -66,6 +66,8 @@ SIGNATURES = {
     "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "lmhead_verify_workspace_bytes": (_SZ, [_I]),
     "lmhead_verify_greedy_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_verify_sample_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, C.c_float, _I, C.c_float, _P, _P, _P, _P,
+                                      _P, _P, _P, _SZ, _P]),
     "lmhead_gemv_bf16": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),
     "qws_debug_dequant_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _P]),

@@ -106,7 +106,11 @@ constexpr int kKbw = kMaxCols / 64 / kHeadWaves;  // k-blocks (64 columns) per w
 constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x (bf16 elements)
 constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
 
-template <int M, bool kVerify>
+// kMode: kGemv (logits only), kGreedy (logits optional, greedy verification epilogue), kKeys
+// (logits and each workgroup's largest key per token, for the sampling kernel).
+enum HeadMode { kGemv = 0, kGreedy = 1, kKeys = 2 };
+
+template <int M, int kMode>
 __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ scale, long long rows, int cols,
     const uint16_t* __restrict__ x, float* __restrict__ out, const int* __restrict__ draft,
@@ -180,8 +184,8 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
       v *= sc;
       const long long row = tile * 16 + er;
       if (row < rows) {
-        if (!kVerify || out) out[(size_t)em * rows + row] = v;
-        if constexpr (kVerify) {
+        if (kMode != kGreedy || out) out[(size_t)em * rows + row] = v;
+        if constexpr (kMode != kGemv) {
           const unsigned long long k = rank_key(sel_key(v), (int)row);
           best = k > best ? k : best;
         }
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
 #pragma unroll
     for (int t = 0; t < kKbw; ++t) cur[t] = nxt[t];
   }
-  if constexpr (kVerify) {
+  if constexpr (kMode != kGemv) {
     // Greedy verification epilogue: the workgroup's largest (logit, lower row) key per token, then
     // the last workgroup to arrive (two-level arrival) reduces all of them to each position's
     // target token and forms the accepted prefix of the M - 1 draft tokens.
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
       }
       if (er == 0) st_coherent(keys + (size_t)em * G + blockIdx.x, best);   // token-major
     }
-    if (!arrive_last_grid(counters, &s_last)) return;
+    if (kMode == kKeys || !arrive_last_grid(counters, &s_last)) return;
     // every thread of the last workgroup loads its share of all keys at once (device-coherent
     // loads, independent of each other), then the maxima meet in registers and LDS
     constexpr int kPer = (kHeadGrid + kHeadWaves * kWave - 1) / (kHeadWaves * kWave);
@@ -251,6 +255,195 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
       for (int m = 0; m < M; ++m) emitted_out[m] = m < a ? draft[m] : (m == a ? target[a] : -1);
       *n_out = a + 1;
     }
+  }
+}
+
+// --------------------------------------------------------------------------- sampled verification
+// The window's positions sampled from the FP8 head's logits (temperature, top_k, top_p, a uniform u
+// per position from the caller), then the accepted prefix of the drafts. Runs after
+// head_fp8_kernel<M, kKeys>, which leaves the logits and, per head workgroup and token, the largest
+// 64-bit key (ordered logit, ~row) of the workgroup's rows. One workgroup per position:
+//  1. t = the k-th largest of those G keys. Every key of the token's top k is at least t (the k
+//     largest workgroup maxima are k keys >= t), and so lies in one of the exactly k workgroups
+//     whose maximum reaches t (every workgroup when G <= k).
+//  2. Candidates: the keys >= t among those workgroups' rows (at most k x tiles x 16), read back
+//     from the logits; the top k of them, in order, by a radix select and a wave sort.
+//  3. Softmax at the temperature, the shortest prefix reaching top_p, inversion at u.
+constexpr int kSampleThreads = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxTilesPerGroup = 8;   // rows <= kHeadGrid x 16 x 8 = 262,144
+constexpr int kCandMax = kMaxTopK * kMaxTilesPerGroup * 16;
+
+// The k-th largest (1 <= k <= n) of the n 64-bit keys a[0 .. n) in LDS, by radix select on 8-bit
+// digits from the top (a histogram per digit; the digit where the count from above reaches k).
+// Every thread of the workgroup calls it.
+__device__ unsigned long long block_kth_largest(const unsigned long long* a, int n, int k, unsigned (*hist)[256],
+                                                unsigned long long* s_sel, int* s_need) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  unsigned long long prefix = 0ull;
+  int need = k;
+  for (int i = tid; i < 256; i += kSampleThreads) hist[0][i] = 0u;
+  __syncthreads();
+  for (int shift = 56, h = 0; shift >= 0; shift -= 8, h ^= 1) {
+    // count this digit into hist[h] and clear the other buffer for the next digit (its last
+    // reader, the scan of the previous digit, finished before the barrier that ended it)
+    for (int i = tid; i < 256; i += kSampleThreads) hist[h ^ 1][i] = 0u;
+    const unsigned long long hi = shift == 56 ? 0ull : ~0ull << (shift + 8);
+    for (int i = tid; i < n; i += kSampleThreads) {
+      const unsigned long long v = a[i];
+      if ((v & hi) == prefix) atomicAdd(&hist[h][(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l counts digits 255 - 4l .. 252 - 4l (from the top)
+      unsigned c[4], sum = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[h][255 - 4 * lane - j];
+        sum += c[j];
+      }
+      unsigned incl = sum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      const unsigned long long reach = __ballot(incl >= (unsigned)need);   // nonzero: the total is >= need
+      if (lane == __builtin_ctzll(reach)) {
+        unsigned above = incl - sum;
+        int d = 252 - 4 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (above + c[j] >= (unsigned)need) {
+            d = 255 - 4 * lane - j;
+            break;
+          }
+          above += c[j];
+        }
+        *s_sel = prefix | ((unsigned long long)d << shift);
+        *s_need = need - (int)above;
+      }
+    }
+    __syncthreads();
+    prefix = *s_sel;
+    need = *s_need;
+  }
+  return prefix;
+}
+
+template <int M>
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(
+    const float* __restrict__ logits, long long rows, const unsigned long long* __restrict__ keys, int G,
+    float temperature, int top_k, float top_p, const float* __restrict__ u, const int* __restrict__ draft,
+    int* __restrict__ token_out, int* __restrict__ topk_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
+    int* __restrict__ tokens, unsigned* __restrict__ counter) {
+  __shared__ unsigned long long s_a[kHeadGrid];
+  __shared__ unsigned long long s_c[kCandMax];
+  __shared__ unsigned long long s_top[kMaxTopK];
+  __shared__ unsigned s_hist[2][256];
+  __shared__ unsigned long long s_sel;
+  __shared__ int s_need, s_nwg, s_nc, s_ntop;
+  __shared__ int s_wg[kMaxTopK];
+  __shared__ bool s_last;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const long long ntiles = (rows + 15) >> 4;
+  const int tpg = (int)((ntiles + G - 1) / G);   // tiles per head workgroup (host: <= 8)
+  const int k = (int)(top_k < rows ? top_k : rows);
+  const float* lg = logits + (size_t)m * rows;
+  {
+    // all loads first (addresses past G repeat the last key), then the LDS stores
+    constexpr int kPer = kHeadGrid / kSampleThreads;
+    unsigned long long kv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) kv[j] = keys[(size_t)m * G + min(tid + j * kSampleThreads, G - 1)];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (tid + j * kSampleThreads < G) s_a[tid + j * kSampleThreads] = kv[j];
+  }
+  if (tid == 0) {
+    s_nwg = 0;
+    s_nc = 0;
+    s_ntop = 0;
+  }
+  __syncthreads();
+  // 1. the workgroups that can hold the top k (keys are distinct and nonzero)
+  const unsigned long long t = G > k ? block_kth_largest(s_a, G, k, s_hist, &s_sel, &s_need) : 0ull;
+  for (int b = tid; b < G; b += kSampleThreads)
+    if (s_a[b] >= t) s_wg[atomicAdd(&s_nwg, 1)] = b;
+  __syncthreads();
+  // 2. their rows' keys that reach t, then the k largest of those
+  const int nwg = s_nwg, per = tpg * 16;
+  {
+    constexpr int kPer = kCandMax / kSampleThreads;
+    long long row[kPer];
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kSampleThreads;
+      const long long tile = i < nwg * per ? s_wg[i / per] + (long long)((i % per) >> 4) * G : ntiles;
+      row[j] = tile < ntiles && tile * 16 + (i & 15) < rows ? tile * 16 + (i & 15) : -1;
+      v[j] = lg[row[j] < 0 ? 0 : row[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const unsigned long long key = rank_key(sel_key(v[j]), (int)row[j]);
+      if (row[j] >= 0 && key >= t) s_c[atomicAdd(&s_nc, 1)] = key;
+    }
+  }
+  __syncthreads();
+  const int nc = s_nc;   // >= k
+  const unsigned long long tk = block_kth_largest(s_c, nc, k, s_hist, &s_sel, &s_need);
+  for (int i = tid; i < nc; i += kSampleThreads)
+    if (s_c[i] >= tk) s_top[atomicAdd(&s_ntop, 1)] = s_c[i];
+  __syncthreads();
+  // 3. wave 0: the k keys in order (bitonic sort across the lanes, descending), then the sample
+  if (wave == 0) {
+    unsigned long long key = lane < k ? s_top[lane] : 0ull;
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1)
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const unsigned long long o = __shfl_xor(key, stride, kWave);
+        const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+        key = keep_max ? (o > key ? o : key) : (o < key ? o : key);
+      }
+    const int row = (int)(0xffffffffu - (uint32_t)key);
+    const float v = key_to_float((uint32_t)(key >> 32));
+    const float v0 = __shfl(v, 0, kWave);
+    // probabilities relative to the largest: exp((v - v0) / temperature), their running sums
+    const float p = lane < k ? expf(__fdiv_rn(v - v0, temperature)) : 0.0f;
+    float c = p;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float w = __shfl_up(c, o, kWave);
+      if (lane >= o) c += w;
+    }
+    const float total = __shfl(c, k - 1, kWave);
+    // the shortest prefix whose share reaches top_p, then the first token of it whose running sum
+    // exceeds u times the prefix's sum
+    const unsigned long long reach = __ballot(lane < k && c >= top_p * total);
+    const int keep = reach ? __builtin_ctzll(reach) + 1 : k;
+    const float sk = __shfl(c, keep - 1, kWave);
+    const unsigned long long over = __ballot(lane < keep && c > u[m] * sk);
+    const int pick = over ? __builtin_ctzll(over) : keep - 1;
+    const int token = __shfl(row, pick, kWave);
+    if (topk_out && lane < top_k) topk_out[(size_t)m * top_k + lane] = lane < k ? row : -1;
+    if (lane == 0) {
+      token_out[m] = token;
+      st_coherent(tokens + m, token);
+    }
+  }
+  // 4. the last position's workgroup forms the accepted prefix
+  if (!arrive_last(counter, M, &s_last)) return;
+  if (tid == 0) {
+    int target[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) target[i] = ld_coherent(tokens + i);
+    int a = 0;
+    while (a < M - 1 && draft[a] == target[a]) ++a;
+#pragma unroll
+    for (int i = 0; i < M; ++i) emitted_out[i] = i < a ? draft[i] : (i == a ? target[a] : -1);
+    *n_out = a + 1;
   }
 }
 
@@ -343,7 +536,7 @@ extern "C" int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long
 
 namespace {
 // One launch of head_fp8_kernel: M tokens, greedy epilogue when `verify`.
-int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out, bool verify,
+int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out, int mode,
                     const int* draft, int* target_out, int* emitted_out, int* n_out, unsigned long long* keys,
                     unsigned* counters, hipStream_t s) {
   const uint8_t* q = static_cast<const uint8_t*>(head->w);
@@ -354,21 +547,21 @@ int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* lo
 #define QWS_HEAD(MM, VV)                                                                                        \
   hipLaunchKernelGGL((head_fp8_kernel<MM, VV>), grid, block, 0, s, q, head->row_scale, head->rows, cols, x,     \
                      logits_out, draft, target_out, emitted_out, n_out, keys, counters)
-  if (verify) {
-    switch (M) {
-      case 1: QWS_HEAD(1, true); break;
-      case 2: QWS_HEAD(2, true); break;
-      case 3: QWS_HEAD(3, true); break;
-      default: QWS_HEAD(4, true); break;
-    }
-  } else {
-    switch (M) {
-      case 1: QWS_HEAD(1, false); break;
-      case 2: QWS_HEAD(2, false); break;
-      case 3: QWS_HEAD(3, false); break;
-      default: QWS_HEAD(4, false); break;
-    }
+#define QWS_HEAD_M(VV)                  \
+  switch (M) {                          \
+    case 1: QWS_HEAD(1, VV); break;     \
+    case 2: QWS_HEAD(2, VV); break;     \
+    case 3: QWS_HEAD(3, VV); break;     \
+    default: QWS_HEAD(4, VV); break;    \
   }
+  if (mode == kGreedy) {
+    QWS_HEAD_M(kGreedy)
+  } else if (mode == kKeys) {
+    QWS_HEAD_M(kKeys)
+  } else {
+    QWS_HEAD_M(kGemv)
+  }
+#undef QWS_HEAD_M
 #undef QWS_HEAD
   return qws_host::check_launch();
 }
@@ -386,13 +579,19 @@ extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M
   if (!x_bf16 || !logits_out) return QWS_ERR_ARG;
   if (M < 1 || M > 4) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
-  return launch_head_fp8(head, x_bf16, M, logits_out, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+  return launch_head_fp8(head, x_bf16, M, logits_out, kGemv, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                          static_cast<hipStream_t>(stream));
 }
 
+// Verification workspace: per-workgroup keys [M][kHeadGrid] u64, the greedy kernel's arrival
+// counters (kArriveGroups + 1 lines of 128 B), then 256 B for the sampling kernel (its arrival
+// counter, then the M sampled tokens on the next 128-byte line).
+size_t verify_keys_bytes(int M) { return qws_host::align256((size_t)kHeadGrid * M * 8); }
+constexpr size_t kGreedyCounterBytes = (size_t)(kArriveGroups + 1) * kCounterStride * 4;
+
 extern "C" size_t lmhead_verify_workspace_bytes(int M) {
   if (M < 1 || M > 4) return 0;
-  return qws_host::align256((size_t)kHeadGrid * M * 8) + (size_t)(kArriveGroups + 1) * kCounterStride * 4;
+  return verify_keys_bytes(M) + kGreedyCounterBytes + 256;
 }
 
 extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
@@ -406,10 +605,44 @@ extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf
   if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
   if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
   unsigned long long* keys = static_cast<unsigned long long*>(workspace);
-  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                                   qws_host::align256((size_t)kHeadGrid * M * 8));
-  return launch_head_fp8(head, x_bf16, M, logits_out, true, draft, target_out, emitted_out, n_out, keys, counters,
+  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + verify_keys_bytes(M));
+  return launch_head_fp8(head, x_bf16, M, logits_out, kGreedy, draft, target_out, emitted_out, n_out, keys, counters,
                          static_cast<hipStream_t>(stream));
+}
+
+extern "C" int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                                        float temperature, int top_k, float top_p, const float* u,
+                                        float* logits_out, int* token_out, int* topk_out, int* emitted_out,
+                                        int* n_out, void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  if (st != QWS_OK) return st;
+  if (!x_bf16 || !u || !logits_out || !token_out || !emitted_out || !n_out || (M > 1 && !draft)) return QWS_ERR_ARG;
+  if (!(temperature > 0.0f) || !(temperature < 3.0e38f) || !(top_p > 0.0f) || !(top_p <= 1.0f)) return QWS_ERR_ARG;
+  if (M < 1 || M > 4 || top_k < 1 || top_k > kMaxTopK) return QWS_ERR_SHAPE;
+  const long long ntiles = (head->rows + 15) / 16;
+  const int G = (int)(ntiles < kHeadGrid ? ntiles : kHeadGrid);
+  if ((ntiles + G - 1) / G > kMaxTilesPerGroup) return QWS_ERR_SHAPE;
+  if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
+  if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
+  if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
+  unsigned long long* keys = static_cast<unsigned long long*>(workspace);
+  char* tail = static_cast<char*>(workspace) + verify_keys_bytes(M) + kGreedyCounterBytes;
+  unsigned* counter = reinterpret_cast<unsigned*>(tail);
+  int* tokens = reinterpret_cast<int*>(tail + 128);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_head_fp8(head, x_bf16, M, logits_out, kKeys, nullptr, nullptr, nullptr, nullptr, keys, nullptr, s);
+  if (st != QWS_OK) return st;
+#define QWS_SAMPLE(MM)                                                                                             \
+  hipLaunchKernelGGL(sample_kernel<MM>, dim3(MM), dim3(kSampleThreads), 0, s, logits_out, head->rows, keys, G,      \
+                     temperature, top_k, top_p, u, draft, token_out, topk_out, emitted_out, n_out, tokens, counter)
+  switch (M) {
+    case 1: QWS_SAMPLE(1); break;
+    case 2: QWS_SAMPLE(2); break;
+    case 3: QWS_SAMPLE(3); break;
+    default: QWS_SAMPLE(4); break;
+  }
+#undef QWS_SAMPLE
+  return qws_host::check_launch();
 }
 
 extern "C" int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,

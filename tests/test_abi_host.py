@@ -179,6 +179,31 @@ def test_verify_validation(lib):
     assert call(ws=None) == _lib.QWS_ERR_WORKSPACE
 
 
+def test_sample_validation(lib):
+    bf = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, 100, 64, A, None))
+    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 100, 64, A, A))
+    big = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 262145, 64, A, A))
+    wsb = lib.lmhead_verify_workspace_bytes(4)
+    ok = dict(head=fp8, x=A, M=4, draft=A, T=0.6, k=29, p=0.95, u=A, lg=A, tok=A, tk=None, e=A, n=A, ws=A, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.lmhead_verify_sample_fp8(a["head"], a["x"], a["M"], a["draft"], a["T"], a["k"], a["p"], a["u"],
+                                            a["lg"], a["tok"], a["tk"], a["e"], a["n"], a["ws"], a["wsb"], None)
+    assert call(head=bf) == _lib.QWS_ERR_FORMAT
+    for name in ("x", "draft", "u", "lg", "tok", "e", "n"):
+        assert call(**{name: None}) == _lib.QWS_ERR_ARG, name
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(T=T) == _lib.QWS_ERR_ARG, T
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        assert call(p=p) == _lib.QWS_ERR_ARG, p
+    assert call(k=0) == _lib.QWS_ERR_SHAPE and call(k=33) == _lib.QWS_ERR_SHAPE
+    assert call(M=0) == _lib.QWS_ERR_SHAPE and call(M=5) == _lib.QWS_ERR_SHAPE
+    assert call(head=big) == _lib.QWS_ERR_SHAPE   # more than 2,048 x 16 x 8 rows
+    assert call(x=MIS) == _lib.QWS_ERR_ALIGN and call(ws=MIS) == _lib.QWS_ERR_ALIGN
+    assert call(wsb=wsb - 1) == _lib.QWS_ERR_WORKSPACE and call(ws=None) == _lib.QWS_ERR_WORKSPACE
+
+
 def test_diagnostics_validation(lib):
     assert lib.qws_debug_dequant_mxfp4(A, A, 4, 64, 2, A, None) == _lib.QWS_ERR_ARG
     assert lib.qws_debug_dequant_mxfp4(A, A, 4, 48, 0, A, None) == _lib.QWS_ERR_SHAPE
