@@ -165,8 +165,24 @@ def probe_ceiling(qws, dev, probe="probe_read"):
 
 
 # ------------------------------------------------------------------------------------ decode step
+def speculation_model(t1_ms, t4_ms, draft_step_ms, drafts=3, accepts=(1.0, 2.68, 3.90, 4.0)):
+    """Decode throughput of speculative decoding priced from measured step times (the pages report
+    accept length and verification-cost ratio so that readers can price the trade: runbyai.xyz
+    signal/190 on the four-position window, Netics post on the 3.90 / 2.68 accept lengths). A round
+    drafts `drafts` tokens (each a draft step at M = 1) and verifies drafts + 1 positions in one
+    step of cost t4; it emits `accept` tokens on average. Plain decoding emits one token per t1."""
+    round_ms = t4_ms + drafts * draft_step_ms
+    return {"t_decode_ms": round(t1_ms, 4), "t_verify_ms": round(t4_ms, 4),
+            "verify_cost_ratio": round(t4_ms / t1_ms, 3), "draft_step_ms": round(draft_step_ms, 4),
+            "round_ms": round(round_ms, 4), "break_even_accept": round(round_ms / t1_ms, 3),
+            "plain_tokens_per_s": round(1e3 / t1_ms, 1),
+            "by_accept": {f"{a:.2f}": {"tokens_per_s": round(a * 1e3 / round_ms, 1),
+                                       "speedup": round(a * t1_ms / round_ms, 3)} for a in accepts}}
+
+
 class DecodeStep:
-    """42 independent MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head."""
+    """42 independent MoE layers in one persistent launch (moe_layers_mxfp4), then the FP8 head
+    (at M > 1 with the greedy verification epilogue: a verification round's target pass)."""
 
     def __init__(self, qws, M, dev, n_layers, head, packed=None):
         import torch
@@ -182,12 +198,20 @@ class DecodeStep:
         self.xh = _bf16(synth.token_vectors(0, 1000, M), dev)
         self.head = head
         self.logits = torch.empty((M, head.rows), dtype=torch.float32, device=dev)
+        if M > 1:
+            self.vws = qws.verify_workspace(M, dev)
+            self.draft = torch.arange(1, M, dtype=torch.int32, device=dev)
+            self.vout = qws.lmhead_verify_greedy_fp8(head, self.xh, self.draft, self.vws, logits=self.logits)
 
     def layers_call(self):
         self.seq.run(self.ws)
 
     def head_call(self):
-        self.qws.lmhead_gemv_fp8(self.head, self.xh, out=self.logits)
+        if self.M == 1:
+            self.qws.lmhead_gemv_fp8(self.head, self.xh, out=self.logits)
+        else:
+            self.qws.lmhead_verify_greedy_fp8(self.head, self.xh, self.draft, self.vws, logits=self.logits,
+                                              out=self.vout)
 
     def bytes(self):
         return sum(layer_bytes(L.union(), self.M) for L in self.layers) + head_bytes(self.M)
@@ -414,6 +438,11 @@ def main():
                                        "mean_union": round(float(np.mean([L.union() for L in step4.layers])), 2)}
         log("decode_step_m4", breakdown["decode_step_m4"])
         del step4
+        # speculation priced from these steps: a draft step taken as one MoE layer plus the shared
+        # head at M = 1 (the draft is the model's one extra NEXTN layer; attention is not modelled)
+        draft_ms = (r["moe_us_mean"] / args.layers + r["head_us_mean"]) / 1e3
+        breakdown["speculation"] = speculation_model(r["wall_ms"], r4["wall_ms"], draft_ms)
+        log("speculation", breakdown["speculation"])
         # FP8 vs bf16 head agreement over seeded x vectors (a measurement, not parity)
         if args.agreement:
             topk1, topk10, in10 = 0, 0.0, 0
