@@ -426,6 +426,32 @@ def main():
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
             breakdown[name] = t
             log(name, t)
+        # run-time specialisation (hipRTC): first call into an empty cache (compile + load), cold
+        # kernel times against the template build, then a first call served by the disk cache
+        import shutil
+        import tempfile
+        rtc_dir = tempfile.mkdtemp(prefix="qws_rtc_")
+        qws.rtc_reset()
+        rtc = {}
+        for m_, xx, lg in ((1, xh, step.logits), (4, x4, lg4)):
+            t0 = time.perf_counter()
+            qws.lmhead_gemv_fp8_rtc(head8, xx, out=lg, cache_dir=rtc_dir)
+            torch.cuda.synchronize(dev)
+            first = (time.perf_counter() - t0) * 1e3
+            tr = time_cold(lambda: qws.lmhead_gemv_fp8_rtc(head8, xx, out=lg, cache_dir=rtc_dir), dev, flush=flush)
+            tt = time_cold(lambda: qws.lmhead_gemv_fp8(head8, xx, out=lg), dev, flush=flush)
+            rtc[f"m{m_}"] = {"first_call_ms": round(first, 1), "rtc_median_us": round(tr["median_us"], 2),
+                             "template_median_us": round(tt["median_us"], 2)}
+        st = qws.rtc_stats()
+        rtc["compiles"], rtc["compile_ms_total"] = st["compiles"], round(st["compile_ms"], 1)
+        qws.rtc_reset()
+        t0 = time.perf_counter()
+        qws.lmhead_gemv_fp8_rtc(head8, x4, out=lg4, cache_dir=rtc_dir)
+        torch.cuda.synchronize(dev)
+        rtc["disk_cache_first_call_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        shutil.rmtree(rtc_dir, ignore_errors=True)
+        breakdown["lmhead_fp8_rtc"] = rtc
+        log("lmhead_fp8_rtc", rtc)
         # decode step at M = 4 (natural routing), sharing the M = 1 step's expert banks
         step4 = DecodeStep(qws, 4, dev, args.layers, head8, packed=[L.packed for L in step.layers])
         step4.layers_call()

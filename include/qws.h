@@ -38,7 +38,8 @@ enum qws_status {
   QWS_ERR_FORMAT = -4,    /* a descriptor whose format tag does not match the entry point */
   QWS_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the matching *_workspace_bytes() */
   QWS_ERR_DEVICE = -6,    /* the HIP runtime refused a launch; qws_strerror appends its message */
-  QWS_ERR_SELFCHECK = -7  /* the device decoded a format differently from the host tables */
+  QWS_ERR_SELFCHECK = -7, /* the device decoded a format differently from the host tables */
+  QWS_ERR_COMPILE = -8    /* run-time compilation failed; qws_strerror appends the compiler log */
 };
 
 /* Format tags carried by descriptors. A descriptor tagged with one format is refused by an entry
@@ -312,6 +313,40 @@ int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, 
                              float temperature, int top_k, float top_p, const float* u,
                              float* logits_out, int* token_out, int* topk_out, int* emitted_out,
                              int* n_out, void* workspace, size_t workspace_bytes, qws_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Run-time specialisation (hipRTC). The pages' first optimisation compiles kernels at run time
+ * for the real shapes, data types and architecture and caches them on disk, so that a kernel
+ * builds in seconds (runbyai.xyz/posts/593 paragraph 4; Netics post, "Humming MXFP4 kernels
+ * compile at run time for the model's real shapes"). Here: the FP8 head GEMV, compiled from the
+ * same source as lmhead_gemv_fp8 with rows and cols as constants, for the current device's
+ * architecture (gcnArchName) and M. Key: (M, rows, cols, architecture, source hash); the disk
+ * cache is `cache_dir` (NULL: $QWS_RTC_CACHE, else $HOME/.cache/qws_rtc), one file per key,
+ * written whole (rename) so that concurrent processes never read half a file.
+ * -------------------------------------------------------------------------------------------*/
+typedef struct {
+  unsigned long long compiles;    /* hipRTC compilations */
+  unsigned long long disk_hits;   /* code objects read from the disk cache */
+  unsigned long long memory_hits; /* launches that found their module already loaded */
+  double compile_ms;              /* wall time spent compiling (and writing the cache) */
+  double load_ms;                 /* wall time spent reading cache files and loading modules */
+} qws_rtc_stats;
+
+/* Same result as lmhead_gemv_fp8, bit for bit (same source, same arithmetic); the first call for a
+ * key compiles or reads the cache, later calls launch the loaded module. Errors: as
+ * lmhead_gemv_fp8, plus QWS_ERR_COMPILE (compiler log in qws_strerror) and QWS_ERR_DEVICE for a
+ * module that does not load. Thread-safe (one lock around the cache). */
+int lmhead_gemv_fp8_rtc(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
+                        const char* cache_dir, qws_stream_t stream);
+/* Compile (or find in the disk cache) the GEMV for an architecture name such as "gfx950" or
+ * "gfx950:sramecc+:xnack-", without a device: for building a cache ahead of time. QWS_ERR_ARG for an
+ * arch name not of that form, QWS_ERR_SHAPE as lmhead_gemv_fp8, QWS_ERR_COMPILE (e.g. an
+ * architecture without the gfx950 conversions the kernel uses). */
+int qws_rtc_compile_head_fp8(int M, long long rows, long long cols, const char* arch, const char* cache_dir);
+/* Counters since load or the last qws_rtc_reset (stats_out: host memory). */
+int qws_rtc_stats_get(qws_rtc_stats* stats_out);
+/* Unload the modules and zero the counters; the disk cache is kept. */
+int qws_rtc_reset(void);
 
 /* logits[m, r] = sum_k W[r, k] * x[m, k]   (head must be BF16-tagged; an FP8 head is refused
  * with QWS_ERR_FORMAT instead of being read as bf16). Same shapes as lmhead_gemv_fp8.       */

@@ -14,6 +14,7 @@ if libqws.so is missing, the first call raises (there is no CPU fallback).
 from __future__ import annotations
 
 import ctypes as C
+import os
 from dataclasses import dataclass
 from typing import Optional
 
@@ -28,7 +29,8 @@ __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_fp8_codes_bytes", "fp8_codes_rowmajor", "lmhead_gemv_fp8", "lmhead_gemv_bf16",
-           "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8",
+           "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8", "lmhead_gemv_fp8_rtc", "rtc_compile_head_fp8",
+           "rtc_stats", "rtc_reset",
            "verify_workspace", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
 
@@ -343,6 +345,39 @@ def lmhead_gemv_fp8(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
 
 def lmhead_gemv_bf16(head: LMHead, x: torch.Tensor, out=None) -> torch.Tensor:
     return _gemv("lmhead_gemv_bf16", head, x, out)
+
+
+# ----------------------------------------------------------------------------------- run-time specialisation
+def _enc(path):
+    return None if path is None else os.fsencode(path)
+
+
+def lmhead_gemv_fp8_rtc(head: LMHead, x: torch.Tensor, out=None, cache_dir=None) -> torch.Tensor:
+    """lmhead_gemv_fp8 compiled at run time for this head's shape, M and the device (hipRTC), with
+    the code object cached in `cache_dir` ($QWS_RTC_CACHE or ~/.cache/qws_rtc when None)."""
+    _need(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, head.rows), dtype=torch.float32, device=x.device)
+    st = lib().lmhead_gemv_fp8_rtc(C.byref(head.desc), _p(x), M, _p(out), _enc(cache_dir), _stream(x.device))
+    check("lmhead_gemv_fp8_rtc", st)
+    return out
+
+
+def rtc_compile_head_fp8(M: int, rows: int, cols: int, arch: str = "gfx950", cache_dir=None) -> None:
+    """Compile (or find cached) the run-time-specialised FP8 head GEMV without a device."""
+    check("qws_rtc_compile_head_fp8", lib().qws_rtc_compile_head_fp8(M, rows, cols, arch.encode(), _enc(cache_dir)))
+
+
+def rtc_stats() -> dict:
+    s = _lib.RtcStats()
+    check("qws_rtc_stats_get", lib().qws_rtc_stats_get(C.byref(s)))
+    return {k: getattr(s, k) for k, _ in _lib.RtcStats._fields_}
+
+
+def rtc_reset() -> None:
+    """Unload the run-time-compiled modules and zero the counters (the disk cache stays)."""
+    check("qws_rtc_reset", lib().qws_rtc_reset())
 
 
 def verify_workspace(M: int, device) -> torch.Tensor:

@@ -15,6 +15,7 @@ QWS_ERR_FORMAT = -4
 QWS_ERR_WORKSPACE = -5
 QWS_ERR_DEVICE = -6
 QWS_ERR_SELFCHECK = -7
+QWS_ERR_COMPILE = -8
 
 QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634
 QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845
@@ -38,6 +39,11 @@ class MoeLayerDesc(C.Structure):
 class LMHeadDesc(C.Structure):
     _fields_ = [("format", C.c_uint), ("rows", C.c_longlong), ("cols", C.c_longlong), ("w", C.c_void_p),
                 ("row_scale", C.c_void_p)]
+
+
+class RtcStats(C.Structure):
+    _fields_ = [("compiles", C.c_ulonglong), ("disk_hits", C.c_ulonglong), ("memory_hits", C.c_ulonglong),
+                ("compile_ms", C.c_double), ("load_ms", C.c_double)]
 
 
 _P = C.c_void_p
@@ -69,6 +75,10 @@ SIGNATURES = {
     "lmhead_verify_sample_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, C.c_float, _I, C.c_float, _P, _P, _P, _P,
                                       _P, _P, _P, _SZ, _P]),
     "lmhead_gemv_bf16": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
+    "lmhead_gemv_fp8_rtc": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, C.c_char_p, _P]),
+    "qws_rtc_compile_head_fp8": (_I, [_I, _LL, _LL, C.c_char_p, C.c_char_p]),
+    "qws_rtc_stats_get": (_I, [C.POINTER(RtcStats)]),
+    "qws_rtc_reset": (_I, []),
     "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),
     "qws_debug_dequant_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _P]),
     "qws_probe_read": (_I, [_P, _SZ, _P, _I, _P]),

@@ -209,6 +209,10 @@ int set_device_error(hipError_t e) {
   snprintf(g_err, sizeof(g_err), "%s", hipGetErrorString(e));
   return QWS_ERR_DEVICE;
 }
+int set_error_text(int status, const char* text) {
+  snprintf(g_err, sizeof(g_err), "%s", text ? text : "");
+  return status;
+}
 }  // namespace qws_host
 
 extern "C" const char* qws_strerror(int status) {
@@ -223,8 +227,9 @@ extern "C" const char* qws_strerror(int status) {
     case QWS_ERR_WORKSPACE: base = "workspace missing or too small"; break;
     case QWS_ERR_DEVICE: base = "HIP runtime error"; break;
     case QWS_ERR_SELFCHECK: base = "device format self-check failed"; break;
+    case QWS_ERR_COMPILE: base = "run-time compilation failed"; break;
   }
-  if (status == QWS_ERR_DEVICE || status == QWS_ERR_SELFCHECK) {
+  if (status == QWS_ERR_DEVICE || status == QWS_ERR_SELFCHECK || status == QWS_ERR_COMPILE) {
     snprintf(buf, sizeof(buf), "%s: %s", base, g_err);
     return buf;
   }

@@ -1,0 +1,193 @@
+// The FP8 LM-head GEMV of libqws on the matrix cores (gfx950), with its verification epilogues.
+// Compiled twice: into the library as a template over (M, mode), and at run time by hipRTC with
+// the head's rows and cols fixed (QWS_SPEC_ROWS / QWS_SPEC_COLS), which lets the compiler fold
+// every shape-dependent bound (see rtc.hip). One source, so both give the same logits bit for bit.
+#pragma once
+
+#include "qws_common.hpp"
+
+namespace qws_head {
+
+using namespace qws;
+
+constexpr int kMaxCols = 2560;
+
+// Non-temporal 16-byte load of head weights (each byte is read once per call).
+__device__ __forceinline__ u32x4_t ld16_weights(const void* p) {
+  return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);
+}
+
+// The head's rows in tiles of 16 on the matrix cores: D (16 rows x 16 columns) += A (16 rows x 32
+// codes, E4M3 -> bf16, exact) x B (32 columns of x x 16 tokens; tokens M .. 15 are zero), fp32
+// accumulation. The codes are stored tile-major (tile t of 16 rows at byte 16 t cols; inside it,
+// chunk c of tile row i at byte 16 (16c + i)) so that the 64 lanes of a wave load 1 KB of
+// consecutive bytes per instruction: chunk c of tile row i is what lane
+// (g = c % 4, i) needs for k-block c / 4. A row-major head read this way moves 16 rows x 64 B per
+// instruction and measured ~25% slower on MI355X.
+// A workgroup takes one tile at a time; its kHeadWaves waves split the tile's columns, the next
+// tile's codes load while the current one is multiplied, and the waves' partial sums meet in LDS.
+// Every token's column is computed the same way whatever M is, so a window of M tokens gives each
+// token the logits it would get alone, bit for bit.
+constexpr int kHeadWaves = 8;
+constexpr int kKbw = kMaxCols / 64 / kHeadWaves;  // k-blocks (64 columns) per wave
+constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x (bf16 elements)
+constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
+
+// kMode: kGemv (logits only), kGreedy (logits optional, greedy verification epilogue), kKeys
+// (logits and each workgroup's largest key per token, for the sampling kernel).
+enum HeadMode { kGemv = 0, kGreedy = 1, kKeys = 2 };
+
+template <int M, int kMode>
+__global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ scale, long long rows, int cols,
+    const uint16_t* __restrict__ x, float* __restrict__ out, const int* __restrict__ draft,
+    int* __restrict__ target_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
+    unsigned long long* __restrict__ keys, unsigned* __restrict__ counters) {
+#ifdef QWS_SPEC_COLS
+  // compiled at run time for one head: the shape is a constant (the arguments carry the same values)
+  rows = QWS_SPEC_ROWS;
+  cols = QWS_SPEC_COLS;
+#endif
+  __shared__ __align__(16) uint16_t xs[M * kXsStride];
+  __shared__ __align__(16) float red[2][kHeadWaves][M][16];
+  __shared__ bool s_last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1), g = lane >> 4, i = lane & 15;
+  const long long ntiles = (rows + 15) >> 4;   // the grid never exceeds it
+  const int ncs = cols >> 4;                   // 16-byte chunks per row
+  const int kb0 = wave * kKbw;
+  // this wave's codes of a tile: k-blocks kb0 .. kb0 + kKbw - 1, 1 KB each (chunks past the row
+  // end are not loaded and add zeros)
+  auto load = [&](long long tl, u32x4_t (&w)[kKbw]) {
+    const uint8_t* p = q + tl * 16 * (long long)cols + lane * 16;
+#pragma unroll
+    for (int t = 0; t < kKbw; ++t)
+      w[t] = 4 * (kb0 + t) + g < ncs ? ld16_weights(p + (kb0 + t) * 1024) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  long long tile = blockIdx.x;
+  u32x4_t cur[kKbw], nxt[kKbw];
+  load(tile, cur);
+  // epilogue thread: tile row er of token em
+  const int er = tid & 15, em = tid >> 4;
+  const bool ep = tid < 16 * M;
+  float sc = ep ? scale[min(tile * 16 + er, rows - 1)] : 0.0f;
+  unsigned long long best = 0ull;   // below every key
+  // x (bf16) into LDS, zero past the row end
+  for (int e = tid; e < M * (kXsStride / 8); e += kHeadWaves * kWave) {
+    const int m = e / (kXsStride / 8), c = (e % (kXsStride / 8)) * 8;
+    *reinterpret_cast<u32x4_t*>(xs + m * kXsStride + c) =
+        c < cols ? ld16(x + (size_t)m * cols + c) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  int buf = 0;
+  for (; tile < ntiles; tile += gridDim.x) {
+    const long long tn = tile + gridDim.x;
+    if (tn < ntiles) load(tn, nxt);
+    const float scn = ep && tn < ntiles ? scale[min(tn * 16 + er, rows - 1)] : 0.0f;
+    f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+#pragma unroll
+    for (int t = 0; t < kKbw; ++t) {
+      // lane (g, i) holds codes 16c .. 16c+15 of tile row i (c = 4 kb + g): the first 8 go with
+      // x columns 16c .. 16c+7 in one product, the last 8 with 16c+8 .. 16c+15 in the other
+      u32x4_t xa = {0u, 0u, 0u, 0u}, xb = xa;
+      if (i < M) {
+        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs + i * kXsStride + 64 * (kb0 + t) + 16 * g);
+        xa = xp[0];
+        xb = xp[1];
+      }
+      const u32x4_t w = cur[t];
+      const u32x4_t alo = {__builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[0])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[0])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[1])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[1]))};
+      const u32x4_t ahi = {__builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[2])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[2])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(w[3])),
+                           __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(w[3]))};
+      d0 = mfma_16x16x32(alo, xa, d0);
+      d1 = mfma_16x16x32(ahi, xb, d1);
+    }
+    // lane (g, i < M) holds token i's partial sums of tile rows 4g .. 4g+3
+    if (i < M) *reinterpret_cast<f32x4_t*>(&red[buf][wave][i][4 * g]) = d0 + d1;
+    __syncthreads();   // red[buf] is rewritten two tiles later, after the next barrier
+    if (ep) {
+      float v = red[buf][0][em][er];
+#pragma unroll
+      for (int w = 1; w < kHeadWaves; ++w) v += red[buf][w][em][er];
+      v *= sc;
+      const long long row = tile * 16 + er;
+      if (row < rows) {
+        if (kMode != kGreedy || out) out[(size_t)em * rows + row] = v;
+        if constexpr (kMode != kGemv) {
+          const unsigned long long k = rank_key(sel_key(v), (int)row);
+          best = k > best ? k : best;
+        }
+      }
+    }
+    sc = scn;
+    buf ^= 1;
+#pragma unroll
+    for (int t = 0; t < kKbw; ++t) cur[t] = nxt[t];
+  }
+  if constexpr (kMode != kGemv) {
+    // Greedy verification epilogue: the workgroup's largest (logit, lower row) key per token, then
+    // the last workgroup to arrive (two-level arrival) reduces all of them to each position's
+    // target token and forms the accepted prefix of the M - 1 draft tokens.
+    __shared__ unsigned long long s_best[kHeadWaves][M];
+    const unsigned G = gridDim.x;
+    if (ep) {   // tokens' epilogue threads are the 16-lane groups of wave 0
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const unsigned long long k = __shfl_xor(best, o, kWave);
+        best = k > best ? k : best;
+      }
+      if (er == 0) st_coherent(keys + (size_t)em * G + blockIdx.x, best);   // token-major
+    }
+    if (kMode == kKeys || !arrive_last_grid(counters, &s_last)) return;
+    // every thread of the last workgroup loads its share of all keys at once (device-coherent
+    // loads, independent of each other), then the maxima meet in registers and LDS
+    constexpr int kPer = (kHeadGrid + kHeadWaves * kWave - 1) / (kHeadWaves * kWave);
+    unsigned long long kk[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) kk[m] = 0ull;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      // past the grid: the last key again (no branch, so the loads issue together)
+      const unsigned b = min(tid + j * kHeadWaves * kWave, G - 1);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const unsigned long long k = ld_coherent(keys + (size_t)m * G + b);
+        kk[m] = k > kk[m] ? k : kk[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long ko = __shfl_xor(kk[m], o, kWave);
+        kk[m] = ko > kk[m] ? ko : kk[m];
+      }
+      if (lane == 0) s_best[wave][m] = kk[m];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int target[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        unsigned long long k = s_best[0][m];
+#pragma unroll
+        for (int w = 1; w < kHeadWaves; ++w) k = s_best[w][m] > k ? s_best[w][m] : k;
+        target[m] = (int)(0xffffffffu - (uint32_t)k);
+        target_out[m] = target[m];
+      }
+      // draft i is accepted while it equals the target of position i; then the target of the
+      // first position not accepted
+      int a = 0;
+      while (a < M - 1 && draft[a] == target[a]) ++a;
+#pragma unroll
+      for (int m = 0; m < M; ++m) emitted_out[m] = m < a ? draft[m] : (m == a ? target[a] : -1);
+      *n_out = a + 1;
+    }
+  }
+}
+
+}  // namespace qws_head

@@ -1,10 +1,18 @@
 // Shared device helpers and host-side plumbing of libqws (gfx950 only).
 #pragma once
 
+#ifndef __HIPCC_RTC__   // hipRTC (rtc.hip) compiles the device part alone, with its own runtime headers
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/qws.h"
+#else
+typedef __hip_internal::uint8_t uint8_t;
+typedef __hip_internal::uint16_t uint16_t;
+typedef __hip_internal::uint32_t uint32_t;
+typedef __hip_internal::int32_t int32_t;
+typedef __hip_internal::uint64_t uint64_t;
+#endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -245,9 +253,12 @@ __device__ __forceinline__ bool arrive_last_grid(unsigned* counters, bool* lds_f
 }  // namespace qws
 
 // ------------------------------------------------------------------------------ host side
+#ifndef __HIPCC_RTC__
 namespace qws_host {
 
 int set_device_error(hipError_t e);  // records the message, returns QWS_ERR_DEVICE
+int set_error_text(int status, const char* text);  // records `text` for qws_strerror, returns status
+int head_fp8_rtc_function(int M, long long rows, long long cols, const char* cache_dir, void** fn_out);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -258,3 +269,4 @@ inline int check_launch() {
 }
 
 }  // namespace qws_host
+#endif
