@@ -349,7 +349,7 @@ def main():
                 "algorithmic_bytes_per_launch": moe_bytes, "launch_us_mean": round(r["moe_us_mean"], 2)}
     head_launch_bytes = head_bytes(1)
     head_gbs = head_launch_bytes / (r["head_us_mean"] * 1e-6) / 1e9
-    roofline_head = {"bound": "hbm", "kernel": "head_fp8_kernel<1, false> (FP8 LM head, 157184x2560)",
+    roofline_head = {"bound": "hbm", "kernel": "head_fp8_kernel<1, 0> (FP8 LM head GEMV, 157184x2560)",
                      "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("lmhead.hip", "head_fp8_kernel"),
                      "algorithmic_bytes_per_launch": head_launch_bytes, "launch_us_mean": round(r["head_us_mean"], 2)}
