@@ -322,7 +322,8 @@ int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, 
  * same source as lmhead_gemv_fp8 with rows and cols as constants, for the current device's
  * architecture (gcnArchName) and M. Key: (M, rows, cols, architecture, source hash); the disk
  * cache is `cache_dir` (NULL: $QWS_RTC_CACHE, else $HOME/.cache/qws_rtc), one file per key,
- * written whole (rename) so that concurrent processes never read half a file.
+ * written whole (rename) so that concurrent processes never read half a file. Cache files are
+ * loaded as device code: the directory must be writable by trusted users only.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   unsigned long long compiles;    /* hipRTC compilations */
