@@ -452,28 +452,31 @@ def main():
         shutil.rmtree(rtc_dir, ignore_errors=True)
         breakdown["lmhead_fp8_rtc"] = rtc
         log("lmhead_fp8_rtc", rtc)
-        # the same 42 layers chained as in a model (x of layer l+1 = layer l's bf16 y): the layers
-        # hand y over row by row instead of passing a layer barrier
+        # chained layers (x of layer l+1 = layer l's bf16 y, one launch) against the same layers
+        # launched as independent layers. Without the model's normalisation between layers |y| grows
+        # ~40x per layer with these weights and is NaN after ~5 layers (every logit then ties), so
+        # the comparison uses the first 4 layers, whose values stay finite.
+        nch = 4
         chain = []
-        for l, L in enumerate(step.layers):
+        for l, L in enumerate(step.layers[:nch]):
             chain.append(qws.MoeLayer(L.x if l == 0 else chain[-1].y_bf16, L.wr, L.packed, K_TOP, want_f32=False))
-        seqc = qws.MoeLayers(chain)
-        for _ in range(3):
-            seqc.run(step.ws)
-        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for a, b in evc:
-            a.record()
-            seqc.run(step.ws)
-            b.record()
-        torch.cuda.synchronize(dev)
-        tc = sorted(a.elapsed_time(b) * 1e3 for a, b in evc)
-        cb = args.layers * layer_bytes(8, 1)
-        breakdown["moe_layers_m1_chained"] = {"us_median": round(tc[len(tc) // 2], 2),
-                                              "us_per_layer": round(tc[len(tc) // 2] / args.layers, 3),
-                                              "bytes": cb, "GBps": round(cb / (tc[len(tc) // 2] * 1e-6) / 1e9, 1),
-                                              "in_kernel_wait_timeouts": step.errors()}
-        log("moe_layers_m1_chained", breakdown["moe_layers_m1_chained"])
-        del chain, seqc
+        cmp = {}
+        for name, seq4 in (("chained", qws.MoeLayers(chain)), ("independent", qws.MoeLayers([L.fused for L in step.layers[:nch]]))):
+            for _ in range(3):
+                seq4.run(step.ws)
+            evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+            for a, b in evc:
+                a.record()
+                seq4.run(step.ws)
+                b.record()
+            torch.cuda.synchronize(dev)
+            tc = sorted(a.elapsed_time(b) * 1e3 for a, b in evc)
+            cmp[name] = {"us_median": round(tc[len(tc) // 2], 2), "us_per_layer": round(tc[len(tc) // 2] / nch, 3)}
+        cmp["finite"] = bool(all(torch.isfinite(L.y_bf16.float()).all() for L in chain))
+        cmp["in_kernel_wait_timeouts"] = step.errors()
+        breakdown["moe_layers_m1_chained_4"] = cmp
+        log("moe_layers_m1_chained_4", cmp)
+        del chain
         # decode step at M = 4 (natural routing), sharing the M = 1 step's expert banks
         step4 = DecodeStep(qws, 4, dev, args.layers, head8, packed=[L.packed for L in step.layers])
         step4.layers_call()
