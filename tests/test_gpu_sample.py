@@ -165,3 +165,34 @@ def test_sample_full_head_window():
         res = _run(h8, xt, draft, u, ws, **PAGES)
         checked += _check(res, draft, u, PAGES, h8.rows)
     assert checked >= 12
+
+
+def test_sample_many_ties_across_workgroups():
+    """100 equal top logits on rows spread over many 16-row tiles (so over many head workgroups):
+    the top 29 are the 29 lowest of those rows, and each tied token takes an equal share."""
+    say("sample: 100 ties across workgroups")
+    rows, cols = 40000, 256
+    w = synth.bf16_normal(17, 0, synth.HEAD, 0, (rows, cols), 0.02).copy()
+    x = synth.token_vectors(17, 0, 1, cols)
+    tied = np.random.default_rng(17).choice(rows, 100, replace=False)
+    w[tied] = np.where(x[0] & 0x8000, 0xC000, 0x4000)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    kw = dict(temperature=0.6, top_k=29, top_p=1.0)
+    res = _run(h8, bf16(x), [], [0.5], qws.verify_workspace(1, "cuda"), **kw)
+    assert res["topk"][0].tolist() == sorted(tied.tolist())[:29]
+    assert int(res["token"][0]) == sorted(tied.tolist())[14]   # u = 0.5 of 29 equal shares
+    _check(res, [], [0.5], kw, rows)
+
+
+def test_sample_all_logits_equal():
+    """x = 0: every logit is 0, the order is the row order, top_p 0.95 keeps 28 of 29 equal tokens."""
+    say("sample: all logits equal")
+    rows, cols = 9000, 128
+    h8 = qws.lmhead_quantize_fp8(bf16(synth.bf16_normal(18, 0, synth.HEAD, 0, (rows, cols), 0.02)))
+    x = np.zeros((2, cols), dtype=np.uint16)
+    ws = qws.verify_workspace(2, "cuda")
+    for u in (0.0, 0.5, 0.99):
+        res = _run(h8, bf16(x), [3], [u, u], ws, **PAGES)
+        assert res["topk"].tolist() == [list(range(29))] * 2
+        assert res["token"].tolist() == [int(u * 28)] * 2
+        assert int(res["n"][0]) == 1 + (int(u * 28) == 3)
