@@ -4,8 +4,8 @@
 // (runbyai.xyz/posts/593 paragraph 3; Netics, "Online FP8 quantization halves the LM head weight
 // reads"). For M <= 4 the GEMV is a pure HBM stream, so the kernels are built around keeping many
 // 128-bit loads in flight per lane, and the weights are read with non-temporal loads (measured on
-// MI355X over the 402 MB FP8 head: 63.6 us against 71.4 us with ordinary loads, whose lines are
-// kept in the caches that a read-once stream never revisits):
+// MI355X with an earlier row-major FP8 GEMV over the 402 MB head: 63.6 us against 71.4 us with
+// ordinary loads, whose lines are kept in the caches that a read-once stream never revisits):
 //  - FP8: the quantiser writes the codes tile-major (16-row tiles) and the GEMV runs each tile on
 //    the matrix cores, with x in LDS: the code registers a wave needs do not grow with M (x held
 //    in registers for every token did, and the M = 4 GEMV ran at half speed for want of waves).
