@@ -351,7 +351,7 @@ def main():
     head_gbs = head_launch_bytes / (r["head_us_mean"] * 1e-6) / 1e9
     roofline_head = {"bound": "hbm", "kernel": "head_fp8_kernel<1, 0> (FP8 LM head GEMV, 157184x2560)",
                      "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("lmhead.hip", "head_fp8_kernel"),
+                     "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("head_fp8.hpp", "head_fp8_kernel"),
                      "algorithmic_bytes_per_launch": head_launch_bytes, "launch_us_mean": round(r["head_us_mean"], 2)}
 
     breakdown = {"decode_step_m1": {"ms_wall": round(r["wall_ms"], 4), "ms_gpu_events": round(r["gpu_ms"], 4),
