@@ -283,6 +283,8 @@ int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* lo
  *   = -1 for i >= n. All of these are device memory owned by the caller.
  *   workspace: lmhead_verify_workspace_bytes(M) bytes, 16-byte aligned, zero-filled before its
  *   first use and left ready for the next call; calls that share it must not overlap.
+ * Two launches: the head GEMV (logits, and each workgroup's largest key per position), then one
+ * workgroup that reduces the keys and forms the window.
  * Errors: QWS_ERR_FORMAT for a head that is not FP8-tagged, QWS_ERR_ARG for a missing pointer,
  * QWS_ERR_SHAPE for M outside 1 .. 4, QWS_ERR_WORKSPACE / QWS_ERR_ALIGN as elsewhere. */
 size_t lmhead_verify_workspace_bytes(int M);

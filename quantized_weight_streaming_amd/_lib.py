@@ -90,10 +90,15 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> C.CDLL:
-    """Load libqws.so once. Raises if it has not been built: there is no fallback path."""
-    global _lib
-    if _lib is None:
+_lib_path = None
+
+
+def load(path: str | None = None) -> C.CDLL:
+    """The loaded libqws: the in-tree build unless `path` names another build, which then replaces
+    it for every later call. Raises if it has not been built: there is no fallback path."""
+    global _lib, _lib_path
+    if _lib is None or (path is not None and os.path.realpath(path) != _lib_path):
+        path = path or LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(f"libqws.so not built at {path}; run quantized_weight_streaming_amd/build.py "
                                "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
@@ -102,7 +107,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = lib
+        _lib, _lib_path = lib, os.path.realpath(path)
     return _lib
 
 

@@ -33,16 +33,14 @@ constexpr int kKbw = kMaxCols / 64 / kHeadWaves;  // k-blocks (64 columns) per w
 constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x (bf16 elements)
 constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
 
-// kMode: kGemv (logits only), kGreedy (logits optional, greedy verification epilogue), kKeys
-// (logits and each workgroup's largest key per token, for the sampling kernel).
-enum HeadMode { kGemv = 0, kGreedy = 1, kKeys = 2 };
+// kMode: kGemv (logits), kKeys (logits optional, and each workgroup's largest (logit, lower row)
+// key per token, for the verification epilogues: greedy_finish_kernel and sample_kernel).
+enum HeadMode { kGemv = 0, kKeys = 1 };
 
 template <int M, int kMode>
 __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ scale, long long rows, int cols,
-    const uint16_t* __restrict__ x, float* __restrict__ out, const int* __restrict__ draft,
-    int* __restrict__ target_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
-    unsigned long long* __restrict__ keys, unsigned* __restrict__ counters) {
+    const uint16_t* __restrict__ x, float* __restrict__ out, unsigned long long* __restrict__ keys) {
 #ifdef QWS_SPEC_COLS
   // compiled at run time for one head: the shape is a constant (the arguments carry the same values)
   rows = QWS_SPEC_ROWS;
@@ -50,7 +48,6 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
 #endif
   __shared__ __align__(16) uint16_t xs[M * kXsStride];
   __shared__ __align__(16) float red[2][kHeadWaves][M][16];
-  __shared__ bool s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1), g = lane >> 4, i = lane & 15;
   const long long ntiles = (rows + 15) >> 4;   // the grid never exceeds it
   const int ncs = cols >> 4;                   // 16-byte chunks per row
@@ -116,8 +113,8 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
       v *= sc;
       const long long row = tile * 16 + er;
       if (row < rows) {
-        if (kMode != kGreedy || out) out[(size_t)em * rows + row] = v;
-        if constexpr (kMode != kGemv) {
+        if (kMode == kGemv || out) out[(size_t)em * rows + row] = v;
+        if constexpr (kMode == kKeys) {
           const unsigned long long k = rank_key(sel_key(v), (int)row);
           best = k > best ? k : best;
         }
@@ -128,64 +125,16 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
 #pragma unroll
     for (int t = 0; t < kKbw; ++t) cur[t] = nxt[t];
   }
-  if constexpr (kMode != kGemv) {
-    // Greedy verification epilogue: the workgroup's largest (logit, lower row) key per token, then
-    // the last workgroup to arrive (two-level arrival) reduces all of them to each position's
-    // target token and forms the accepted prefix of the M - 1 draft tokens.
-    __shared__ unsigned long long s_best[kHeadWaves][M];
-    const unsigned G = gridDim.x;
-    if (ep) {   // tokens' epilogue threads are the 16-lane groups of wave 0
+  if constexpr (kMode == kKeys) {
+    // the workgroup's largest key per token (epilogue threads of token m: the 16-lane groups of
+    // wave 0), token-major, for greedy_finish_kernel / sample_kernel
+    if (ep) {
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) {
         const unsigned long long k = __shfl_xor(best, o, kWave);
         best = k > best ? k : best;
       }
-      if (er == 0) st_coherent(keys + (size_t)em * G + blockIdx.x, best);   // token-major
-    }
-    if (kMode == kKeys || !arrive_last_grid(counters, &s_last)) return;
-    // every thread of the last workgroup loads its share of all keys at once (device-coherent
-    // loads, independent of each other), then the maxima meet in registers and LDS
-    constexpr int kPer = (kHeadGrid + kHeadWaves * kWave - 1) / (kHeadWaves * kWave);
-    unsigned long long kk[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) kk[m] = 0ull;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      // past the grid: the last key again (no branch, so the loads issue together)
-      const unsigned b = min(tid + j * kHeadWaves * kWave, G - 1);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const unsigned long long k = ld_coherent(keys + (size_t)m * G + b);
-        kk[m] = k > kk[m] ? k : kk[m];
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const unsigned long long ko = __shfl_xor(kk[m], o, kWave);
-        kk[m] = ko > kk[m] ? ko : kk[m];
-      }
-      if (lane == 0) s_best[wave][m] = kk[m];
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int target[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        unsigned long long k = s_best[0][m];
-#pragma unroll
-        for (int w = 1; w < kHeadWaves; ++w) k = s_best[w][m] > k ? s_best[w][m] : k;
-        target[m] = (int)(0xffffffffu - (uint32_t)k);
-        target_out[m] = target[m];
-      }
-      // draft i is accepted while it equals the target of position i; then the target of the
-      // first position not accepted
-      int a = 0;
-      while (a < M - 1 && draft[a] == target[a]) ++a;
-#pragma unroll
-      for (int m = 0; m < M; ++m) emitted_out[m] = m < a ? draft[m] : (m == a ? target[a] : -1);
-      *n_out = a + 1;
+      if (er == 0) keys[(size_t)em * gridDim.x + blockIdx.x] = best;
     }
   }
 }

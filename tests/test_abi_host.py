@@ -303,3 +303,18 @@ def test_pack_bytes(lib):
 def test_pack_validation(lib, kw, status):
     assert _pack(lib, **kw) == status
 
+
+
+def test_load_switches_to_another_build(tmp_path):
+    import shutil
+    default = _lib.load()
+    assert _lib.load() is default and _lib.load(_lib.LIB_PATH) is default
+    copy = str(tmp_path / "libqws_copy.so")
+    shutil.copy(_lib.LIB_PATH, copy)
+    try:
+        other = _lib.load(copy)
+        assert other is not default and _lib.load() is other      # later calls use the named build
+        assert other.qws_abi_version() == default.qws_abi_version()
+    finally:
+        _lib.load(_lib.LIB_PATH)
+    assert _lib.load() is not other
