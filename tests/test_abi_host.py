@@ -318,3 +318,20 @@ def test_load_switches_to_another_build(tmp_path):
     finally:
         _lib.load(_lib.LIB_PATH)
     assert _lib.load() is not other
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/qws.h compiles as C99 (no C++ or HIP types in the boundary) and as C++17."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "qws.h"\nint main(void) { qws_lmhead h; qws_rtc_stats s; (void)h; (void)s;'
+                   ' return qws_abi_version() == 0; }\n')
+    inc = os.path.join(ROOT, "include")
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not installed")
+        lang = ["-x", "c++"] if cc == "g++" else []
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, *lang, str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
