@@ -111,3 +111,39 @@ def test_verify_full_head_window():
     for draft in _drafts(res["target"], h8.rows):
         res, lg = _run(h8, xt, draft, ws)
         _check_window(res, lg, draft)
+
+
+def test_verify_in_a_hip_graph():
+    """The head GEMV and both verification epilogues captured in one HIP graph: every replay (with
+    eager work between the replays) equals the eager result."""
+    say("verify graph replay")
+    rows, cols = 6000, 512
+    w = synth.bf16_normal(19, 0, synth.HEAD, 0, (rows, cols), 0.02)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    x = bf16(synth.token_vectors(19, 0, 4, cols))
+    d = torch.tensor([1, 2, 3], dtype=torch.int32, device="cuda")
+    u = torch.tensor([0.2, 0.4, 0.6, 0.8], dtype=torch.float32, device="cuda")
+    ws_g, ws_s = qws.verify_workspace(4, "cuda"), qws.verify_workspace(4, "cuda")
+    lg = torch.empty((4, rows), dtype=torch.float32, device="cuda")
+    g_out = qws.lmhead_verify_greedy_fp8(h8, x, d, ws_g, logits=lg)
+    s_out = qws.lmhead_verify_sample_fp8(h8, x, d, u, ws_s)
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in g_out.items()}
+    want.update({"s_" + k: v.clone() for k, v in s_out.items()})
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qws.lmhead_verify_greedy_fp8(h8, x, d, ws_g, logits=lg, out=g_out)
+        qws.lmhead_verify_sample_fp8(h8, x, d, u, ws_s, out=s_out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in list(g_out.values()) + list(s_out.values()):
+            v.zero_()                                  # eager work between the replays
+        lg.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = dict(g_out)
+        got.update({"s_" + k: v for k, v in s_out.items()})
+        for k, v in want.items():
+            assert torch.equal(got[k], v), f"replay {rep}: {k}"
+        assert torch.equal(lg, want["s_logits"])           # the greedy call's logits: the same values
