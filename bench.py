@@ -452,6 +452,24 @@ def main():
         shutil.rmtree(rtc_dir, ignore_errors=True)
         breakdown["lmhead_fp8_rtc"] = rtc
         log("lmhead_fp8_rtc", rtc)
+        # the same M = 1 step captured once in a HIP graph (the 42-layer launch and the head) and
+        # replayed: the host's per-step launch work leaves the loop
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.layers_call()
+            step.head_call()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        breakdown["decode_step_m1_graph"] = {"ms_wall": round(gms, 4), "GBps": round(sb / (gms * 1e-3) / 1e9, 1),
+                                             "in_kernel_wait_timeouts": step.errors()}
+        log("decode_step_m1_graph", breakdown["decode_step_m1_graph"])
+        del graph
         # chained layers (x of layer l+1 = layer l's bf16 y, one launch) against the same layers
         # launched as independent layers. Without the model's normalisation between layers |y| grows
         # ~40x per layer with these weights and is NaN after ~5 layers (every logit then ties), so
