@@ -52,13 +52,28 @@ def assert_close(got, ref, tol=TOL, what=""):
     return e
 
 
-def check_topk(gpu_idx: np.ndarray, gpu_logits: np.ndarray, ref_logits: np.ndarray, K: int) -> int:
-    """Top-k parity with a near-tie allowance. Where every adjacent gap among the oracle's top K+1
+def check_topk(gpu_idx: np.ndarray, gpu_logits: np.ndarray, ref_logits: np.ndarray, K: int,
+               gpu_w: np.ndarray | None = None) -> int:
+    """Top-k parity in two parts.
+
+    (i) Always, bit for bit: the oracle's selection routine run on the GPU's own float32 logits
+    gives the GPU's ordered indices (ties to the lower index), and, when gpu_w is given, the
+    oracle's softmax over those logits gives the GPU's gate weights (2e-6 absolute: a float32 exp,
+    sum of at most 8 terms and division, each within a few ulps of 1, against float64).
+    (ii) Against the float64 oracle logits: where every adjacent gap among the oracle's top K+1
     logits exceeds tau = 4 * max|l_gpu - l_ref| (+ a float32 ulp floor), the ordered indices must
-    be equal. Otherwise the GPU's set must still be a valid top-K of the oracle logits within tau.
-    Returns the number of tokens that needed the allowance."""
+    be equal; otherwise the GPU's set must still be a valid top-K of the oracle logits within tau.
+    Returns the number of tokens that needed that allowance."""
     near = 0
     for m in range(ref_logits.shape[0]):
+        own = gpu_logits[m].astype(np.float64)[None]
+        own_idx = OM.topk_select(own, K)[0]
+        assert list(gpu_idx[m]) == list(own_idx), \
+            f"token {m}: gpu {list(gpu_idx[m])} != oracle selection on the gpu logits {list(own_idx)}"
+        if gpu_w is not None:
+            own_w = OM.route_weights(own, own_idx[None])[0]
+            err = float(np.max(np.abs(np.asarray(gpu_w[m], np.float64) - own_w)))
+            assert err <= 2e-6, f"token {m}: gate weights differ from the oracle softmax of the gpu logits by {err:.3g}"
         ref = ref_logits[m]
         tau = 4 * float(np.max(np.abs(gpu_logits[m].astype(np.float64) - ref))) + 4e-7 * max(1.0, float(np.max(np.abs(ref))))
         order = OM.topk_select(ref[None], min(K + 1, ref.size))[0]
@@ -76,7 +91,8 @@ def check_topk(gpu_idx: np.ndarray, gpu_logits: np.ndarray, ref_logits: np.ndarr
 
 
 def check_argmax(gpu_logits: np.ndarray, ref_logits: np.ndarray, gap=ARGMAX_GAP) -> int:
-    """argmax must agree wherever the oracle's top-2 gap exceeds `gap`; returns the rows checked."""
+    """argmax must agree wherever the oracle's top-2 gap exceeds `gap`; returns the rows checked
+    (callers assert that it is above zero, so the rule cannot pass vacuously)."""
     checked = 0
     for m in range(ref_logits.shape[0]):
         top2 = np.sort(ref_logits[m])[-2:]

@@ -42,7 +42,8 @@ def _layer_case(layer: Layer):
     idx_t, w_t = qws.moe_route_topk(layer.x_t, layer.wr_t, layer.shape.topk, layer.bias_t, logits_out=logits)
     y16, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, idx_t, w_t)
     ridx, rw, rlg = layer.oracle_route()
-    near = check_topk(idx_t.cpu().numpy(), logits.cpu().numpy(), rlg, layer.shape.topk)
+    near = check_topk(idx_t.cpu().numpy(), logits.cpu().numpy(), rlg, layer.shape.topk,
+                      gpu_w=w_t.cpu().numpy())
     assert near == 0, "near-tie in a seeded layer case: pick another seed"
     ref = layer.oracle_y(ridx, rw)
     e = assert_close(y32.cpu().numpy(), ref, what=f"layer seed={layer.seed} M={layer.M}")

@@ -30,7 +30,8 @@ def _fused(layer: Layer, ws=None, logits=True):
 
 def _check_layer(layer: Layer, L):
     ridx, rw, rlg = layer.oracle_route()
-    near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, layer.shape.topk)
+    near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, layer.shape.topk,
+                      gpu_w=L.topk_w.cpu().numpy())
     assert near == 0
     e = assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"fused layer seed={layer.seed} M={layer.M}")
     _assert_bf16_is_rne_of_f32(L.y_bf16, L.y_f32)
@@ -294,7 +295,8 @@ def _oracle_chain_check(layers, Ls):
     for t, L in zip(layers, Ls):
         t.x = x                                            # the oracle chain's own input
         ridx, rw, rlg = t.oracle_route()
-        near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, t.shape.topk)
+        near = check_topk(L.topk_idx.cpu().numpy(), L.logits_out.cpu().numpy(), rlg, t.shape.topk,
+                          gpu_w=L.topk_w.cpu().numpy())
         if near:
             break
         y = t.oracle_y(ridx, rw)

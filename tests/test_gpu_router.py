@@ -25,7 +25,7 @@ def _check(x, wr, K, bias=None):
     idx, w, lg = _run(x, wr, K, bias)
     ridx, rw, rlg = OM.route(x, wr, K, bias)
     assert_close(lg, rlg, tol=1e-5, what="logits")
-    near = check_topk(idx, lg, rlg, K)
+    near = check_topk(idx, lg, rlg, K, gpu_w=w)
     if near == 0:
         assert_close(w, rw, tol=1e-5, what="gate weights")
     assert np.allclose(w.sum(1), 1.0, atol=1e-6)

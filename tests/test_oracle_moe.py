@@ -49,6 +49,29 @@ def test_negative_zero_ties_with_positive_zero():
     assert moe.topk_select(logits, 2).tolist() == [[1, 2]]
 
 
+def test_nan_ranks_as_minus_infinity_and_ties_with_it_by_index():
+    """A NaN logit ranks below every number and ties with -inf by index (the selection's reading
+    of NaN, stated with the router's entry point), written out by hand for a small row."""
+    nan, inf = np.nan, np.inf
+    logits = np.array([[nan, -inf, 1.0, nan, -inf, -3.0, 0.0]])
+    # numbers first (1.0 @2, 0.0 @6, -3.0 @5), then the five -inf/NaN entries in index order
+    assert moe.topk_select(logits, 7).tolist() == [[2, 6, 5, 0, 1, 3, 4]]
+    assert moe.topk_select(logits, 4).tolist() == [[2, 6, 5, 0]]
+    # a row of NaN only: index order, like an all-equal row
+    assert moe.topk_select(np.full((1, 5), nan), 3).tolist() == [[0, 1, 2]]
+    # brute force: a pure-Python insertion of each index behind every key that beats it
+    rng = np.random.default_rng(9)
+    row = rng.choice(np.array([nan, -inf, inf, -0.0, 0.0, 1.0, -1.0]), size=40)
+    key = [(-inf if math.isnan(v) else float(v)) for v in row]
+    order = []
+    for i in range(len(row)):
+        pos = 0
+        while pos < len(order) and (key[order[pos]] > key[i] or key[order[pos]] == key[i]):
+            pos += 1
+        order.insert(pos, i)
+    assert moe.topk_select(row[None], 40)[0].tolist() == order
+
+
 def test_topk_matches_torch_on_distinct_values():
     rng = np.random.default_rng(2)
     logits = rng.standard_normal((5, 512))
