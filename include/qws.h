@@ -49,9 +49,10 @@ enum qws_status {
  * interface makes the stack slower than baseline"). */
 enum qws_format {
   QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634, /* e2m1 nibbles + one E8M0 scale per 32 elements */
-  QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes + one fp32 scale per row */
+  QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes, row-major, + one fp32 scale per row */
   QWS_FMT_BF16 = 0x42463136,                /* plain bf16 */
-  QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654 /* MXFP4 experts, task-major (moe_pack_mxfp4) */
+  QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654, /* MXFP4 experts, task-major (moe_pack_mxfp4) */
+  QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 = 0x46503854 /* E4M3 codes in 16-row tiles (below) + fp32 row scales */
 };
 
 /* Text for a status code. For QWS_ERR_DEVICE the text of the calling thread's last HIP error is
@@ -226,15 +227,20 @@ int moe_workspace_errors(const void* workspace, int M, int K, int E, int inter, 
  * Vocabulary LM head (non-owning view). The head projects H = 2,560 onto 157,184 tokens and
  * every generated token reads all of it: ~805 MB per token in bf16, half in FP8 (posts/593
  * paragraph 3).
- *   format QWS_FMT_BF16:                w = bf16 [rows, cols], row_scale NULL.
- *   format QWS_FMT_FP8_E4M3FN_ROWSCALE: w = E4M3 codes u8, tile-major (below), row_scale fp32
- *                                       [rows]; weight[r, k] = e4m3(q[r, k]) * row_scale[r].
+ *   format QWS_FMT_BF16:                    w = bf16 [rows, cols], row_scale NULL.
+ *   format QWS_FMT_FP8_E4M3FN_ROWSCALE_T16: w = E4M3 codes u8, tile-major (below), row_scale fp32
+ *                                           [rows]; weight[r, k] = e4m3(q[r, k]) * row_scale[r].
+ *   format QWS_FMT_FP8_E4M3FN_ROWSCALE:     the same codes row-major, w = u8 [rows, cols]. The FP8
+ *                                           GEMVs read only tile-major codes and refuse this tag
+ *                                           (QWS_ERR_FORMAT): lmhead_fp8_tile_major converts.
  * rows >= 1; cols multiple of 32, 32 .. 2560.
  * Tile-major FP8 codes (lmhead_fp8_codes_bytes(rows, cols) bytes): the rows in tiles of 16, the
  * last one padded with zero-code rows; tile t starts at byte 16 t cols; inside it, the 16 codes
  * q[16 t + i, 16 c .. 16 c + 15] (chunk c of tile row i) are at byte 16 (16 c + i). A wave of the
  * GEMV then reads 1 KB of consecutive bytes per load instruction: 4 chunks of 16 rows, the
- * operand of one matrix-core product each.
+ * operand of one matrix-core product each. The layout is part of the tag, so row-major codes are
+ * never read as tiles (the pages' silent failure is a head read in the wrong format: posts/593
+ * paragraph 9).
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   unsigned format;
@@ -254,7 +260,8 @@ int lmhead_bf16_desc(const void* w_bf16, long long rows, long long cols, qws_lmh
  * Both divisions are IEEE float32 round-to-nearest-even.
  *   w_bf16 [rows, cols] in; codes_out u8, lmhead_fp8_codes_bytes(rows, cols) bytes (tile-major,
  *   pad rows written as zero codes) and row_scale_out fp32 [rows] out, all device memory owned by
- *   the caller. desc_out (host memory) is filled with an FP8-tagged descriptor of the outputs.
+ *   the caller. desc_out (host memory) is filled with a QWS_FMT_FP8_E4M3FN_ROWSCALE_T16
+ *   descriptor of the outputs.
  * Errors: QWS_ERR_ARG for a missing pointer, QWS_ERR_SHAPE for rows or cols out of range,
  * QWS_ERR_ALIGN for w_bf16 or codes_out not 16-byte aligned.                                 */
 int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long cols,
@@ -265,7 +272,18 @@ int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long cols,
  * rows or cols out of range. */
 size_t lmhead_fp8_codes_bytes(long long rows, long long cols);
 
-/* logits[m, r] = row_scale[r] * sum_k e4m3(q[r, k]) * x[m, k]   (head must be FP8-tagged)
+/* Tile-major copy of a head whose E4M3 codes are row-major (for example quantised elsewhere): the
+ * codes are moved into the layout above (pad rows zero), never changed. src must be tagged
+ * QWS_FMT_FP8_E4M3FN_ROWSCALE (QWS_ERR_FORMAT otherwise), with row_scale set; codes_out holds
+ * codes_bytes >= lmhead_fp8_codes_bytes(rows, cols) bytes of device memory, 16-byte aligned and
+ * not overlapping src->w (QWS_ERR_WORKSPACE, QWS_ERR_ALIGN, QWS_ERR_ARG otherwise). desc_out
+ * (host memory) receives a QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 descriptor of codes_out with src's
+ * row_scale pointer. */
+int lmhead_fp8_tile_major(const qws_lmhead* src, unsigned char* codes_out, size_t codes_bytes,
+                          qws_lmhead* desc_out, qws_stream_t stream);
+
+/* logits[m, r] = row_scale[r] * sum_k e4m3(q[r, k]) * x[m, k]   (head must be tagged
+ * QWS_FMT_FP8_E4M3FN_ROWSCALE_T16; QWS_ERR_FORMAT for any other tag, row-major FP8 included)
  *   x_bf16 [M, cols], 1 <= M <= 4; logits_out fp32 [M, rows]. Each token gets the same logits,
  *   bit for bit, whatever M and its place in the window.                                    */
 int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
@@ -285,7 +303,7 @@ int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* lo
  *   first use and left ready for the next call; calls that share it must not overlap.
  * Two launches: the head GEMV (logits, and each workgroup's largest key per position), then one
  * workgroup that reduces the keys and forms the window.
- * Errors: QWS_ERR_FORMAT for a head that is not FP8-tagged, QWS_ERR_ARG for a missing pointer,
+ * Errors: QWS_ERR_FORMAT for a head not tagged QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, QWS_ERR_ARG for a missing pointer,
  * QWS_ERR_SHAPE for M outside 1 .. 4, QWS_ERR_WORKSPACE / QWS_ERR_ALIGN as elsewhere. */
 size_t lmhead_verify_workspace_bytes(int M);
 int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
@@ -366,7 +384,7 @@ int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int M, float* l
 int qws_debug_dequant_mxfp4(const unsigned char* q, const unsigned char* s, long long rows,
                             int cols, int path, float* out, qws_stream_t stream);
 
-/* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for an FP8-tagged head (tile-major codes),
+/* out[r, k] = fl32(e4m3(q[r, k]) * row_scale[r]) for a QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 head,
  * fp32 [rows, cols] row-major.                                                              */
 int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t stream);
 

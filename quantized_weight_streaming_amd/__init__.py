@@ -22,7 +22,7 @@ import torch
 
 from . import _lib
 from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1_E8M0_B32,  # noqa: F401
-                   QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, QWS_TASK_BYTES, LMHeadDesc, MoeLayerDesc, MxFp4Experts,
+                   QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, QWS_TASK_BYTES, LMHeadDesc, MoeLayerDesc, MxFp4Experts,
                    QwsError, check)
 
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
@@ -316,6 +316,23 @@ def lmhead_quantize_fp8(w: torch.Tensor, codes=None, row_scale=None) -> LMHead:
     d = LMHeadDesc()
     st = lib().lmhead_quantize_fp8(_p(w), rows, cols, _p(codes), _p(row_scale), C.byref(d), _stream(w.device))
     check("lmhead_quantize_fp8", st)
+    return LMHead(codes, row_scale, d)
+
+
+def lmhead_fp8_tile_major(codes_rowmajor: torch.Tensor, row_scale: torch.Tensor, codes=None) -> LMHead:
+    """An FP8 head from row-major E4M3 codes uint8 [rows, cols] and fp32 row scales [rows]: the
+    codes are moved into the library's tile-major layout (lmhead_fp8_tile_major)."""
+    _need(codes_rowmajor, "codes_rowmajor", torch.uint8, 2)
+    _need(row_scale, "row_scale", torch.float32, 1)
+    rows, cols = codes_rowmajor.shape
+    n = lmhead_fp8_codes_bytes(rows, cols)
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.uint8, device=codes_rowmajor.device)
+    src = LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, _p(codes_rowmajor), _p(row_scale))
+    d = LMHeadDesc()
+    st = lib().lmhead_fp8_tile_major(C.byref(src), _p(codes), codes.numel(), C.byref(d),
+                                     _stream(codes_rowmajor.device))
+    check("lmhead_fp8_tile_major", st)
     return LMHead(codes, row_scale, d)
 
 

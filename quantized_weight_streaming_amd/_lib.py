@@ -21,6 +21,7 @@ QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634
 QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845
 QWS_FMT_BF16 = 0x42463136
 QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654
+QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 = 0x46503854
 QWS_TASK_BYTES = 131072
 
 
@@ -69,6 +70,7 @@ SIGNATURES = {
     "lmhead_bf16_desc": (_I, [_P, _LL, _LL, C.POINTER(LMHeadDesc)]),
     "lmhead_quantize_fp8": (_I, [_P, _LL, _LL, _P, _P, C.POINTER(LMHeadDesc), _P]),
     "lmhead_fp8_codes_bytes": (_SZ, [_LL, _LL]),
+    "lmhead_fp8_tile_major": (_I, [C.POINTER(LMHeadDesc), _P, _SZ, C.POINTER(LMHeadDesc), _P]),
     "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "lmhead_verify_workspace_bytes": (_SZ, [_I]),
     "lmhead_verify_greedy_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),

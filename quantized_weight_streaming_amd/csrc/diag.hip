@@ -304,7 +304,7 @@ extern "C" int qws_debug_dequant_mxfp4(const unsigned char* q, const unsigned ch
 
 extern "C" int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t stream) {
   if (!head || !head->w || !out) return QWS_ERR_ARG;
-  if (head->format != QWS_FMT_FP8_E4M3FN_ROWSCALE) return QWS_ERR_FORMAT;
+  if (head->format != QWS_FMT_FP8_E4M3FN_ROWSCALE_T16) return QWS_ERR_FORMAT;
   if (!head->row_scale) return QWS_ERR_ARG;
   if (head->rows < 1 || head->cols < 32 || head->cols > 65536 || head->cols % 32) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(head->w) || !qws_host::aligned16(out)) return QWS_ERR_ALIGN;

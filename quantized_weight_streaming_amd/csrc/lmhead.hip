@@ -85,6 +85,20 @@ __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const uint16_t* __
   }
 }
 
+// Row-major E4M3 codes -> tile-major: one thread per 16-byte chunk of the output (chunk c of tile
+// row i of tile t); the pad rows of the last tile get zero codes. Bytes move, values never change.
+__global__ void tile_major_fp8_kernel(const uint8_t* __restrict__ src, long long rows, int cols,
+                                      uint8_t* __restrict__ out, long long n_chunks) {
+  for (long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x; o < n_chunks;
+       o += (long long)gridDim.x * blockDim.x) {
+    const long long t = o / cols;          // a tile holds 16 x cols bytes = cols chunks
+    const int p = (int)(o - t * cols), c = p >> 4, i = p & 15;
+    const long long row = 16 * t + i;
+    const u32x4_t v = row < rows ? ld16(src + row * cols + 16 * c) : u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(out + o * 16) = v;
+  }
+}
+
 // --------------------------------------------------------------------------- greedy verification
 // After head_fp8_kernel<M, kKeys>: one workgroup reduces the head workgroups' largest keys of each
 // position to its target (the argmax, ties to the lower row) and forms the accepted prefix of the
@@ -391,7 +405,8 @@ int grid_for(long long units) {
 int check_head(const qws_lmhead* h, unsigned fmt) {
   if (!h || !h->w) return QWS_ERR_ARG;
   if (h->format != fmt) return QWS_ERR_FORMAT;
-  if (fmt == QWS_FMT_FP8_E4M3FN_ROWSCALE && !h->row_scale) return QWS_ERR_ARG;
+  if ((fmt == QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 || fmt == QWS_FMT_FP8_E4M3FN_ROWSCALE) && !h->row_scale)
+    return QWS_ERR_ARG;
   if (h->rows < 1 || h->rows > (1ll << 31) || h->cols < 32 || h->cols > kMaxCols || h->cols % 32) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(h->w)) return QWS_ERR_ALIGN;
   return QWS_OK;
@@ -415,7 +430,28 @@ extern "C" int lmhead_quantize_fp8(const void* w_bf16, long long rows, long long
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3(grid_for(rows)), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(w_bf16), rows, (int)cols, codes_out, row_scale_out);
   int st = qws_host::check_launch();
-  if (st == QWS_OK) *desc_out = qws_lmhead{QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, codes_out, row_scale_out};
+  if (st == QWS_OK) *desc_out = qws_lmhead{QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, rows, cols, codes_out, row_scale_out};
+  return st;
+}
+
+extern "C" int lmhead_fp8_tile_major(const qws_lmhead* src, unsigned char* codes_out, size_t codes_bytes,
+                                     qws_lmhead* desc_out, qws_stream_t stream) {
+  if (!desc_out || !codes_out) return QWS_ERR_ARG;
+  int st = check_head(src, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  if (st != QWS_OK) return st;
+  const size_t need = (size_t)((src->rows + 15) / 16 * 16) * (size_t)src->cols;
+  if (codes_bytes < need) return QWS_ERR_WORKSPACE;
+  if (!qws_host::aligned16(codes_out)) return QWS_ERR_ALIGN;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src->w), b = reinterpret_cast<uintptr_t>(codes_out);
+  const size_t in_bytes = (size_t)src->rows * (size_t)src->cols;
+  if (a < b + need && b < a + in_bytes) return QWS_ERR_ARG;
+  const long long n = (long long)(need / 16);
+  const long long want = (n + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(tile_major_fp8_kernel, dim3((unsigned)(want < 65536 ? want : 65536)), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src->w), src->rows, (int)src->cols,
+                     codes_out, n);
+  st = qws_host::check_launch();
+  if (st == QWS_OK) *desc_out = qws_lmhead{QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, src->rows, src->cols, codes_out, src->row_scale};
   return st;
 }
 
@@ -456,7 +492,7 @@ extern "C" size_t lmhead_fp8_codes_bytes(long long rows, long long cols) {
 
 extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out,
                                qws_stream_t stream) {
-  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE_T16);
   if (st != QWS_OK) return st;
   if (!x_bf16 || !logits_out) return QWS_ERR_ARG;
   if (M < 1 || M > 4) return QWS_ERR_SHAPE;
@@ -476,7 +512,7 @@ extern "C" size_t lmhead_verify_workspace_bytes(int M) {
 extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
                                         float* logits_out, int* target_out, int* emitted_out, int* n_out,
                                         void* workspace, size_t workspace_bytes, qws_stream_t stream) {
-  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE_T16);
   if (st != QWS_OK) return st;
   if (!x_bf16 || !target_out || !emitted_out || !n_out || (M > 1 && !draft)) return QWS_ERR_ARG;
   if (M < 1 || M > 4) return QWS_ERR_SHAPE;
@@ -506,7 +542,7 @@ extern "C" int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf
                                         float temperature, int top_k, float top_p, const float* u,
                                         float* logits_out, int* token_out, int* topk_out, int* emitted_out,
                                         int* n_out, void* workspace, size_t workspace_bytes, qws_stream_t stream) {
-  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE);
+  int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE_T16);
   if (st != QWS_OK) return st;
   if (!x_bf16 || !u || !logits_out || !token_out || !emitted_out || !n_out || (M > 1 && !draft)) return QWS_ERR_ARG;
   if (!(temperature > 0.0f) || !(temperature < 3.0e38f) || !(top_p > 0.0f) || !(top_p <= 1.0f)) return QWS_ERR_ARG;

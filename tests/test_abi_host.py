@@ -114,14 +114,47 @@ def test_expert_workspace_for_larger_window_is_required(lib):
 
 
 def test_lmhead_format_tags_refuse_mismatched_heads(lib):
-    fp8 = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 157184, 2560, A, A)
+    fp8 = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, 157184, 2560, A, A)
     bf16 = _lib.LMHeadDesc(_lib.QWS_FMT_BF16, 157184, 2560, A, None)
     # an FP8 head handed to the bf16 GEMV is refused instead of being read as bf16, and vice versa
     assert lib.lmhead_gemv_bf16(C.byref(fp8), A, 1, A, None) == _lib.QWS_ERR_FORMAT
     assert lib.lmhead_gemv_fp8(C.byref(bf16), A, 1, A, None) == _lib.QWS_ERR_FORMAT
     assert lib.qws_debug_dequant_fp8(C.byref(bf16), A, None) == _lib.QWS_ERR_FORMAT
-    nos = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 157184, 2560, A, None)
+    nos = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, 157184, 2560, A, None)
     assert lib.lmhead_gemv_fp8(C.byref(nos), A, 1, A, None) == _lib.QWS_ERR_ARG
+
+
+def test_row_major_fp8_head_is_refused_by_every_tile_major_reader(lib):
+    """The tile layout is part of the format tag: a head whose descriptor says its E4M3 codes are
+    row-major is refused by every entry point that reads tiles, instead of giving wrong logits."""
+    rm = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 157184, 2560, A, A))
+    wsb = lib.lmhead_verify_workspace_bytes(4)
+    assert lib.lmhead_gemv_fp8(rm, A, 1, A, None) == _lib.QWS_ERR_FORMAT
+    assert lib.lmhead_gemv_fp8_rtc(rm, A, 1, A, None, None) == _lib.QWS_ERR_FORMAT
+    assert lib.qws_debug_dequant_fp8(rm, A, None) == _lib.QWS_ERR_FORMAT
+    assert lib.lmhead_verify_greedy_fp8(rm, A, 4, A, None, A, A, A, A, wsb, None) == _lib.QWS_ERR_FORMAT
+    assert lib.lmhead_verify_sample_fp8(rm, A, 4, A, 0.6, 29, 0.95, A, A, A, None, A, A, A, wsb,
+                                        None) == _lib.QWS_ERR_FORMAT
+    assert lib.lmhead_gemv_bf16(rm, A, 1, A, None) == _lib.QWS_ERR_FORMAT
+
+
+def test_fp8_tile_major_validation(lib):
+    rows, cols = 100, 64
+    need = lib.lmhead_fp8_codes_bytes(rows, cols)
+    out = _lib.LMHeadDesc()
+    src = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, A, A)
+    far = A + (1 << 24)
+    call = lambda s, o=far, n=need, d=C.byref(out): lib.lmhead_fp8_tile_major(C.byref(s), o, n, d, None)  # noqa: E731
+    # only row-major FP8 is converted: tile-major or bf16 sources are refused
+    assert call(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, rows, cols, A, A)) == _lib.QWS_ERR_FORMAT
+    assert call(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, rows, cols, A, None)) == _lib.QWS_ERR_FORMAT
+    assert call(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, A, None)) == _lib.QWS_ERR_ARG
+    assert call(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, 48, A, A)) == _lib.QWS_ERR_SHAPE
+    assert call(src, n=need - 1) == _lib.QWS_ERR_WORKSPACE
+    assert call(src, o=far + 8) == _lib.QWS_ERR_ALIGN
+    assert call(src, o=A + 16 * cols) == _lib.QWS_ERR_ARG            # overlaps the source codes
+    assert call(src, o=None) == _lib.QWS_ERR_ARG
+    assert call(src, d=None) == _lib.QWS_ERR_ARG
 
 
 @pytest.mark.parametrize("rows,cols,x,M,status", [
@@ -130,7 +163,7 @@ def test_lmhead_format_tags_refuse_mismatched_heads(lib):
     (10, 2560, None, 1, _lib.QWS_ERR_ARG),
 ])
 def test_lmhead_gemv_validation(lib, rows, cols, x, M, status):
-    d = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, A, A)
+    d = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, rows, cols, A, A)
     assert lib.lmhead_gemv_fp8(C.byref(d), x, M, A, None) == status
 
 
@@ -157,7 +190,7 @@ def test_fp8_codes_bytes(lib):
 
 def test_verify_validation(lib):
     bf = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, 100, 64, A, None))
-    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 100, 64, A, A))
+    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, 100, 64, A, A))
     wsb = lib.lmhead_verify_workspace_bytes(4)
     assert wsb > 0 and lib.lmhead_verify_workspace_bytes(0) == 0 and lib.lmhead_verify_workspace_bytes(5) == 0
     ok = dict(head=fp8, x=A, M=4, draft=A, lg=None, t=A, e=A, n=A, ws=A, wsb=wsb)
@@ -181,8 +214,8 @@ def test_verify_validation(lib):
 
 def test_sample_validation(lib):
     bf = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_BF16, 100, 64, A, None))
-    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 100, 64, A, A))
-    big = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, 262145, 64, A, A))
+    fp8 = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, 100, 64, A, A))
+    big = C.byref(_lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, 262145, 64, A, A))
     wsb = lib.lmhead_verify_workspace_bytes(4)
     ok = dict(head=fp8, x=A, M=4, draft=A, T=0.6, k=29, p=0.95, u=A, lg=A, tok=A, tk=None, e=A, n=A, ws=A, wsb=wsb)
 

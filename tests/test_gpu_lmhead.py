@@ -9,7 +9,7 @@ import quantized_weight_streaming_amd as qws
 import synth
 from oracle import lmhead as OL
 
-from .helpers import assert_close, bf16, check_argmax, fp8_tile_major, say
+from .helpers import assert_close, bf16, check_argmax, f32, fp8_tile_major, say, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,24 @@ def test_quantize_writes_the_tile_major_layout(rows, cols):
     assert got.size == qws.lmhead_fp8_codes_bytes(rows, cols) == (rows + 15) // 16 * 16 * cols
     assert np.array_equal(got, fp8_tile_major(codes))
     assert np.array_equal(qws.fp8_codes_rowmajor(h8).cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (17, 96), (999, 544), (2049, 2560)])
+def test_row_major_codes_converted_to_tiles(rows, cols):
+    """lmhead_fp8_tile_major on the oracle's row-major codes gives the quantiser's bytes and a head
+    whose logits equal the quantised head's bit for bit (and the oracle's within 2e-3)."""
+    say("fp8 row-major -> tiles", rows, cols)
+    w = synth.bf16_normal(9, 0, synth.HEAD, rows + cols, (rows, cols), 0.02)
+    codes, scales = OL.fp8_rowquant(w)
+    h = qws.lmhead_fp8_tile_major(u8(codes), f32(scales))
+    assert h.format == qws.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16
+    assert np.array_equal(h.w.cpu().numpy(), fp8_tile_major(codes))
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    x = synth.token_vectors(9, 1, 4, cols)
+    a = qws.lmhead_gemv_fp8(h, bf16(x)).cpu().numpy()
+    b = qws.lmhead_gemv_fp8(h8, bf16(x)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert_close(a, OL.lmhead_fp8(codes, scales, x), what="converted head")
 
 
 def test_gemv_one_hot_columns():

@@ -13,7 +13,7 @@ def test_fp8_codes_rowmajor_inverts_the_tile_major_layout():
     rng = np.random.default_rng(5)
     for rows, cols in ((1, 32), (17, 96), (40, 544)):
         codes = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
-        d = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE, rows, cols, None, None)
+        d = _lib.LMHeadDesc(_lib.QWS_FMT_FP8_E4M3FN_ROWSCALE_T16, rows, cols, None, None)
         head = qws.LMHead(torch.from_numpy(fp8_tile_major(codes)), None, d)
         assert np.array_equal(qws.fp8_codes_rowmajor(head).numpy(), codes)
 
