@@ -217,9 +217,12 @@ int moe_layer_mxfp4(const qws_moe_layer* layer, int M, int K, void* workspace, s
 int moe_layers_mxfp4(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
                      int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream);
 
-/* Number of bounded in-kernel waits that timed out so far in this workspace (0 when healthy; a
- * timeout means the grid was not co-resident, and that launch's outputs are not valid).
- * Synchronises `stream`; errors_out is host memory. */
+/* Timeouts of bounded in-kernel waits so far in this workspace: a count that only increases (0
+ * when healthy). A wait times out only if the grid was not co-resident; the launch it belongs to
+ * then ends all of its waits and its outputs are not valid. Later launches are not affected: they
+ * wait normally and add to the count only for their own timeouts, so a count that is unchanged
+ * across a launch means that launch's outputs are valid. Synchronises `stream`; errors_out is host
+ * memory. */
 int moe_workspace_errors(const void* workspace, int M, int K, int E, int inter, unsigned* errors_out,
                          qws_stream_t stream);
 

@@ -106,7 +106,9 @@ struct Work {
   unsigned long long* trace;     // NULL, or [n_layers][G][kTracePoints] wall-clock stamps (100 MHz)
   unsigned long long* sync;      // kSyncCounters monotonic counters, kSyncStride apart
   unsigned long long* launches;  // launch counter (each workgroup adds 1 per launch)
-  unsigned* errors;              // count of bounded waits that timed out (sticky)
+  unsigned* errors;              // count of launches' waits that timed out (only ever increases)
+  unsigned long long* abort;     // launch number + 1 of the last launch one of whose waits timed out
+  unsigned long long launch1;    // this launch's number + 1 (set in the kernel)
   // Hand-off buffers. Each 128-byte line is written by one workgroup only: on MI355X an exchange
   // among all workgroups takes ~1.8 us that way and ~3 us when writers share lines.
   unsigned long long* logits;    // [E][kLine] tagged logits: expert e, token m at e*kLine + m (one line per router row)
@@ -157,15 +159,20 @@ __device__ __forceinline__ unsigned long long tagged(uint32_t tag, uint32_t v) {
 }
 __device__ __forceinline__ uint32_t tag_of(unsigned long long v) { return (uint32_t)(v >> 32); }
 
-__device__ __forceinline__ bool gave_up(const Work& w) { return ld_coherent(w.errors) != 0u; }
+// True once a wait of THIS launch has timed out (a timeout of an earlier launch does not count).
+__device__ __forceinline__ bool gave_up(const Work& w) { return ld_coherent(w.abort) == w.launch1; }
 
 // Poll count, error check and back-off of a bounded wait; returns true when the wait must end.
-// Once any wait has timed out (the error count is sticky) every other wait ends at its next check.
+// Once a wait of this launch has timed out, every other wait of the launch ends at its next check;
+// the next launch waits normally again.
 __device__ __forceinline__ bool wait_expired(const Work& w, unsigned& spins) {
   if ((++spins & 255u) == 0) {
     const bool other = gave_up(w);
     if (other || spins > kSpinLimit) {
-      if (!other && (threadIdx.x % kWave) == 0) atomicAdd(w.errors, 1u);
+      if (!other && (threadIdx.x % kWave) == 0) {
+        st_coherent(w.abort, w.launch1);
+        atomicAdd(w.errors, 1u);
+      }
       return true;
     }
   }
@@ -804,7 +811,7 @@ __device__ __forceinline__ Layer desc_from_lds(const unsigned long long* raw) {
 
 template <int M>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
-                                                              int n_layers, Shape sh_arg, Work w) {
+                                                              int n_layers, Shape sh_arg, Work w_arg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ Union un;
   __shared__ int s_idx[kMaxM][kMaxK];
@@ -837,8 +844,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   if (tid < kTracePoints) s_stamp[tid] = 0ull;
   // launch number -> this launch's tag base (every workgroup adds 1 per launch)
   if (tid == 0)
-    s_launch = __hip_atomic_fetch_add(w.launches, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / (unsigned)G;
+    s_launch = __hip_atomic_fetch_add(w_arg.launches, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / (unsigned)G;
   __syncthreads();
+  Work w = w_arg;
+  w.launch1 = uniform_u64(s_launch) + 1ull;
   const uint32_t tag_base = (uint32_t)(s_launch * kTagsPerLaunch);
   if (s_launch > 0 && tag_base == 0) {
     // tags repeat from here on: clear every tagged word (tag 0 is never valid) before any use
@@ -1226,6 +1235,8 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
     w->sync = reinterpret_cast<unsigned long long*>(base);
     w->launches = reinterpret_cast<unsigned long long*>(base + sync);
     w->errors = reinterpret_cast<unsigned*>(base + sync + 128);
+    w->abort = reinterpret_cast<unsigned long long*>(base + sync + 192);
+    w->launch1 = 0;
     w->logits = reinterpret_cast<unsigned long long*>(base + sync + misc);
     w->ytag = reinterpret_cast<unsigned long long*>(base + sync + misc + lg);
     w->done = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt);

@@ -362,3 +362,39 @@ def test_chained_graph_replay():
         seq.run(ws)
         torch.cuda.synchronize()
     assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 0
+
+
+def _error_word_offset(ws: torch.Tensor) -> int:
+    """Byte offset of the timeout count in a fused-layer workspace, found through the ABI: with
+    every 32-bit word of the workspace holding its own index, moe_workspace_errors returns the index
+    of the word it reads."""
+    ws.view(torch.int32).copy_(torch.arange(ws.numel() // 4, dtype=torch.int32, device=ws.device))
+    idx = qws.moe_workspace_errors(ws, 1, 8, 512, 768)
+    ws.zero_()
+    return 4 * idx
+
+
+def test_earlier_timeouts_do_not_end_later_launches():
+    """A timeout recorded by an earlier launch (the count and the give-up word, written here from the
+    host) does not end the waits of a later launch: its outputs equal a healthy workspace's, bit for
+    bit, and it adds nothing to the count. The give-up word is the 64-bit word 64 bytes after the
+    32-bit count, holding the timed-out launch's number + 1; the launch counter (64-bit, 128 bytes
+    before the count) holds the number of workgroups started in earlier launches."""
+    say("stale timeout flag")
+    layer = Layer(12, 0, synth.LayerShape(), 1)
+    ref = _fused(layer).y_f32.clone()
+    ws = qws.moe_layer_workspace(1, 8, 512, 2560, 768, "cuda")
+    off = _error_word_offset(ws)
+    _fused(layer, ws)                              # launch 0
+    torch.cuda.synchronize()
+    started = int(ws[off - 128:off - 120].view(torch.int64).item())
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    assert started == G                            # one workgroup per compute unit, one launch
+    ws[off:off + 4].view(torch.int32).fill_(7)     # seven earlier timeouts
+    ws[off + 64:off + 72].view(torch.int64).fill_(1)   # ... the last of them in launch 0
+    for i in range(3):
+        L = _fused(layer, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(L.y_f32.view(torch.int32), ref.view(torch.int32)), f"launch {i + 1}"
+        assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 7
+        ws[off + 64:off + 72].view(torch.int64).fill_(i + 2)   # as if this launch had timed out
