@@ -313,6 +313,19 @@ int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, 
                              float* logits_out, int* target_out, int* emitted_out, int* n_out,
                              void* workspace, size_t workspace_bytes, qws_stream_t stream);
 
+/* lmhead_verify_greedy_fp8 without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The same two launches and results; the head workgroups' keys go to a 64 KB device array of the
+ * library instead (one per GPU, held until the process ends; its device address is looked up on
+ * the first call on each device). No call allocates or frees memory. Every call on one GPU shares
+ * that array: calls that overlap in time on one GPU (other streams, other threads) race and must
+ * be serialised by the caller. Nothing in it needs clearing: each call writes every key it reads.
+ * Errors: as lmhead_verify_greedy_fp8 (a window of more than 4 positions, which the array could
+ * not hold, is QWS_ERR_SHAPE), plus QWS_ERR_DEVICE if the array's address cannot be found. */
+int lmhead_verify_greedy_fp8_noalloc(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                                     float* logits_out, int* target_out, int* emitted_out, int* n_out,
+                                     qws_stream_t stream);
+
 /* Sampled verification of a speculative window after the FP8 head, for the pages' sampled run
  * (temperature 0.6, top_p 0.95, top_k 29: Netics post, "GSM8K measured a 42.5% throughput gain").
  * Per position m: the logits divided by the temperature, the top_k largest (ties to the lower row;

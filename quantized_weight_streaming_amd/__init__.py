@@ -423,6 +423,25 @@ def lmhead_verify_greedy_fp8(head: LMHead, x: torch.Tensor, draft: torch.Tensor 
     return out
 
 
+def lmhead_verify_greedy_fp8_noalloc(head: LMHead, x: torch.Tensor, draft: torch.Tensor | None,
+                                     logits: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """lmhead_verify_greedy_fp8 with the library's own device scratch instead of a workspace: no
+    allocation on the library's side (outputs come from `out` when given, else are allocated here
+    by torch). Calls that overlap in time on one GPU race."""
+    _need(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = {k: torch.empty(n, dtype=torch.int32, device=dev) for k, n in (("target", M), ("emitted", M), ("n", 1))}
+    if draft is not None and (draft.dtype != torch.int32 or draft.numel() != M - 1 or draft.device != dev):
+        raise ValueError("draft: int32 [M - 1] on the device of x")
+    st = lib().lmhead_verify_greedy_fp8_noalloc(C.byref(head.desc), _p(x), M, None if draft is None else _p(draft),
+                                                None if logits is None else _p(logits), _p(out["target"]),
+                                                _p(out["emitted"]), _p(out["n"]), _stream(dev))
+    check("lmhead_verify_greedy_fp8_noalloc", st)
+    return out
+
+
 def lmhead_verify_sample_fp8(head: LMHead, x: torch.Tensor, draft: torch.Tensor | None, u: torch.Tensor,
                              workspace: torch.Tensor, temperature: float = 0.6, top_k: int = 29, top_p: float = 0.95,
                              logits: torch.Tensor | None = None, topk: bool = False, out: dict | None = None) -> dict:

@@ -74,6 +74,7 @@ SIGNATURES = {
     "lmhead_gemv_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "lmhead_verify_workspace_bytes": (_SZ, [_I]),
     "lmhead_verify_greedy_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_verify_greedy_fp8_noalloc": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P, _P, _P, _P, _P]),
     "lmhead_verify_sample_fp8": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, C.c_float, _I, C.c_float, _P, _P, _P, _P,
                                       _P, _P, _P, _SZ, _P]),
     "lmhead_gemv_bf16": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),

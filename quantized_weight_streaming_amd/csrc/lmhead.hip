@@ -13,6 +13,8 @@
 //    scale multiplies the reduced sum once.
 //  - bf16: one wave per row, 5 x 16 B per lane, x in registers, the next row's loads issued
 //    before the current row is reduced.
+#include <mutex>
+
 #include "head_fp8.hpp"
 
 namespace {
@@ -509,19 +511,23 @@ extern "C" size_t lmhead_verify_workspace_bytes(int M) {
   return verify_keys_bytes(M) + 256;
 }
 
-extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
-                                        float* logits_out, int* target_out, int* emitted_out, int* n_out,
-                                        void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+namespace {
+// Argument checks of the greedy verification (everything but the workspace).
+int check_verify_greedy(const qws_lmhead* head, const void* x_bf16, int M, const int* draft, const int* target_out,
+                        const int* emitted_out, const int* n_out) {
   int st = check_head(head, QWS_FMT_FP8_E4M3FN_ROWSCALE_T16);
   if (st != QWS_OK) return st;
   if (!x_bf16 || !target_out || !emitted_out || !n_out || (M > 1 && !draft)) return QWS_ERR_ARG;
   if (M < 1 || M > 4) return QWS_ERR_SHAPE;
   if (!qws_host::aligned16(x_bf16)) return QWS_ERR_ALIGN;
-  if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
-  if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
-  unsigned long long* keys = static_cast<unsigned long long*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_head_fp8(head, x_bf16, M, logits_out, keys, s);
+  return QWS_OK;
+}
+
+// The two launches of the greedy verification, with the head workgroups' keys in `keys`
+// (kHeadGrid x M words; written by the first launch before the second reads them).
+int launch_verify_greedy(const qws_lmhead* head, const void* x_bf16, int M, const int* draft, float* logits_out,
+                         int* target_out, int* emitted_out, int* n_out, unsigned long long* keys, hipStream_t s) {
+  int st = launch_head_fp8(head, x_bf16, M, logits_out, keys, s);
   if (st != QWS_OK) return st;
   const long long ntiles = (head->rows + 15) / 16;
   const int G = (int)(ntiles < kHeadGrid ? ntiles : kHeadGrid);
@@ -536,6 +542,66 @@ extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf
   }
 #undef QWS_FINISH
   return qws_host::check_launch();
+}
+}  // namespace
+
+extern "C" int lmhead_verify_greedy_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                                        float* logits_out, int* target_out, int* emitted_out, int* n_out,
+                                        void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+  int st = check_verify_greedy(head, x_bf16, M, draft, target_out, emitted_out, n_out);
+  if (st != QWS_OK) return st;
+  if (!workspace || workspace_bytes < lmhead_verify_workspace_bytes(M)) return QWS_ERR_WORKSPACE;
+  if (!qws_host::aligned16(workspace)) return QWS_ERR_ALIGN;
+  return launch_verify_greedy(head, x_bf16, M, draft, logits_out, target_out, emitted_out, n_out,
+                              static_cast<unsigned long long*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Greedy verification without a caller's workspace, for callers that cannot allocate. The keys go
+// to `scratch`, a device array of this library (one per GPU, kept until the process ends). In host
+// code `scratch` names a host-side stand-in, not device memory: its device address is looked up
+// once per device with hipGetSymbolAddress and only that address is used.
+namespace {
+constexpr size_t kScratchBytes = (size_t)kHeadGrid * 4 * 8;   // keys of a 4-position window
+static_assert(kScratchBytes == 65536, "scratch: one 64-bit key per (head workgroup, position)");
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];   // per device: the device address of `scratch`, 0 until looked up
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return qws_host::set_device_error(e);
+  if (dev < 0 || dev >= 64) return QWS_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return qws_host::set_device_error(e);
+    if (!p) return QWS_ERR_DEVICE;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QWS_OK;
+}
+}  // namespace
+
+extern "C" int lmhead_verify_greedy_fp8_noalloc(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
+                                                float* logits_out, int* target_out, int* emitted_out, int* n_out,
+                                                qws_stream_t stream) {
+  int st = check_verify_greedy(head, x_bf16, M, draft, target_out, emitted_out, n_out);
+  if (st != QWS_OK) return st;
+  if ((size_t)kHeadGrid * (size_t)M * 8 > kScratchBytes)
+    return qws_host::set_error_text(QWS_ERR_WORKSPACE, "window larger than the library's verification scratch");
+  void* keys = nullptr;
+  st = scratch_address(&keys);
+  if (st != QWS_OK) return st;
+  return launch_verify_greedy(head, x_bf16, M, draft, logits_out, target_out, emitted_out, n_out,
+                              static_cast<unsigned long long*>(keys), static_cast<hipStream_t>(stream));
 }
 
 extern "C" int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,
