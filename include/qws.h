@@ -409,7 +409,8 @@ int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t strea
  * `bytes` writes, per layer and workgroup, 16 timestamps of the device wall clock (100 MHz,
  * uint64): [0] layer start, [1] x staged, [2] router rows done, [3] shared-expert task done,
  * [4] logits received, [10] selection threshold found, [11] candidates above it compacted,
- * [12] candidate ranks done, [5] selection and union done, [6] routed tasks done, [7] partial
+ * [12] candidate ranks done, [5] selection and union done, [15] the last task's record has
+ * arrived (thread 0; taking it makes wave 0 wait there), [6] routed tasks done, [7] partial
  * sums received (row owners), [13] row sums done, [8] output written, [14] layer-end stores
  * acknowledged, [9] layer barrier passed (sequences that are not chained); layout [n_layers][grid][16]. NULL unregisters.
  * Diagnostics only. */

@@ -382,6 +382,11 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
     d0 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][2], sc), x2, d0);
     d1 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][3], sc), x3, d1);
   }
+  if (w.trace && tid == 0) {
+    // trace only: every piece of this thread's record has arrived (waits for them here, in wave 0)
+    __builtin_amdgcn_s_waitcnt(0);
+    s_stamp[15] = wall_clock64();
+  }
   // lane (g, i) holds rows 4g .. 4g+3 of the row group for token i
   if (i < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + i) * 64 + rg * 16 + 4 * g) = d0 + d1;
   // the next task's (nrec) gate/up pieces load into these registers during this task's down
