@@ -177,10 +177,13 @@ int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* out, size_t out_
  * persistent workgroup per compute unit. Its hand-offs are 64-bit words that carry a 32-bit value
  * with a tag unique to (launch, layer, kind), so a reader polls the data itself. Experts must be
  * packed by moe_pack_mxfp4 (QWS_ERR_FORMAT otherwise). The expert products run on the matrix
- * cores (bf16 operands, exact dequantisation of e2m1 x E8M0; the fp32 SwiGLU activation enters as
- * the exact sum of three bf16 parts; fp32 accumulation), and the down projection is summed per
- * block of 32 activations and then over blocks, so results agree with moe_expert_gemv_mxfp4 to
- * float32 rounding, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
+ * cores: gate/up on the scaled FP4 x FP8 instruction, the e2m1 codes and E8M0 scales as stored
+ * against x written as two E4M3 parts per element with one E8M0 scale per 32 (exact for every
+ * element within 2^13 of its block's largest magnitude, smaller ones rounded at 2^-16 of it);
+ * down on bf16 operands, the fp32 SwiGLU activation entering as the exact sum of three bf16
+ * parts. The instruction's internal accumulation is a little coarser than float32 (about 1e-4 of
+ * one op's largest output, measured), so results agree with moe_expert_gemv_mxfp4 to ~1e-5 of
+ * max|y|, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   const void* x_bf16;         /* [M, H] bf16, ready before the launch                               */

@@ -291,6 +291,69 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
   __syncthreads();
 }
 
+// ------------------------------------------------------------------------------ FP8 activations
+// The gate/up products run on the scaled matrix instruction with FP4 weights (A) and FP8
+// activations (B): v_mfma_scale_f32_16x16x128_f8f6f4 takes 128 k per op in four blocks of 32, each
+// with one E8M0 scale per row of A and per column of B. Measured operand layout on gfx950: lane
+// (g, i) = (lane / 16, lane % 16) supplies block g of A row i as 16 bytes (element 2j in the low
+// nibble of byte j: an MX chunk as stored) and A's scale byte for it; B column i's block b comes
+// from lane groups 2 (b % 2) (elements 0 .. 15 of the block) and 2 (b % 2) + 1 (16 .. 31), in
+// dwords 4 (b / 2) .. +3 of the lane's eight, and B's scale for block b from lane group b; D is as
+// for the bf16 op (lane (g, i): rows 4g .. 4g+3 of column i).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+template <int OPSEL_A>
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(u32x4_t a, u32x4_t b_lo, u32x4_t b_hi, uint32_t scale_a,
+                                                uint32_t scale_b, f32x4_t c) {
+  // an FP4 operand is the low four registers of the tuple; the op never reads the high four
+  const int u = __builtin_nondeterministic_value(0);
+  const i32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], u, u, u, u};
+  const i32x8_t bv = {(int)b_lo[0], (int)b_lo[1], (int)b_lo[2], (int)b_lo[3],
+                      (int)b_hi[0], (int)b_hi[1], (int)b_hi[2], (int)b_hi[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4 /* A: FP4 e2m1 */, 0 /* B: FP8 e4m3 */,
+                                                          OPSEL_A, (int)scale_a, 0, (int)scale_b);
+}
+
+// x (bf16, LDS) -> two E4M3 parts per element for the B operand, written to x8 [2M][H] (row 2m + s
+// = part s of token m) with one E8M0 scale per (row, 32-element block) in xs8 [2M][H/32]. Part 0
+// keeps the top four significant bits of x (the bf16 value with its low four fraction bits
+// cleared), part 1 the low four (exactly x minus part 0). With e the largest bf16 exponent field
+// of the block, part 0 is scaled by 2^(e-134) and part 1 by 2^(e-138) (scale bytes e - 7 and
+// e - 11): both then lie within +-240 and, for every element whose exponent is within 13 of e, are
+// E4M3 values exactly, so x = part 0 + part 1 enters the products exactly; smaller elements are
+// rounded to nearest even at 2^-9 of their part's scale (at most 2^-16 of the block's largest
+// magnitude). Threads t0 .. kThreads-1 take part: 8 lanes per block, 4 elements per lane (one
+// 8-byte read, the block maximum by three lane swaps, two 4-byte writes).
+__device__ __forceinline__ void stage_x8(const uint16_t* xs, uint8_t* x8, uint8_t* xs8, int M, int H, int tid, int t0) {
+  const int nch = H >> 5, j = tid & 7;
+  for (int u = (tid - t0) >> 3; u < M * nch; u += (kThreads - t0) >> 3) {
+    const int m = u / nch, c = u - m * nch;
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(xs + (size_t)m * H + 32 * c + 4 * j);
+    const uint32_t b0 = v[0] & 0xffffu, b1 = v[0] >> 16, b2 = v[1] & 0xffffu, b3 = v[1] >> 16;
+    uint32_t e = max(max((b0 >> 7) & 0xffu, (b1 >> 7) & 0xffu), max((b2 >> 7) & 0xffu, (b3 >> 7) & 0xffu));
+    e = max(e, dpp<0xB1>(e));    // lanes 8k .. 8k+7 share the block: quad swaps, then the half-row mirror
+    e = max(e, dpp<0x4E>(e));
+    e = max(e, dpp<0x141>(e));
+    const int sh = min(max((int)e - 7, 1), 253), sl = min(max((int)e - 11, 1), 253);
+    const float fh = __uint_as_float((uint32_t)(254 - sh) << 23), fl = __uint_as_float((uint32_t)(254 - sl) << 23);
+    float hi[4], lo[4];
+    const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float h = bf16_bits_to_f32(bb[q] & 0xfff0u);
+      hi[q] = h * fh;                               // part 0 / 2^(sh - 127)
+      lo[q] = (bf16_bits_to_f32(bb[q]) - h) * fl;   // part 1 / 2^(sl - 127)
+    }
+    const uint32_t ch = f32x2_to_e4m3x2<true>(hi[2], hi[3], f32x2_to_e4m3x2<false>(hi[0], hi[1], 0u));
+    const uint32_t cl = f32x2_to_e4m3x2<true>(lo[2], lo[3], f32x2_to_e4m3x2<false>(lo[0], lo[1], 0u));
+    *reinterpret_cast<uint32_t*>(x8 + (size_t)(2 * m) * H + 32 * c + 4 * j) = ch;
+    *reinterpret_cast<uint32_t*>(x8 + (size_t)(2 * m + 1) * H + 32 * c + 4 * j) = cl;
+    if (j == 0) {
+      xs8[2 * m * nch + c] = (uint8_t)sh;
+      xs8[(2 * m + 1) * nch + c] = (uint8_t)sl;
+    }
+  }
+}
+
 // Non-temporal 16-byte load of weights that are read once per step.
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);
@@ -351,44 +414,50 @@ __device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
 // k-slice sums of gate/up and the activation parts.
 template <int M>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
-                                             int u, unsigned mask, const uint16_t* xs, float* gu_s,
+                                             int u, unsigned mask, const uint8_t* x8, const uint8_t* xs8, float* gu_s,
                                              unsigned tid, uint32_t tag, const uint8_t* nrec, int line_shared,
                                              int line_routed, bool first, bool last, float (&outv)[kDnTpw]) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
   const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
-  // gate/up: B column i is token i, read from LDS by the lanes of this slot's tokens only (one
-  // exec mask per chunk); other columns are zero. Two accumulators (s even / odd) halve the chain
-  // of dependent MFMAs.
-  const bool xcol = i < M && (M == 1 || ((mask >> i) & 1u));
-  const uint16_t* xrow = xs + min(i, M - 1) * H;
-  f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+  (void)R;
+  // gate/up: FP4 weights x FP8 activations, one scaled op per piece (4 chunks = 128 k). B column i
+  // is part i % 2 of token i / 2 (x8 row i), read from LDS by the lanes of this slot's tokens only;
+  // other columns are zero. Two accumulators (t even / odd) halve the chain of dependent ops.
+  const bool xcol = i < 2 * M && (M == 1 || ((mask >> (i >> 1)) & 1u));
+  const uint8_t* xrow = x8 + (size_t)min(i, 2 * M - 1) * H;
+  const uint8_t* srow = xs8 + min(i, 2 * M - 1) * nch;
+  f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
-    // no branch on the chunk index: a chunk past the row end gets scale 0 and adds zeros
     // chunks past the row end are zero in the record (codes and scales): they add zeros
-    const int c = min(kGuCpk * ks + 4 * t + g, nch - 1);
-    const float sc = e8m0_normal_to_f32(t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu);
-    u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = x0, x2 = x0, x3 = x0;
+    const int cb = kGuCpk * ks + 4 * t;
+    u32x4_t blo = {0u, 0u, 0u, 0u}, bhi = blo;
+    uint32_t bsc = 127u;
     if (xcol) {
-      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow + c * 32);
-      x0 = xp[0];
-      x1 = xp[1];
-      x2 = xp[2];
-      x3 = xp[3];
+      blo = *reinterpret_cast<const u32x4_t*>(xrow + 32 * min(cb + (g >> 1), nch - 1) + 16 * (g & 1));
+      bhi = *reinterpret_cast<const u32x4_t*>(xrow + 32 * min(cb + 2 + (g >> 1), nch - 1) + 16 * (g & 1));
+      bsc = srow[min(cb + g, nch - 1)];
     }
-    d0 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][0], sc), x0, d0);
-    d1 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][1], sc), x1, d1);
-    d0 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][2], sc), x2, d0);
-    d1 = mfma_16x16x32(fp4x8_to_bf16x8(r.p[1 + t][3], sc), x3, d1);
+    const uint32_t asc = t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu;   // this lane's chunk scale
+    d0 = mfma_fp4_fp8<0>(r.p[1 + t], blo, bhi, asc, bsc, d0);
   }
+  const f32x4_t d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // the two parts of token m are columns 2m and 2m + 1: adjacent lanes
+  // (four scalar swaps: the same swap written on the vector's elements in a loop was compiled into
+  // one swap of element 0 added to every element)
+  (void)d1;
+  const float s0 = d0[0], s1 = d0[1], s2 = d0[2], s3 = d0[3];
+  const float t0 = __uint_as_float(dpp<0xB1>(__float_as_uint(s0))), t1 = __uint_as_float(dpp<0xB1>(__float_as_uint(s1)));
+  const float t2 = __uint_as_float(dpp<0xB1>(__float_as_uint(s2))), t3 = __uint_as_float(dpp<0xB1>(__float_as_uint(s3)));
+  const f32x4_t dsum = {s0 + t0, s1 + t1, s2 + t2, s3 + t3};
   if (w.trace && tid == 0) {
     // trace only: every piece of this thread's record has arrived (waits for them here, in wave 0)
     __builtin_amdgcn_s_waitcnt(0);
     s_stamp[15] = wall_clock64();
   }
-  // lane (g, i) holds rows 4g .. 4g+3 of the row group for token i
-  if (i < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + i) * 64 + rg * 16 + 4 * g) = d0 + d1;
+  // lane (g, 2m) holds rows 4g .. 4g+3 of the row group for token m
+  if ((i & 1) == 0 && (i >> 1) < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + (i >> 1)) * 64 + rg * 16 + 4 * g) = dsum;
   // the next task's (nrec) gate/up pieces load into these registers during this task's down
   // projection, its down pieces after it; the down-phase words of piece 0 are kept first
   const uint32_t dn8 = r.p[0][0], dn9 = r.p[0][1], dsw = r.p[0][3];
@@ -839,7 +908,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
   // then the combine's per-wave row sums [waves][M][kLine] fp32
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   uint16_t* wr_s = reinterpret_cast<uint16_t*>(lds + (size_t)M * H * 2);
-  unsigned char* scratch = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
+  uint8_t* x8 = lds + (size_t)M * H * 2 + (size_t)sh.nrw * H * 2;
+  uint8_t* xs8 = x8 + (size_t)2 * M * H;
+  unsigned char* scratch = xs8 + (((size_t)2 * M * (H >> 5) + 15) & ~(size_t)15);
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(scratch);
   float* red = reinterpret_cast<float*>(scratch);
 
@@ -976,6 +1047,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     }
     if (has_next && wave == kWaves - 1 && lane < kDescWords) s_desc[(l + 1) & 1][lane] = next_desc;
     stamp(w, l, 2);
+    // x in FP8 parts for the tasks' gate/up products (published by the next barrier: the shared
+    // task's, or the selection's). With one token wave 0 polls the logits meanwhile, so waves 1 ..
+    // 15 stage x unless this workgroup runs the shared task first.
+    if (tid >= (M == 1 && !shared_task ? kWave : 0)) stage_x8(xs, x8, xs8, M, H, tid, M == 1 && !shared_task ? kWave : 0);
     if (shared_task) {
       // the shared expert needs no routing: its tasks run while the logits are exchanged
       if (tid == 0) {
@@ -988,7 +1063,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       TaskRegs sreg;
       float sout[kDnTpw];
       task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
-      task_compute<M>(sh, w, sreg, un, 0, (1u << M) - 1u, xs, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true, sout);
+      task_compute<M>(sh, w, sreg, un, 0, (1u << M) - 1u, x8, xs8, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true,
+                      sout);
     }
     stamp(w, l, 3);
 
@@ -1033,7 +1109,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           }
           const uint8_t* nrec =
               gn < n_gr ? task_rec(L, sh, un.id[s0 + gn / jg], (gn % jg) * kg + tn, tid) : nullptr;
-          task_compute<M>(sh, w, cur, un, s0 + gi / jg, un.mask[s0 + gi / jg], xs, red, tid, tag_pt, nrec, 0,
+          task_compute<M>(sh, w, cur, un, s0 + gi / jg, un.mask[s0 + gi / jg], x8, xs8, red, tid, tag_pt, nrec, 0,
                           s0 * M * J + gi % jg, t == 0, t == kg - 1, outv);
           if (!nrec) break;
           gi = gn;
@@ -1219,7 +1295,8 @@ size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
   const size_t sel = (size_t)M * (E + kWave + 1) * 8 + (M > 1 ? (size_t)M * E * 4 : 0), gu = (size_t)4 * M * 64 * 4 + M * 4 * 32 * 2;
   const size_t comb = (size_t)kWaves * M * kLine * 4;
   const size_t scratch = sel > comb ? (sel > gu ? sel : gu) : (comb > gu ? comb : gu);
-  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + scratch;
+  const size_t x8 = (size_t)2 * M * H + (((size_t)2 * M * (H / 32) + 15) & ~(size_t)15);   // FP8 parts of x, scales
+  return (size_t)M * H * 2 + (size_t)nrw * H * 2 + x8 + scratch;
 }
 
 // n words rounded up to whole 128-byte lines

@@ -178,8 +178,12 @@ def test_fused_matches_two_call_routing():
     assert torch.equal(idx.cpu(), L.topk_idx.cpu())
     assert torch.equal(w.cpu().view(torch.int32), L.topk_w.cpu().view(torch.int32))
     _, y32 = qws.moe_expert_gemv_mxfp4(_bank(layer), layer.x_t, idx, w)
-    # same arithmetic, different float32 summation order (blocks of 32 activations, then blocks)
-    assert_close(L.y_f32.cpu().numpy(), y32.cpu().numpy(), tol=1e-6, what="fused vs two-call")
+    # the same products in another arithmetic: the fused layer's gate/up runs on the scaled FP4 x FP8
+    # matrix op (x as two exact E4M3 parts), whose internal accumulation of 128 products is less
+    # precise than float32 (measured on MI355X: up to ~8e-5 of one op's largest output), then the
+    # down projection sums per block of 32 activations; 5e-5 of max|y| bounds the difference with
+    # margin (measured 6e-6), far inside the 2e-3 both paths keep against the oracle
+    assert_close(L.y_f32.cpu().numpy(), y32.cpu().numpy(), tol=5e-5, what="fused vs two-call")
 
 
 def test_fused_deterministic_and_workspace_healthy():
