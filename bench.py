@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--no-breakdown", action="store_true", help="skip the per-configuration breakdown")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--agreement", type=int, default=1000, help="x vectors for FP8-vs-bf16 head agreement")
+    p.add_argument("--profile", action="store_true",
+                   help="a short fixed sequence for hardware-counter runs (rocprofv3 --pmc): per kernel two "
+                        "launches, in this order: copy probe, 42-layer launch at M=1, FP8 head M=1, bf16 head "
+                        "M=1, one cold layer at M=1, 42-layer launch at M=4, FP8 head verification M=4; no JSON")
     return p.parse_args()
 
 
@@ -92,8 +96,9 @@ class Flusher:
         self.qws.probe_read(self.buf, self.sink, 4096)
 
 
-def time_cold(fn, dev, iters=50, warm=5, flush=None):
-    """Median / p10 / p90 microseconds of fn() between HIP events, flushing caches before each."""
+def time_cold(fn, dev, iters=100, warm=10, flush=None):
+    """Median / p10 / p90 microseconds of fn() between HIP events, flushing caches before each
+    (outside the event pair): 10 warm-up calls, then 100 timed."""
     import torch
     for _ in range(warm):
         fn()
@@ -114,10 +119,12 @@ class MoeLayer:
     """Device-resident inputs and outputs of one MoE layer, runnable through the fused one-launch
     entry point or through the two-call path (router kernel, then the expert kernels)."""
 
-    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None, packed=None, x=None, keep_canonical=True):
+    def __init__(self, qws, seed, layer, M, dev, bias=None, bank=None, packed=None, x=None, keep_canonical=True,
+                 n_routed=512):
         import torch
         import synth
-        shape = synth.LayerShape()
+        shape = synth.LayerShape(n_routed=n_routed)
+        self.E = n_routed
         # canonical bank: the two-call path; task-major copy: the fused path. Layers that only run
         # fused drop the canonical bank once packed (a 42-layer step then holds ~70 GB, not ~137)
         self.bank_t = bank
@@ -241,6 +248,24 @@ class DecodeStep:
         return {"wall_ms": wall * 1e3, "gpu_ms": gpu_ms, "moe_us_mean": sum(moe_us) / len(moe_us),
                 "head_us_mean": sum(head_us) / len(head_us), "head_us_median": head_us[len(head_us) // 2]}
 
+    def timed_flushed(self, steps, flush):
+        """The same step with the caches flushed before each one, outside its event pair: no byte
+        of the step (router rows, experts, head) can be served from the L2 or the Infinity Cache
+        left warm by the previous step."""
+        import torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for a, b, c in ev:
+            flush()
+            a.record()
+            self.layers_call()
+            b.record()
+            self.head_call()
+            c.record()
+        torch.cuda.synchronize(self.dev)
+        step_ms = sorted(a.elapsed_time(c) for a, _, c in ev)
+        moe_us = sorted(a.elapsed_time(b) * 1e3 for a, b, _ in ev)
+        return {"step_ms_median": step_ms[len(step_ms) // 2], "moe_us_median": moe_us[len(moe_us) // 2]}
+
 
 # ------------------------------------------------------------------------------------ traffic
 def traffic_for(kernel_src: str, name: str):
@@ -265,41 +290,98 @@ def traffic_for(kernel_src: str, name: str):
 
 
 # ------------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(step_bytes_m1, n_layer_sample=3, head_rows=8192):
-    """The oracle as it stands, on a bounded sample of the M = 1 step, extrapolated to one step."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(step_bytes_m1, n_layer_sample=2, head_rows=8192, repeats=3):
+    """The oracle as it stands, on a bounded sample of the M = 1 step (n_layer_sample MoE layers and
+    head_rows FP8 head rows), extrapolated to one step: the median of `repeats` runs with all the
+    cores this process may use, and the same sample on one thread. Input generation is excluded."""
     import numpy as np
     import synth
     from oracle import lmhead as OL
     from oracle import moe as OM
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        blas = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     shape = synth.LayerShape()
-    t_layers = []
+    layers = []
     for l in range(n_layer_sample):
         x = synth.token_vectors(0, l, 1)
         wr = synth.router_weights(0, l, 512)
-        # input generation (not timed): the bytes of the experts this token activates
         idx0, _, _ = OM.route(x, wr, 8)
         experts = {e: synth.expert_np(0, l, e, shape) for e in set(idx0.reshape(-1).tolist()) | {512}}
-        t0 = time.perf_counter()
-        idx, w, _ = OM.route(x, wr, 8)
-        OM.moe_layer(x, idx, w, experts, 512)
-        t_layers.append(time.perf_counter() - t0)
+        layers.append((x, wr, experts))
     wh = synth.head_chunk(0, 0, head_rows)
     codes, scales = OL.fp8_rowquant(wh)
-    x = synth.token_vectors(0, 1000, 1)
-    t0 = time.perf_counter()
-    OL.lmhead_fp8(codes, scales, x)
-    t_head = time.perf_counter() - t0
-    t_step = N_LAYERS * (sum(t_layers) / len(t_layers)) + (157184 / head_rows) * t_head
-    return {"value": round(step_bytes_m1 / t_step / 1e9, 3), "unit": "GB/s", "cores": int(max(1, blas)),
-            "kind": "oracle", "step_s": round(t_step, 3),
+    xh = synth.token_vectors(0, 1000, 1)
+
+    def one_step_s():
+        t_layers = []
+        for x, wr, experts in layers:
+            t0 = time.perf_counter()
+            idx, w, _ = OM.route(x, wr, 8)
+            OM.moe_layer(x, idx, w, experts, 512)
+            t_layers.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        OL.lmhead_fp8(codes, scales, xh)
+        t_head = time.perf_counter() - t0
+        return N_LAYERS * (sum(t_layers) / len(t_layers)) + (157184 / head_rows) * t_head
+
+    with threadpool_limits(limits=cores):
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        runs = sorted(one_step_s() for _ in range(repeats))
+    with threadpool_limits(limits=1):
+        one = one_step_s()
+    t_step = runs[len(runs) // 2]
+    return {"value": round(step_bytes_m1 / t_step / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "step_s": round(t_step, 3), "step_s_runs": [round(r, 3) for r in runs],
+            "value_1_thread": round(step_bytes_m1 / one / 1e9, 3), "step_s_1_thread": round(one, 3),
+            "cpu_model": _cpu_model(), "numpy": np.__version__, "blas_threads": int(blas),
             "sample": f"numpy fp64 oracle on {n_layer_sample} of the 42 MoE layers (route + dequantise the activated "
                       f"experts + SwiGLU + combine) and {head_rows} of 157,184 FP8 head rows at M=1, extrapolated to "
-                      "one step; input generation excluded; cores = BLAS threads (elementwise numpy is 1 thread)"}
+                      f"one step; median of {repeats} runs on the process's {cores} cores (BLAS threads {blas}; "
+                      "elementwise numpy runs on one thread), and one run on one thread; input generation excluded"}
+
+
+def profile_sequence(qws, dev, n_layers):
+    """Two launches of each kernel whose HBM traffic the counters measure, in a fixed order, with the
+    caches flushed before each launch (the counter summaries under profiles/ name the dispatches by
+    this order)."""
+    import torch
+    import synth
+    flush = Flusher(qws, dev)
+    cp_src = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    wh_t = _bf16(synth.head_weights(0), dev)
+    head_bf16 = qws.lmhead_bf16(wh_t)
+    head8 = qws.lmhead_quantize_fp8(wh_t)
+    step = DecodeStep(qws, 1, dev, n_layers, head8)
+    step4 = DecodeStep(qws, 4, dev, n_layers, head8, packed=[L.packed for L in step.layers])
+    one = qws.MoeLayers([step.layers[0].fused])
+    ws1 = qws.moe_layer_workspace(1, K_TOP, 512, 2560, 768, dev)
+    seq = [("probe_copy", lambda: qws.probe_copy(cp_src, cp_dst, 4096)),
+           ("moe_layers_m1", step.layers_call),
+           ("head_fp8_m1", lambda: qws.lmhead_gemv_fp8(head8, step.xh, out=step.logits)),
+           ("head_bf16_m1", lambda: qws.lmhead_gemv_bf16(head_bf16, step.xh, out=step.logits)),
+           ("moe_layer_m1_single", lambda: one.run(ws1)),
+           ("moe_layers_m4", step4.layers_call),
+           ("verify_greedy_m4", step4.head_call)]
+    for name, fn in seq:
+        for _ in range(2):
+            flush()
+            torch.cuda.synchronize(dev)
+            fn()
+            torch.cuda.synchronize(dev)
+        log("profile", name, "done")
+    print("profile sequence:", ", ".join(f"{n} x2" for n, _ in seq), flush=True)
 
 
 # ------------------------------------------------------------------------------------ main
@@ -321,6 +403,9 @@ def main():
     qws.lib()
     qws.selfcheck(dev)
     log("selfcheck ok")
+    if args.profile:
+        profile_sequence(qws, dev, args.layers)
+        return
 
     # LM head: bf16 weights generated on the host, quantised online to FP8 on the device (one-off)
     t0 = time.perf_counter()
@@ -365,6 +450,15 @@ def main():
                  "roofline_lmhead_fp8": roofline_head,
                  "lmhead_quantize_fp8_us": round(quant_us, 1)}
 
+    # the same step with every cache flushed before each step (outside the events): nothing of one
+    # step (router rows, experts, head) is left in the L2 or the Infinity Cache for the next
+    rf = step.timed_flushed(args.steps, flush)
+    breakdown["decode_step_m1_flushed"] = {"ms_median": round(rf["step_ms_median"], 4),
+                                           "moe_us_per_layer": round(rf["moe_us_median"] / args.layers, 3),
+                                           "GBps": round(sb / (rf["step_ms_median"] * 1e-3) / 1e9, 1),
+                                           "back_to_back_ms": round(r["gpu_ms"], 4)}
+    log("decode_step_m1_flushed", breakdown["decode_step_m1_flushed"])
+
     if not args.no_breakdown:
         breakdown["probe_read_ceiling"] = probe_ceiling(qws, dev)
         log("probe", breakdown["probe_read_ceiling"])
@@ -379,16 +473,22 @@ def main():
         lay["moe_layer_m1_seed0"] = MoeLayer(qws, 0, 0, 1, dev, packed=L0.packed)   # canonical again: two-call path
         bank1 = synth.expert_bank_torch(1, 0, synth.LayerShape(), device=dev)
         lay["moe_layer_m1_seed1_zipf"] = MoeLayer(qws, 1, 0, 1, dev, bias=synth.zipf_bias(1, 0, 512), bank=bank1)
+        # the reduced layer: 64 routed experts + shared (one expert-parallel shard's bank at 8 GPUs)
+        bank64 = synth.expert_bank_torch(0, 0, synth.LayerShape(n_routed=64), device=dev)
+        lay["moe_layer_m1_e64"] = MoeLayer(qws, 0, 0, 1, dev, bank=bank64, keep_canonical=False, n_routed=64)
         for reg in synth.REGIMES:
             sets = synth.regime_sets(0, 0, reg, 4, 512)
             lay[f"moe_layer_m4_{reg}"] = MoeLayer(qws, 0, 0, 4, dev, bias=synth.regime_bias(sets, 512), packed=L0.packed,
                                                  keep_canonical=False)
+        wsf64 = qws.moe_layer_workspace(1, K_TOP, 64, 2560, 768, dev)
         for name, Lr in lay.items():
-            t = time_cold(lambda: Lr.run(wsf[Lr.M]), dev, flush=flush)
+            ws_ = wsf64 if Lr.E == 64 else wsf[Lr.M]
+            t = time_cold(lambda: Lr.run(ws_), dev, flush=flush)
             u = Lr.union()
-            b = layer_bytes(u, Lr.M)
+            b = layer_bytes(u, Lr.M, E=Lr.E)
             t.update({"union": u, "bytes": b, "GBps": round(b / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
+            t["frac_of_nt_probe"] = round(t["GBps"] / breakdown["probe_read_nt_ceiling"]["GBps"], 4)
             breakdown[name] = t
             log(name, t)
         L2 = lay["moe_layer_m1_seed0"]
@@ -424,6 +524,7 @@ def main():
             t = time_cold(fn, dev, flush=flush)
             t.update({"bytes": nb, "GBps": round(nb / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
+            t["frac_of_nt_probe"] = round(t["GBps"] / breakdown["probe_read_nt_ceiling"]["GBps"], 4)
             breakdown[name] = t
             log(name, t)
         # run-time specialisation (hipRTC): first call into an empty cache (compile + load), cold
