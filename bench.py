@@ -489,6 +489,8 @@ def main():
             t.update({"union": u, "bytes": b, "GBps": round(b / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
             t["frac_of_nt_probe"] = round(t["GBps"] / breakdown["probe_read_nt_ceiling"]["GBps"], 4)
+            if name == "moe_layer_m1_seed0":
+                t["traffic"] = traffic_for("moe_fused.hip", "moe_layers_kernel_single_layer")
             breakdown[name] = t
             log(name, t)
         L2 = lay["moe_layer_m1_seed0"]
@@ -511,6 +513,9 @@ def main():
         # the sampled run's settings (temperature 0.6, top_k 29, top_p 0.95) with seeded uniforms
         u4 = torch.tensor(np.random.default_rng(1002).random(4), dtype=torch.float32, device=dev)
         sout = qws.lmhead_verify_sample_fp8(head8, x4, draft, u4, ws_v, logits=lg4)
+        head_traffic = {"lmhead_fp8_m1": ("head_fp8.hpp", "head_fp8_kernel"),
+                        "lmhead_bf16_m1": ("lmhead.hip", "gemv_bf16_kernel"),
+                        "lmhead_verify_greedy_fp8_m4": ("head_fp8.hpp", "head_fp8_kernel_verify_m4")}
         for name, fn, nb in (("lmhead_fp8_m1", lambda: qws.lmhead_gemv_fp8(head8, xh, out=step.logits), head_bytes(1)),
                              ("lmhead_bf16_m1", lambda: qws.lmhead_gemv_bf16(head_bf16, xh, out=step.logits),
                               head_bytes(1, fp8=False)),
@@ -525,6 +530,8 @@ def main():
             t.update({"bytes": nb, "GBps": round(nb / (t["median_us"] * 1e-6) / 1e9, 1)})
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
             t["frac_of_nt_probe"] = round(t["GBps"] / breakdown["probe_read_nt_ceiling"]["GBps"], 4)
+            if name in head_traffic:
+                t["traffic"] = traffic_for(*head_traffic[name])
             breakdown[name] = t
             log(name, t)
         # run-time specialisation (hipRTC): first call into an empty cache (compile + load), cold
@@ -605,7 +612,9 @@ def main():
         breakdown["decode_step_m4"] = {"ms_wall": round(r4["wall_ms"], 4), "bytes": b4,
                                        "moe_us_per_layer": round(r4["moe_us_mean"] / args.layers, 3),
                                        "GBps": round(b4 / (r4["wall_ms"] * 1e-3) / 1e9, 1),
-                                       "mean_union": round(float(np.mean([L.union() for L in step4.layers])), 2)}
+                                       "mean_union": round(float(np.mean([L.union() for L in step4.layers])), 2),
+                                       "moe_layers_traffic": traffic_for("moe_fused.hip", "moe_layers_kernel_m4"),
+                                       "moe_layers_algorithmic_bytes": b4 - head_bytes(4)}
         log("decode_step_m4", breakdown["decode_step_m4"])
         del step4
         # speculation priced from these steps: a draft step taken as one MoE layer plus the shared
