@@ -220,6 +220,25 @@ int moe_layer_mxfp4(const qws_moe_layer* layer, int M, int K, void* workspace, s
 int moe_layers_mxfp4(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
                      int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream);
 
+/* W4A8 variants of the two calls above: MXFP4 weights x MXFP8 activations (the baseline's W4A8
+ * recipe: Netics Labs, "Three MoE Inference Optimizations NVIDIA Measured on DGX Spark", section on
+ * the Humming MXFP4 kernels; the pages give no activation format, and the one used is MXFP8 from
+ * the same OCP Microscaling family as the weights). Same arguments, validation, workspace, errors
+ * and outputs as moe_layer_mxfp4 / moe_layers_mxfp4 on the same task-major banks; only the
+ * arithmetic of the experts differs: x is quantised per token and per 32 elements to E4M3 codes
+ * with one E8M0 scale 2^(floor(log2 max|x|) - 8) (OCP MX v1.0 conversion: nearest E4M3 value,
+ * ties to even, magnitudes past 448 clamped; scale exponent at least -127), the gate/up products
+ * run on the scaled FP4 x FP8 instruction, and each expert's SwiGLU output a (float32) is
+ * quantised the same way in blocks of 32 along the intermediate dimension (the down weights' MX
+ * blocks) before the down products, which also run on that instruction. Router, top-K, gate
+ * weights, combine and the shared expert are those of the bf16 layer. An element of a that lies
+ * within float32 rounding of an E4M3 rounding point may round differently than in an exact
+ * computation. */
+int moe_layer_w4a8(const qws_moe_layer* layer, int M, int K, void* workspace, size_t workspace_bytes,
+                   qws_stream_t stream);
+int moe_layers_w4a8(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
+                    int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream);
+
 /* Timeouts of bounded in-kernel waits so far in this workspace: a count that only increases (0
  * when healthy). A wait times out only if the grid was not co-resident; the launch it belongs to
  * then ends all of its waits and its outputs are not valid. Later launches are not affected: they
@@ -418,6 +437,16 @@ int qws_debug_dequant_fp8(const qws_lmhead* head, float* out, qws_stream_t strea
  * acknowledged, [9] layer barrier passed (sequences that are not chained); layout [n_layers][grid][16]. NULL unregisters.
  * Diagnostics only. */
 int qws_debug_trace_buffer(void* buf, size_t bytes);
+
+/* Activations of the W4A8 layer on the current device: while `buf` is registered (device memory,
+ * 16-byte aligned), every moe_layer_w4a8 launch (one layer) whose record fits in `bytes` writes,
+ * for each (expert e, token m) it computes (e = E: the shared expert), the float32 SwiGLU output
+ * a[e][m][k] (k < I) at float offset (e * M + m) * I + k, its E4M3 code at byte offset
+ * (E+1) * M * I * 4 + (e * M + m) * I + k and the block's E8M0 scale byte at byte offset
+ * (E+1) * M * I * 5 + ((e * M + m) * I + k) / 32; needs (E+1) * M * I * 5 + (E+1) * M * I / 32 bytes.
+ * Entries of experts the launch does not run are left as they were. NULL unregisters.
+ * Diagnostics only (the parity test compares these with the oracle's). */
+int qws_debug_w4a8_act_buffer(void* buf, size_t bytes);
 
 /* Streaming-read probe: reads `bytes` (multiple of 16, 16-byte aligned) with 128-bit loads and
  * writes one checksum word per workgroup into sink[0 .. blocks) (blocks <= 65536). Measures the

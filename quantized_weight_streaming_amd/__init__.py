@@ -8,6 +8,7 @@ if libqws.so is missing, the first call raises (there is no CPU fallback).
     y      = moe_expert_gemv_mxfp4(bank, x, idx, w)       # union of experts, SwiGLU, combine
     packed = moe_pack_mxfp4(bank)                         # task-major copy, once per bank
     layer  = moe_layer_mxfp4(MoeLayer(x, w_router, packed, K))   # the whole layer, one launch
+    layer  = moe_layer_w4a8(MoeLayer(x, w_router, packed, K))    # the same with MXFP8 activations
     head   = lmhead_quantize_fp8(w_head_bf16)             # online FP8 head, once
     logits = lmhead_gemv_fp8(head, x)
 """
@@ -27,7 +28,7 @@ from ._lib import (QWS_FMT_BF16, QWS_FMT_FP8_E4M3FN_ROWSCALE, QWS_FMT_MXFP4_E2M1
 
 __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank", "moe_pack_mxfp4", "LMHead",
            "lmhead_bf16",
-           "moe_layer_mxfp4", "moe_layers_mxfp4", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
+           "moe_layer_mxfp4", "moe_layers_mxfp4", "moe_layer_w4a8", "moe_layers_w4a8", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_fp8_codes_bytes", "fp8_codes_rowmajor", "lmhead_gemv_fp8", "lmhead_gemv_bf16",
            "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8", "lmhead_gemv_fp8_rtc", "rtc_compile_head_fp8",
            "rtc_stats", "rtc_reset",
@@ -230,15 +231,25 @@ class MoeLayer:
                                  None if y_f32 is None else y_f32.data_ptr())
 
 
-def moe_layer_mxfp4(layer: MoeLayer, workspace=None) -> MoeLayer:
-    """Router + top-K + experts of one layer in one launch; fills the layer's output tensors."""
+def _run_layer(name: str, layer: MoeLayer, workspace) -> MoeLayer:
     b = layer.bank
     if workspace is None:
         workspace = moe_layer_workspace(layer.M, layer.K, b.n_routed, b.hidden, b.inter, layer.x.device)
-    st = lib().moe_layer_mxfp4(C.byref(layer.desc), layer.M, layer.K, _p(workspace), workspace.numel(),
-                               _stream(layer.x.device))
-    check("moe_layer_mxfp4", st)
+    st = getattr(lib(), name)(C.byref(layer.desc), layer.M, layer.K, _p(workspace), workspace.numel(),
+                              _stream(layer.x.device))
+    check(name, st)
     return layer
+
+
+def moe_layer_mxfp4(layer: MoeLayer, workspace=None) -> MoeLayer:
+    """Router + top-K + experts of one layer in one launch; fills the layer's output tensors."""
+    return _run_layer("moe_layer_mxfp4", layer, workspace)
+
+
+def moe_layer_w4a8(layer: MoeLayer, workspace=None) -> MoeLayer:
+    """moe_layer_mxfp4 with MXFP8 activations: x and each expert's SwiGLU output quantised per 32
+    elements (E4M3 codes, E8M0 scale) before they meet the MXFP4 weights."""
+    return _run_layer("moe_layer_w4a8", layer, workspace)
 
 
 class MoeLayers:
@@ -251,15 +262,20 @@ class MoeLayers:
         raw = torch.frombuffer(bytearray(C.string_at(C.addressof(self.host), C.sizeof(self.host))), dtype=torch.uint8)
         self.dev = raw.to(layers[0].x.device)
 
-    def run(self, workspace) -> None:
+    def run(self, workspace, w4a8: bool = False) -> None:
         L0 = self.layers[0]
-        st = lib().moe_layers_mxfp4(self.host, _p(self.dev), len(self.layers), L0.M, L0.K, _p(workspace),
-                                    workspace.numel(), _stream(L0.x.device))
-        check("moe_layers_mxfp4", st)
+        name = "moe_layers_w4a8" if w4a8 else "moe_layers_mxfp4"
+        st = getattr(lib(), name)(self.host, _p(self.dev), len(self.layers), L0.M, L0.K, _p(workspace),
+                                  workspace.numel(), _stream(L0.x.device))
+        check(name, st)
 
 
 def moe_layers_mxfp4(layers: MoeLayers, workspace) -> None:
     layers.run(workspace)
+
+
+def moe_layers_w4a8(layers: MoeLayers, workspace) -> None:
+    layers.run(workspace, w4a8=True)
 
 
 def moe_workspace_errors(workspace: torch.Tensor, M: int, K: int, E: int, inter: int) -> int:
@@ -488,6 +504,13 @@ def debug_dequant_fp8(head: LMHead) -> torch.Tensor:
     out = torch.empty((head.desc.rows, head.desc.cols), dtype=torch.float32, device=head.w.device)
     check("qws_debug_dequant_fp8", lib().qws_debug_dequant_fp8(C.byref(head.desc), _p(out), _stream(head.w.device)))
     return out
+
+
+def debug_w4a8_act_buffer(buf) -> None:
+    """Register (or, with None, unregister) a uint8 device buffer for the W4A8 layer's activations,
+    codes and scales (layout in include/qws.h); diagnostics only."""
+    check("qws_debug_w4a8_act_buffer",
+          lib().qws_debug_w4a8_act_buffer(_p(buf), 0 if buf is None else buf.numel() * buf.element_size()))
 
 
 def debug_trace_buffer(buf) -> None:

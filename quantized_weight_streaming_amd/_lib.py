@@ -66,6 +66,8 @@ SIGNATURES = {
     "moe_layer_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_layer_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _I, _I, _P, _SZ, _P]),
     "moe_layers_mxfp4": (_I, [C.POINTER(MoeLayerDesc), _P, _I, _I, _I, _P, _SZ, _P]),
+    "moe_layer_w4a8": (_I, [C.POINTER(MoeLayerDesc), _I, _I, _P, _SZ, _P]),
+    "moe_layers_w4a8": (_I, [C.POINTER(MoeLayerDesc), _P, _I, _I, _I, _P, _SZ, _P]),
     "moe_workspace_errors": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_uint), _P]),
     "lmhead_bf16_desc": (_I, [_P, _LL, _LL, C.POINTER(LMHeadDesc)]),
     "lmhead_quantize_fp8": (_I, [_P, _LL, _LL, _P, _P, C.POINTER(LMHeadDesc), _P]),
@@ -88,6 +90,7 @@ SIGNATURES = {
     "qws_probe_read_nt": (_I, [_P, _SZ, _P, _I, _P]),
     "qws_probe_copy": (_I, [_P, _P, _SZ, _I, _P]),
     "qws_debug_trace_buffer": (_I, [_P, _SZ]),
+    "qws_debug_w4a8_act_buffer": (_I, [_P, _SZ]),
 }
 
 _lib = None

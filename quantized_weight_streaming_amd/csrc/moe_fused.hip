@@ -109,6 +109,8 @@ struct Work {
   unsigned* errors;              // count of launches' waits that timed out (only ever increases)
   unsigned long long* abort;     // launch number + 1 of the last launch one of whose waits timed out
   unsigned long long launch1;    // this launch's number + 1 (set in the kernel)
+  float* act;                    // NULL, or the W4A8 activations of a one-layer launch (diagnostics):
+                                 // a [E+1][M][I] fp32, then codes [E+1][M][I] u8, then scale bytes [E+1][M][I/32]
   // Hand-off buffers. Each 128-byte line is written by one workgroup only: on MI355X an exchange
   // among all workgroups takes ~1.8 us that way and ~3 us when writers share lines.
   unsigned long long* logits;    // [E][kLine] tagged logits: expert e, token m at e*kLine + m (one line per router row)
@@ -313,6 +315,13 @@ __device__ __forceinline__ f32x4_t mfma_fp4_fp8(u32x4_t a, u32x4_t b_lo, u32x4_t
                                                           OPSEL_A, (int)scale_a, 0, (int)scale_b);
 }
 
+// A matrix instruction takes its operands from every lane of the wave, so it must run with all
+// lanes enabled. When its result is used only under a lane condition (a store by some lanes), the
+// compiler sinks the scaled instruction into that branch, where the disabled lanes supply no
+// operands (observed: only the rows of the enabled lanes came out right). An empty asm statement
+// that takes the result in place keeps the instruction where it is written.
+__device__ __forceinline__ void mfma_result(f32x4_t& d) { asm volatile("" : "+v"(d)); }
+
 // x (bf16, LDS) -> two E4M3 parts per element for the B operand, written to x8 [2M][H] (row 2m + s
 // = part s of token m) with one E8M0 scale per (row, 32-element block) in xs8 [2M][H/32]. Part 0
 // keeps the top four significant bits of x (the bf16 value with its low four fraction bits
@@ -354,6 +363,33 @@ __device__ __forceinline__ void stage_x8(const uint16_t* xs, uint8_t* x8, uint8_
   }
 }
 
+// x (bf16, LDS) -> MXFP8 for the W4A8 layer: E4M3 codes in x8 [M][H] (row m = token m) and one
+// E8M0 scale per (token, 32-element block) in xs8 [M][H/32], by the OCP MX conversion: with e the
+// largest bf16 exponent field of the block, the scale is 2^(e - 127 - 8) (byte e - 8, at least 0:
+// the smallest E8M0 scale), and each element is x / scale (exact: a power of two) rounded to the
+// nearest E4M3 value, ties to even, magnitudes past 448 clamped to it. Threads t0 .. kThreads-1
+// take part: 8 lanes per block, 4 elements per lane.
+__device__ __forceinline__ void stage_x8_mx(const uint16_t* xs, uint8_t* x8, uint8_t* xs8, int M, int H, int tid,
+                                            int t0) {
+  const int nch = H >> 5, j = tid & 7;
+  for (int u = (tid - t0) >> 3; u < M * nch; u += (kThreads - t0) >> 3) {
+    const int m = u / nch, c = u - m * nch;
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(xs + (size_t)m * H + 32 * c + 4 * j);
+    const uint32_t b0 = v[0] & 0xffffu, b1 = v[0] >> 16, b2 = v[1] & 0xffffu, b3 = v[1] >> 16;
+    uint32_t e = max(max((b0 >> 7) & 0xffu, (b1 >> 7) & 0xffu), max((b2 >> 7) & 0xffu, (b3 >> 7) & 0xffu));
+    e = max(e, dpp<0xB1>(e));
+    e = max(e, dpp<0x4E>(e));
+    e = max(e, dpp<0x141>(e));
+    const uint32_t sb = e >= 8u ? e - 8u : 0u;
+    const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb): exact, normal for sb <= 246
+    const uint32_t code = f32x2_to_e4m3x2<true>(bf16_bits_to_f32(b2) * inv, bf16_bits_to_f32(b3) * inv,
+                                                f32x2_to_e4m3x2<false>(bf16_bits_to_f32(b0) * inv,
+                                                                       bf16_bits_to_f32(b1) * inv, 0u));
+    *reinterpret_cast<uint32_t*>(x8 + (size_t)m * H + 32 * c + 4 * j) = code;
+    if (j == 0) xs8[m * nch + c] = (uint8_t)sb;
+  }
+}
+
 // Non-temporal 16-byte load of weights that are read once per step.
 __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const QWS_GLOBAL u32x4_t*)p);
@@ -380,6 +416,9 @@ __device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
 constexpr int kGuCpk = 4 * kGuCpl;            // chunks of a row per k-slice: H <= 4 * 20 * 32
 constexpr int kDnTpw = kHMax / 16 / kWaves;   // down-projection row tiles (16 rows) per wave
 constexpr int kPieces = 8;                    // 16-byte pieces per lane of a task record
+// a lane's down sums kept across a task group: 10 tiles (bf16 down) or 3 ops x up to 4 tokens (W4A8)
+template <bool A8>
+constexpr int kOutv = A8 ? 12 : kDnTpw;
 // At M = 1 the shared expert's J tasks run before selection on the last J workgroups (the routed
 // tasks leave them idle). With more tokens the union needs most workgroups for several tasks, so
 // the shared expert joins the grouped task pool after selection instead.
@@ -410,23 +449,27 @@ __device__ __forceinline__ void task_load(const uint8_t* rec, TaskRegs& r) {
 // Computes task (slot u: tokens in `mask` (un.mask[u]), pairs un.pair0[u] + rank, gate weights un.w[u][m],
 // block j) from its loaded registers, and stores
 // partial[p][j][row] = w * sum_k W_down[row][32j+k] * a[k] for every row, tagged, at the row's
-// offset in its owner's region. gu_s (LDS: 4 x M x 64 floats, then M x 4 x 32 bf16) takes the
-// k-slice sums of gate/up and the activation parts.
-template <int M>
+// offset in its owner's region. gu_s (LDS: 4 x M x 64 floats, then the activations) takes the
+// k-slice sums of gate/up and the activations: M x 4 x 32 bf16 parts, or for the W4A8 layer (A8)
+// M x 32 E4M3 codes and M scale bytes.
+template <int M, bool A8>
 __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, TaskRegs& r, const Union& un,
                                              int u, unsigned mask, const uint8_t* x8, const uint8_t* xs8, float* gu_s,
                                              unsigned tid, uint32_t tag, const uint8_t* nrec, int line_shared,
-                                             int line_routed, bool first, bool last, float (&outv)[kDnTpw]) {
+                                             int line_routed, bool first, bool last, float (&outv)[kOutv<A8>],
+                                             int jblk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & (kWave - 1);
   const int g = lane >> 4, i = lane & 15, rg = wave >> 2, ks = wave & 3;
   const int H = sh.H, nch = H >> 5, J = sh.I / kBlk, R = sh.R;
   (void)R;
   // gate/up: FP4 weights x FP8 activations, one scaled op per piece (4 chunks = 128 k). B column i
-  // is part i % 2 of token i / 2 (x8 row i), read from LDS by the lanes of this slot's tokens only;
-  // other columns are zero. Two accumulators (t even / odd) halve the chain of dependent ops.
-  const bool xcol = i < 2 * M && (M == 1 || ((mask >> (i >> 1)) & 1u));
-  const uint8_t* xrow = x8 + (size_t)min(i, 2 * M - 1) * H;
-  const uint8_t* srow = xs8 + min(i, 2 * M - 1) * nch;
+  // is x8 row i, read from LDS by the lanes of this slot's tokens only; other columns are zero. The
+  // bf16 layer stages x as two parts per token (row i = part i % 2 of token i / 2), the W4A8 layer
+  // as one (row i = token i).
+  constexpr int kRows = A8 ? M : 2 * M;
+  const bool xcol = i < kRows && (M == 1 || ((mask >> (A8 ? i : i >> 1)) & 1u));
+  const uint8_t* xrow = x8 + (size_t)min(i, kRows - 1) * H;
+  const uint8_t* srow = xs8 + min(i, kRows - 1) * nch;
   f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t = 0; t < kGuCpl; ++t) {
@@ -442,110 +485,206 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
     const uint32_t asc = t < 4 ? (r.p[0][2] >> (8 * t)) & 0xffu : r.p[0][3] & 0xffu;   // this lane's chunk scale
     d0 = mfma_fp4_fp8<0>(r.p[1 + t], blo, bhi, asc, bsc, d0);
   }
-  const f32x4_t d1 = {0.0f, 0.0f, 0.0f, 0.0f};
-  // the two parts of token m are columns 2m and 2m + 1: adjacent lanes
-  // (four scalar swaps: the same swap written on the vector's elements in a loop was compiled into
-  // one swap of element 0 added to every element)
-  (void)d1;
-  const float s0 = d0[0], s1 = d0[1], s2 = d0[2], s3 = d0[3];
-  const float t0 = __uint_as_float(dpp<0xB1>(__float_as_uint(s0))), t1 = __uint_as_float(dpp<0xB1>(__float_as_uint(s1)));
-  const float t2 = __uint_as_float(dpp<0xB1>(__float_as_uint(s2))), t3 = __uint_as_float(dpp<0xB1>(__float_as_uint(s3)));
-  const f32x4_t dsum = {s0 + t0, s1 + t1, s2 + t2, s3 + t3};
+  mfma_result(d0);
+  f32x4_t dsum = d0;
+  if constexpr (!A8) {
+    // the two parts of token m are columns 2m and 2m + 1: adjacent lanes
+    // (four scalar swaps: the same swap written on the vector's elements in a loop was compiled into
+    // one swap of element 0 added to every element)
+    const float s0 = d0[0], s1 = d0[1], s2 = d0[2], s3 = d0[3];
+    const float t0 = __uint_as_float(dpp<0xB1>(__float_as_uint(s0))), t1 = __uint_as_float(dpp<0xB1>(__float_as_uint(s1)));
+    const float t2 = __uint_as_float(dpp<0xB1>(__float_as_uint(s2))), t3 = __uint_as_float(dpp<0xB1>(__float_as_uint(s3)));
+    dsum = f32x4_t{s0 + t0, s1 + t1, s2 + t2, s3 + t3};
+  }
   if (w.trace && tid == 0) {
     // trace only: every piece of this thread's record has arrived (waits for them here, in wave 0)
     __builtin_amdgcn_s_waitcnt(0);
     s_stamp[15] = wall_clock64();
   }
-  // lane (g, 2m) holds rows 4g .. 4g+3 of the row group for token m
-  if ((i & 1) == 0 && (i >> 1) < M) *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + (i >> 1)) * 64 + rg * 16 + 4 * g) = dsum;
+  // lane (g, 2m) (bf16 layer) or (g, m) (W4A8) holds rows 4g .. 4g+3 of the row group for token m
+  if (A8 ? i < M : ((i & 1) == 0 && (i >> 1) < M))
+    *reinterpret_cast<f32x4_t*>(gu_s + (ks * M + (A8 ? i : i >> 1)) * 64 + rg * 16 + 4 * g) = dsum;
   // the next task's (nrec) gate/up pieces load into these registers during this task's down
   // projection, its down pieces after it; the down-phase words of piece 0 are kept first
   const uint32_t dn8 = r.p[0][0], dn9 = r.p[0][1], dsw = r.p[0][3];
+  u32x4_t dq0 = {0u, 0u, 0u, 0u}, dq1 = dq0;
+  if constexpr (A8) {
+    dq0 = r.p[6];
+    dq1 = r.p[7];
+  }
   if (nrec) task_load<0, kPieces - 2>(nrec, r);
   __syncthreads();
 
-  // a = silu(gate) * up in fp32, once per (token, activation), split exactly into three bf16 parts
-  // (hi + mid + lo, each truncated from the remainder), so the down products below stay exact fp32
-  // products of a. a_s holds them as the down MFMA's A rows: row 4m + s = part s of token m (s = 3
-  // and tokens outside the slot: zero), 32 activations each.
-  uint16_t* a_s = reinterpret_cast<uint16_t*>(gu_s + 4 * M * 64);
-  if (tid < 32 * M) {
-    const int am = tid >> 5, k = tid & 31;
-    const float* gp = gu_s + am * 64 + k;
-    float gate = gp[0], up = gp[32];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) {
-      gate += gp[q * M * 64];
-      up += gp[q * M * 64 + 32];
-    }
-    const bool in = M == 1 || ((mask >> am) & 1u);
-    const float av = in ? silu(gate) * up : 0.0f;
-    const float hi = __uint_as_float(__float_as_uint(av) & 0xffff0000u);
-    const float r1 = av - hi;
-    const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
-    const float r2 = r1 - mid;
-    uint16_t* ap = a_s + am * 4 * 32 + k;
-    ap[0] = (uint16_t)(__float_as_uint(hi) >> 16);
-    ap[32] = (uint16_t)(__float_as_uint(mid) >> 16);
-    ap[64] = (uint16_t)(__float_as_uint(r2) >> 16);
-    ap[96] = 0;
-  }
-  __syncthreads();
-
-  // down: A = the activation parts (lane (g, n): row n = 4m + s, k = 8g .. 8g+7), B = 16 down rows
-  // of the block (column n = tile row n); lane (g, n) of D then holds token g's three parts of
-  // tile row n.
   const int n = lane & 15;
-  const u32x4_t ab = n < 4 * M ? *reinterpret_cast<const u32x4_t*>(a_s + n * 32 + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
-  // D lane (g, n) holds token g's three parts of tile row n. With fewer than four tokens the D
-  // rows of absent tokens are empty, so the results of T = 4 / MP tiles are gathered into one
-  // register first (MP = M rounded up to a power of two): lane (g, n) then holds token g % MP of
-  // tile slot g / MP, and one store instruction per T tiles has every row of lanes busy.
-  constexpr int MP = M == 1 ? 1 : (M == 2 ? 2 : 4);
-  constexpr int T = 4 / MP;
-  const int mt = g % MP;
-  const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
-  const float wt = un.w[u][min(mt, M - 1)];
-  const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
+  constexpr int MP = M == 1 ? 1 : (M == 2 ? 2 : 4);   // M rounded up to a power of two
   // partial line of (pair pm, this task's block or block group): at M = 1 the shared slot's pairs
   // (run early) come first with one line per block, then the other pairs with one line per group
-  const int nsm = kEarlyShared<M> && sh.has_shared ? M : 0;
   // (a line is one row-contiguous vector of H tagged words: a store of 16 rows fills a 128-byte
   // line of memory, and a row owner reads its R consecutive words of every line)
-  unsigned long long* pdst = w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
+  const int nsm = kEarlyShared<M> && sh.has_shared ? M : 0;
   const int ntile = H >> 4;
+  if constexpr (A8) {
+    // a = silu(gate) * up in fp32, then MXFP8 per token: the block of 32 is this task's (the down
+    // weights' MX block), its scale 2^(e - 127 - 8) for the largest exponent field e of the 32
+    // (byte e - 8, at least 0), each code the nearest E4M3 value of a / scale (ties to even,
+    // clamped at 448). Lanes 32m .. 32m+31 hold token m's activations.
+    uint8_t* a8 = reinterpret_cast<uint8_t*>(gu_s + 4 * M * 64);   // [M][32] codes, then [M] scale bytes
+    if (tid < 32 * M) {
+      const int am = tid >> 5, k = tid & 31;
+      const float* gp = gu_s + am * 64 + k;
+      float gate = gp[0], up = gp[32];
 #pragma unroll
-  for (int q0 = 0; q0 < kDnTpw; q0 += T) {
-    float vt[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int q = q0 + t;
-      if (q < kDnTpw) {
-        // this lane's down scale (tile q, row n) is held by lane n + 16 (q / 3), in byte
-        // 13 + q % 3 of its first piece
-        const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
-        const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : (q == 8 ? dn8 : dn9);
-        const float dsc = e8m0_normal_to_f32((sw >> (8 + 8 * (q % 3))) & 0xffu);
-        const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, dsc), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-        vt[t] = (dd[0] + dd[1]) + dd[2];
-      } else {
-        vt[t] = 0.0f;
+      for (int q = 1; q < 4; ++q) {
+        gate += gp[q * M * 64];
+        up += gp[q * M * 64 + 32];
+      }
+      const bool in = M == 1 || ((mask >> am) & 1u);
+      const float av = in ? silu(gate) * up : 0.0f;
+      uint32_t e = (__float_as_uint(av) >> 23) & 0xffu;
+      e = max(e, dpp<0xB1>(e));    // lanes 8k .. 8k+7
+      e = max(e, dpp<0x4E>(e));
+      e = max(e, dpp<0x141>(e));
+      e = max(e, dpp<0x140>(e));   // row mirror: lanes 16k .. 16k+15
+      const auto pr = __builtin_amdgcn_permlane16_swap(e, e, false, false);   // rows 2k and 2k+1
+      e = max(pr[0], pr[1]);
+      const uint32_t sb = e >= 8u ? e - 8u : 0u;
+      const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb)
+      const uint8_t code = (uint8_t)(f32x2_to_e4m3x2<false>(av * inv, 0.0f, 0u) & 0xffu);
+      a8[am * 32 + k] = code;
+      if (k == 0) a8[kMaxM * 32 + am] = (uint8_t)sb;
+      if (w.act && in) {
+        // diagnostics: this token's activation, code and scale of expert un.id[u], block jblk
+        const size_t na = (size_t)(sh.E + 1) * M * sh.I, at = ((size_t)un.id[u] * M + am) * sh.I + kBlk * jblk + k;
+        w.act[at] = av;
+        reinterpret_cast<uint8_t*>(w.act + na)[at] = code;
+        if (k == 0) reinterpret_cast<uint8_t*>(w.act + na)[na + at / kBlk] = (uint8_t)sb;
       }
     }
-    float v = vt[0];
-    if constexpr (T == 2) {
-      v = __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[1]), false, false)[0]);
-    } else if constexpr (T == 4) {
-      const uint32_t lo = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[2]), false, false)[0];
-      const uint32_t hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[1]), __float_as_uint(vt[3]), false, false)[0];
-      v = __uint_as_float(__builtin_amdgcn_permlane16_swap(lo, hi, false, false)[0]);
+    __syncthreads();
+
+    // down on the scaled instruction, 64 rows per op: A block b = 16-row tile 4Q + b of this
+    // wave's tiles w + 16 q (q < 10: ops Q = 0, 1 take q 0 .. 7, op 2 takes q 8, 9 in blocks 0, 1),
+    // row i, the task's 32 codes; B column n = token slot c = n / 4 and tile slot b = n % 4 holds
+    // token c % MP's 32 codes in block b and zeros elsewhere, so D column n = tile b's 16 rows for
+    // that token. The record gives lane (g, n) word g (codes 8g .. 8g+7) of row n of each tile;
+    // two lane-group swaps per register pair turn four such words into one row's 16 bytes.
+    const int c = n >> 2, bq = n & 3, mt = c % MP;
+    const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const u32x4_t av16 = tok ? *reinterpret_cast<const u32x4_t*>(a8 + min(mt, M - 1) * 32 + 16 * (g & 1)) : zero;
+    const u32x4_t blo = bq == (g >> 1) ? av16 : zero, bhi = bq == 2 + (g >> 1) ? av16 : zero;
+    const uint32_t bsc = a8[kMaxM * 32 + min(mt, M - 1)];
+    const float wt = un.w[u][min(mt, M - 1)];
+    const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
+    unsigned long long* pdst =
+        w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
+    constexpr int D = 4 / MP;   // copies of each token's column group
+    const int dup = c / MP;
+#pragma unroll
+    for (int Q = 0; Q < 3; ++Q) {
+      uint32_t v0 = Q == 0 ? dq0[0] : (Q == 1 ? dq1[0] : dn8), v1 = Q == 0 ? dq0[1] : (Q == 1 ? dq1[1] : dn9);
+      uint32_t v2 = Q == 0 ? dq0[2] : (Q == 1 ? dq1[2] : 0u), v3 = Q == 0 ? dq0[3] : (Q == 1 ? dq1[3] : 0u);
+      // 4 x 4 transpose of (lane group, register): register t of group g = word g of tile 4Q + t
+      const auto p02 = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+      const auto p13 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+      const auto p01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+      const auto p23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+      const u32x4_t arow = {p01[0], p01[1], p23[0], p23[1]};   // group b: words 0 .. 3 of tile 4Q + b, row n
+      // this lane's A scale (tile q = 4Q + g, row n) is held by lane n + 16 (q / 3), in byte
+      // 1 + q % 3 of its first piece's last word
+      const int q = min(4 * Q + g, kDnTpw - 1);
+      const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
+      const uint32_t asc = (sw >> (8 + 8 * (q % 3))) & 0xffu;
+      f32x4_t dd = mfma_fp4_fp8<0>(arow, blo, bhi, asc, bsc, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      mfma_result(dd);
+      // lane (g, n) holds rows 4g .. 4g+3 of tile 4Q + bq for token mt: it stores rows 4g + dup + D s
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+        const int el = dup + D * t;
+        const float v = el == 0 ? dd[0] : (el == 1 ? dd[1] : (el == 2 ? dd[2] : dd[3]));
+        outv[Q * MP + t] = first ? v : outv[Q * MP + t] + v;
+        const int qt = 4 * Q + bq, rt = wave + kWaves * qt;
+        if (last && tok && qt < kDnTpw && rt < ntile)
+          st_coherent(pdst + rt * 16 + 4 * g + el, tagged(tag, __float_as_uint(wt * outv[Q * MP + t])));
+      }
     }
-    // a workgroup's tasks of one group (same slot, consecutive blocks) add up in registers and
-    // store once, after the last
-    outv[q0 / T] = first ? v : outv[q0 / T] + v;
-    const int q = q0 + g / MP, rt = wave + kWaves * q;
-    if (last && tok && q < kDnTpw && rt < ntile)
-      st_coherent(pdst + rt * 16 + n, tagged(tag, __float_as_uint(wt * outv[q0 / T])));
+  } else {
+    // a = silu(gate) * up in fp32, once per (token, activation), split exactly into three bf16 parts
+    // (hi + mid + lo, each truncated from the remainder), so the down products below stay exact fp32
+    // products of a. a_s holds them as the down MFMA's A rows: row 4m + s = part s of token m (s = 3
+    // and tokens outside the slot: zero), 32 activations each.
+    uint16_t* a_s = reinterpret_cast<uint16_t*>(gu_s + 4 * M * 64);
+    if (tid < 32 * M) {
+      const int am = tid >> 5, k = tid & 31;
+      const float* gp = gu_s + am * 64 + k;
+      float gate = gp[0], up = gp[32];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        gate += gp[q * M * 64];
+        up += gp[q * M * 64 + 32];
+      }
+      const bool in = M == 1 || ((mask >> am) & 1u);
+      const float av = in ? silu(gate) * up : 0.0f;
+      const float hi = __uint_as_float(__float_as_uint(av) & 0xffff0000u);
+      const float r1 = av - hi;
+      const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+      const float r2 = r1 - mid;
+      uint16_t* ap = a_s + am * 4 * 32 + k;
+      ap[0] = (uint16_t)(__float_as_uint(hi) >> 16);
+      ap[32] = (uint16_t)(__float_as_uint(mid) >> 16);
+      ap[64] = (uint16_t)(__float_as_uint(r2) >> 16);
+      ap[96] = 0;
+    }
+    __syncthreads();
+
+    // down: A = the activation parts (lane (g, n): row n = 4m + s, k = 8g .. 8g+7), B = 16 down rows
+    // of the block (column n = tile row n); lane (g, n) of D then holds token g's three parts of
+    // tile row n.
+    const u32x4_t ab = n < 4 * M ? *reinterpret_cast<const u32x4_t*>(a_s + n * 32 + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+    // D lane (g, n) holds token g's three parts of tile row n. With fewer than four tokens the D
+    // rows of absent tokens are empty, so the results of T = 4 / MP tiles are gathered into one
+    // register first: lane (g, n) then holds token g % MP of tile slot g / MP, and one store
+    // instruction per T tiles has every row of lanes busy.
+    constexpr int T = 4 / MP;
+    const int mt = g % MP;
+    const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
+    const float wt = un.w[u][min(mt, M - 1)];
+    const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
+    unsigned long long* pdst =
+        w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
+#pragma unroll
+    for (int q0 = 0; q0 < kDnTpw; q0 += T) {
+      float vt[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int q = q0 + t;
+        if (q < kDnTpw) {
+          // this lane's down scale (tile q, row n) is held by lane n + 16 (q / 3), in byte
+          // 13 + q % 3 of its first piece
+          const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
+          const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : (q == 8 ? dn8 : dn9);
+          const float dsc = e8m0_normal_to_f32((sw >> (8 + 8 * (q % 3))) & 0xffu);
+          const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, dsc), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+          vt[t] = (dd[0] + dd[1]) + dd[2];
+        } else {
+          vt[t] = 0.0f;
+        }
+      }
+      float v = vt[0];
+      if constexpr (T == 2) {
+        v = __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[1]), false, false)[0]);
+      } else if constexpr (T == 4) {
+        const uint32_t lo = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[2]), false, false)[0];
+        const uint32_t hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[1]), __float_as_uint(vt[3]), false, false)[0];
+        v = __uint_as_float(__builtin_amdgcn_permlane16_swap(lo, hi, false, false)[0]);
+      }
+      // a workgroup's tasks of one group (same slot, consecutive blocks) add up in registers and
+      // store once, after the last
+      outv[q0 / T] = first ? v : outv[q0 / T] + v;
+      const int q = q0 + g / MP, rt = wave + kWaves * q;
+      if (last && tok && q < kDnTpw && rt < ntile)
+        st_coherent(pdst + rt * 16 + n, tagged(tag, __float_as_uint(wt * outv[q0 / T])));
+    }
   }
   if (nrec) task_load<kPieces - 2, kPieces>(nrec, r);
   __syncthreads();  // gu_s is rewritten by the next task
@@ -883,7 +1022,7 @@ __device__ __forceinline__ Layer desc_from_lds(const unsigned long long* raw) {
   return to_layer(d);
 }
 
-template <int M>
+template <int M, bool A8>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
                                                               int n_layers, Shape sh_arg, Work w_arg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -1050,10 +1189,14 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     // x in FP8 parts for the tasks' gate/up products (published by the next barrier: the shared
     // task's, or the selection's). With one token wave 0 polls the logits meanwhile, so waves 1 ..
     // 15 stage x unless this workgroup runs the shared task first.
-    if (tid >= (M == 1 && !shared_task ? kWave : 0)) stage_x8(xs, x8, xs8, M, H, tid, M == 1 && !shared_task ? kWave : 0);
+    if (tid >= (M == 1 && !shared_task ? kWave : 0)) {
+      if constexpr (A8) stage_x8_mx(xs, x8, xs8, M, H, tid, M == 1 && !shared_task ? kWave : 0);
+      else stage_x8(xs, x8, xs8, M, H, tid, M == 1 && !shared_task ? kWave : 0);
+    }
     if (shared_task) {
       // the shared expert needs no routing: its tasks run while the logits are exchanged
       if (tid == 0) {
+        un.id[0] = E;
         un.mask[0] = (1u << M) - 1u;
         un.pair0[0] = 0;
 #pragma unroll
@@ -1061,10 +1204,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       TaskRegs sreg;
-      float sout[kDnTpw];
+      float sout[kOutv<A8>];
       task_load<0, kPieces>(task_rec(L, sh, E, b - (G - J), tid), sreg);
-      task_compute<M>(sh, w, sreg, un, 0, (1u << M) - 1u, x8, xs8, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true,
-                      sout);
+      task_compute<M, A8>(sh, w, sreg, un, 0, (1u << M) - 1u, x8, xs8, red, tid, tag_pt, nullptr, b - (G - J), 0, true, true,
+                          sout, b - (G - J));
     }
     stamp(w, l, 3);
 
@@ -1098,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       int gi = b;
       if (gi < n_gr) {
         TaskRegs cur;
-        float outv[kDnTpw];
+        float outv[kOutv<A8>];
         int t = 0;
         task_load<0, kPieces>(task_rec(L, sh, un.id[s0 + gi / jg], (gi % jg) * kg, tid), cur);
         for (;;) {
@@ -1109,8 +1252,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           }
           const uint8_t* nrec =
               gn < n_gr ? task_rec(L, sh, un.id[s0 + gn / jg], (gn % jg) * kg + tn, tid) : nullptr;
-          task_compute<M>(sh, w, cur, un, s0 + gi / jg, un.mask[s0 + gi / jg], x8, xs8, red, tid, tag_pt, nrec, 0,
-                          s0 * M * J + gi % jg, t == 0, t == kg - 1, outv);
+          task_compute<M, A8>(sh, w, cur, un, s0 + gi / jg, un.mask[s0 + gi / jg], x8, xs8, red, tid, tag_pt, nrec, 0,
+                              s0 * M * J + gi % jg, t == 0, t == kg - 1, outv, (gi % jg) * kg + t);
           if (!nrec) break;
           gi = gn;
           t = tn;
@@ -1285,6 +1428,8 @@ __global__ void pack_tasks_kernel(const uint8_t* __restrict__ gq, const uint8_t*
 int g_grid[64];       // workgroups per launch, per device (one per CU)
 unsigned long long* g_trace[64];  // per device: trace buffer registered by qws_debug_trace_buffer
 size_t g_trace_bytes[64];
+float* g_act[64];                 // per device: activation buffer registered by qws_debug_w4a8_act_buffer
+size_t g_act_bytes[64];
 constexpr size_t kMaxDynLds = 160 * 1024 - 16 * 1024;
 
 size_t lds_bytes(int M, int E, int H, int P, int J, int nrw) {
@@ -1354,29 +1499,29 @@ int check_layer(const qws_moe_layer& d, int E, int H, int I, int has_shared) {
   return QWS_OK;
 }
 
-template <int M>
+template <int M, bool A8>
 int launch(const Layer& first, const qws_moe_layer* rest, int n, const Shape& sh, const Work& w, int G, size_t lds,
            hipStream_t s) {
   static bool configured[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (!configured[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layers_kernel<M>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layers_kernel<M, A8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e != hipSuccess) return qws_host::set_device_error(e);
     configured[dev] = true;
   }
   // the in-kernel hand-offs need every workgroup resident at once: one per compute unit
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layers_kernel<M>, kThreads, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layers_kernel<M, A8>, kThreads, lds);
   if (e != hipSuccess) return qws_host::set_device_error(e);
   if (per_cu < 1) return QWS_ERR_SHAPE;
-  hipLaunchKernelGGL(moe_layers_kernel<M>, dim3(G), dim3(kThreads), lds, s, first, rest, n, sh, w);
+  hipLaunchKernelGGL((moe_layers_kernel<M, A8>), dim3(G), dim3(kThreads), lds, s, first, rest, n, sh, w);
   return qws_host::check_launch();
 }
 
 int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_layers, int M, int K,
-               void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+               void* workspace, size_t workspace_bytes, qws_stream_t stream, bool a8) {
   if (!host || n_layers < 1) return QWS_ERR_ARG;
   if (n_layers > 1 && !dev_copy) return QWS_ERR_ARG;
   if (n_layers > kMaxLayers) return QWS_ERR_SHAPE;
@@ -1418,6 +1563,9 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
     (void)hipGetDevice(&dev);
     const size_t need = (size_t)n_layers * G * kTracePoints * 8;
     w.trace = (dev >= 0 && dev < 64 && g_trace[dev] && g_trace_bytes[dev] >= need) ? g_trace[dev] : nullptr;
+    const size_t na = (size_t)(E + 1) * M * I, need_act = na * 5 + na / kBlk;
+    w.act = (a8 && n_layers == 1 && dev >= 0 && dev < 64 && g_act[dev] && g_act_bytes[dev] >= need_act) ? g_act[dev]
+                                                                                                       : nullptr;
   }
   // x_fresh: no layer's x overlaps an output of any layer of this launch (all x were written before it)
   bool x_fresh = !chained;
@@ -1443,11 +1591,19 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
                  x_fresh ? 1 : 0, J};
   const Layer first = to_layer(host[0]);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a8) {
+    switch (M) {
+      case 1: return launch<1, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      case 2: return launch<2, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      case 3: return launch<3, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      default: return launch<4, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    }
+  }
   switch (M) {
-    case 1: return launch<1>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    case 2: return launch<2>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    case 3: return launch<3>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    default: return launch<4>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 1: return launch<1, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 2: return launch<2, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 3: return launch<3, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    default: return launch<4, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
   }
 }
 
@@ -1462,12 +1618,22 @@ extern "C" size_t moe_layer_workspace_bytes(int M, int K, int E, int hidden, int
 
 extern "C" int moe_layer_mxfp4(const qws_moe_layer* layer, int M, int K, void* workspace, size_t workspace_bytes,
                                qws_stream_t stream) {
-  return run_layers(layer, nullptr, 1, M, K, workspace, workspace_bytes, stream);
+  return run_layers(layer, nullptr, 1, M, K, workspace, workspace_bytes, stream, false);
 }
 
 extern "C" int moe_layers_mxfp4(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
                                 int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream) {
-  return run_layers(layers_host, layers_device, n_layers, M, K, workspace, workspace_bytes, stream);
+  return run_layers(layers_host, layers_device, n_layers, M, K, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int moe_layer_w4a8(const qws_moe_layer* layer, int M, int K, void* workspace, size_t workspace_bytes,
+                              qws_stream_t stream) {
+  return run_layers(layer, nullptr, 1, M, K, workspace, workspace_bytes, stream, true);
+}
+
+extern "C" int moe_layers_w4a8(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers,
+                               int M, int K, void* workspace, size_t workspace_bytes, qws_stream_t stream) {
+  return run_layers(layers_host, layers_device, n_layers, M, K, workspace, workspace_bytes, stream, true);
 }
 
 extern "C" int moe_workspace_errors(const void* workspace, int M, int K, int E, int inter, unsigned* errors_out,
@@ -1518,6 +1684,17 @@ extern "C" int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* out, 
     desc_out->down_s = nullptr;
   }
   return st;
+}
+
+extern "C" int qws_debug_w4a8_act_buffer(void* buf, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return qws_host::set_device_error(e);
+  if (dev < 0 || dev >= 64) return QWS_ERR_DEVICE;
+  if (buf && !qws_host::aligned16(buf)) return QWS_ERR_ALIGN;
+  g_act[dev] = static_cast<float*>(buf);
+  g_act_bytes[dev] = buf ? bytes : 0;
+  return QWS_OK;
 }
 
 extern "C" int qws_debug_trace_buffer(void* buf, size_t bytes) {
