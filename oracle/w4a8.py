@@ -115,27 +115,3 @@ def moe_layer_w4a8(x_bits: np.ndarray, idx: np.ndarray, w: np.ndarray, experts, 
             acts[(m, e)] = (we, a)
     return (y, acts) if detail else y
 
-
-def rounding_slack(a: np.ndarray, eta: float) -> np.ndarray:
-    """How far mxfp8(a') can be from mxfp8(a), element by element, for any a' with
-    |a' - a| <= eta * max|a| of its block of 32 in every element: 0 where no such a' changes
-    the element's scale or code; otherwise twice the element's E4M3 step at the coarser scale it
-    may get, plus eta * max|a|. The bound for comparing a quantisation taken on values computed
-    in another precision (float32 on a GPU) with this one (float64)."""
-    a = np.asarray(a, dtype=np.float64)
-    blk = a.reshape(*a.shape[:-1], -1, MX_BLOCK)
-    amax = np.max(np.abs(blk), axis=-1, keepdims=True)
-    tol = eta * amax
-    s = scale_exponent_of_max(amax)
-    # the scale changes only if max|a'| can cross a power of two
-    scale_moves = (scale_exponent_of_max(np.maximum(amax - tol, 0.0)) != s) | (scale_exponent_of_max(amax + tol) != s)
-    # the code changes only if a' / X can cross a rounding point of E4M3 (rounding is monotonic,
-    # so comparing the codes of the two ends of the interval finds every crossing)
-    X = np.ldexp(1.0, s)
-    v, t = np.abs(blk) / X, tol / X
-    code_moves = e4m3_encode(np.minimum(v + t, 1e4)) != e4m3_encode(np.maximum(v - t, 0.0))
-    # E4M3 step at v + t (subnormal step 2^-9 below 2^-6), at the coarser scale if it may move
-    step = np.ldexp(1.0, np.maximum(np.floor(np.log2(np.maximum(v + t, 2.0 ** -6))), -6).astype(np.int64) - 3)
-    step = step * X * np.where(scale_moves, 2.0, 1.0)
-    slack = np.where(scale_moves | code_moves, 2.0 * step + tol, 0.0)
-    return np.broadcast_to(slack, blk.shape).reshape(a.shape)

@@ -1,7 +1,6 @@
 """Pins of the W4A8 oracle (oracle/w4a8.py) against what the MX and E4M3 definitions fix: hand-worked
 MXFP8 blocks, exact round trips of representable blocks, the round-to-nearest error bound, a
-brute-force scalar layer at a tiny shape, closeness to the bf16 layer, and the bound that
-compares a quantisation decided in float32 with the oracle's."""
+brute-force scalar layer at a tiny shape, and closeness to the bf16 layer."""
 import json
 import math
 import os
@@ -176,32 +175,3 @@ def test_w4a8_degenerate_inputs():
     x = synth.token_vectors(2, 0, 2, 64)
     y = W.moe_layer_w4a8(x, np.array([[0, 1], [4, 1]]), np.array([[0.5, 0.5], [0.5, 0.5]]), experts, 4)
     assert np.all(np.isfinite(y[0])) and np.all(np.isnan(y[1]))
-
-
-# ----------------------------------------------------------------------------- slack bound
-@pytest.mark.parametrize("eta", [1e-6, 1e-4, 1e-3])
-def test_rounding_slack_bounds_every_perturbation(eta):
-    """For a' within eta * max|a| of a (per block), |mxfp8(a') - mxfp8(a)| <= |a' - a| + slack(a, eta),
-    checked on random perturbations of random vectors and of vectors placed on E4M3 midpoints
-    and on powers of two (where scales and codes flip)."""
-    rng = np.random.default_rng(int(1 / eta))
-    base = [rng.standard_normal((8, 64)) * np.exp(rng.standard_normal((8, 64)))]
-    mid = np.ldexp(1.0 + (2 * rng.integers(0, 8, (8, 64)) + 1) / 16.0, rng.integers(-6, 8, (8, 64)))
-    mid *= np.where(rng.random((8, 64)) < 0.5, -1.0, 1.0)
-    mid[:, ::32] = 256.0        # block max 256: the scale is fixed by it, the rest sit on midpoints
-    base.append(mid * 2.0 ** -8)
-    pow2 = rng.standard_normal((8, 64))
-    pow2[:, ::32] = 4.0          # block max exactly a power of two: the scale may flip
-    base.append(pow2)
-    for a in base:
-        sl = W.rounding_slack(a, eta)
-        q = W.mxfp8_round(a)
-        amax = np.repeat(np.max(np.abs(a.reshape(a.shape[0], -1, 32)), axis=-1), 32, axis=-1)
-        for _ in range(50):
-            d = (2 * rng.random(a.shape) - 1) * eta * amax
-            d *= rng.random(a.shape) < 0.5
-            assert np.all(np.abs(W.mxfp8_round(a + d) - q) <= np.abs(d) + sl + 1e-300)
-        for sgn in (-1.0, 1.0):          # the ends of the interval
-            assert np.all(np.abs(W.mxfp8_round(a + sgn * eta * amax) - q) <= eta * amax + sl + 1e-300)
-    assert not W.rounding_slack(base[0], 0.0).any()
-    assert W.rounding_slack(base[1], eta).any() and W.rounding_slack(base[2], eta).any()
