@@ -315,6 +315,20 @@ __device__ __forceinline__ f32x4_t mfma_fp4_fp8(u32x4_t a, u32x4_t b_lo, u32x4_t
                                                           OPSEL_A, (int)scale_a, 0, (int)scale_b);
 }
 
+// The same instruction with the formats swapped: A FP8 (rows in the B layout above: row i, block
+// b from lane groups 2 (b % 2) and 2 (b % 2) + 1, dwords 4 (b / 2) .. +3), B FP4 (column n, block
+// b: lane (b, n), 16 bytes); the scale of A row i block b in lane (b, i), of B column n block b in
+// lane (b, n) (measured on gfx950 with random operands).
+__device__ __forceinline__ f32x4_t mfma_fp8_fp4(u32x4_t a_lo, u32x4_t a_hi, u32x4_t b, uint32_t scale_a,
+                                                uint32_t scale_b, f32x4_t c) {
+  const int u = __builtin_nondeterministic_value(0);
+  const i32x8_t av = {(int)a_lo[0], (int)a_lo[1], (int)a_lo[2], (int)a_lo[3],
+                      (int)a_hi[0], (int)a_hi[1], (int)a_hi[2], (int)a_hi[3]};
+  const i32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], u, u, u, u};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0 /* A: FP8 e4m3 */, 4 /* B: FP4 e2m1 */,
+                                                          0, (int)scale_a, 0, (int)scale_b);
+}
+
 // A matrix instruction takes its operands from every lane of the wave, so it must run with all
 // lanes enabled. When its result is used only under a lane condition (a store by some lanes), the
 // compiler sinks the scaled instruction into that branch, where the disabled lanes supply no
@@ -562,24 +576,28 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
     }
     __syncthreads();
 
-    // down on the scaled instruction, 64 rows per op: A block b = 16-row tile 4Q + b of this
-    // wave's tiles w + 16 q (q < 10: ops Q = 0, 1 take q 0 .. 7, op 2 takes q 8, 9 in blocks 0, 1),
-    // row i, the task's 32 codes; B column n = token slot c = n / 4 and tile slot b = n % 4 holds
-    // token c % MP's 32 codes in block b and zeros elsewhere, so D column n = tile b's 16 rows for
-    // that token. The record gives lane (g, n) word g (codes 8g .. 8g+7) of row n of each tile;
-    // two lane-group swaps per register pair turn four such words into one row's 16 bytes.
-    const int c = n >> 2, bq = n & 3, mt = c % MP;
-    const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
+    // down on the scaled instruction, 64 rows per op, activations as A (FP8) and weights as B
+    // (FP4). B block b = 16-row tile 4Q + b of this wave's tiles w + 16 q (q < 10: ops Q = 0, 1
+    // take q 0 .. 7, op 2 takes q 8, 9 in blocks 0, 1), column n = tile row n, the task's 32 codes.
+    // A row 4 bq + c holds token c's 32 codes in block bq and zeros elsewhere, so D row 4 bq + c,
+    // column n is row n of tile 4Q + bq for token c: lane (g, n) holds it in register c for bq = g,
+    // and one store instruction per token writes four whole 16-row lines. The record gives lane
+    // (g, n) word g (codes 8g .. 8g+7) of row n of each tile; two lane-group swaps per register
+    // pair turn four such words into one row's 16 bytes.
+    const int ca = n & 3, ba = n >> 2;
+    const bool toka = ca < M && (M == 1 || ((mask >> ca) & 1u));
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    const u32x4_t av16 = tok ? *reinterpret_cast<const u32x4_t*>(a8 + min(mt, M - 1) * 32 + 16 * (g & 1)) : zero;
-    const u32x4_t blo = bq == (g >> 1) ? av16 : zero, bhi = bq == 2 + (g >> 1) ? av16 : zero;
-    const uint32_t bsc = a8[kMaxM * 32 + min(mt, M - 1)];
-    const float wt = un.w[u][min(mt, M - 1)];
-    const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
-    unsigned long long* pdst =
-        w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
-    constexpr int D = 4 / MP;   // copies of each token's column group
-    const int dup = c / MP;
+    const u32x4_t av16 = toka ? *reinterpret_cast<const u32x4_t*>(a8 + min(ca, M - 1) * 32 + 16 * (g & 1)) : zero;
+    const u32x4_t alo = ba == (g >> 1) ? av16 : zero, ahi = ba == 2 + (g >> 1) ? av16 : zero;
+    const uint32_t asc = a8[kMaxM * 32 + min(ca, M - 1)];
+    unsigned long long* pdst[M];
+    float wt[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int pm = un.pair0[u] + __popc(mask & ((1u << m) - 1u));
+      pdst[m] = w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
+      wt[m] = un.w[u][m];
+    }
 #pragma unroll
     for (int Q = 0; Q < 3; ++Q) {
       uint32_t v0 = Q == 0 ? dq0[0] : (Q == 1 ? dq1[0] : dn8), v1 = Q == 0 ? dq0[1] : (Q == 1 ? dq1[1] : dn9);
@@ -589,23 +607,20 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
       const auto p13 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
       const auto p01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
       const auto p23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
-      const u32x4_t arow = {p01[0], p01[1], p23[0], p23[1]};   // group b: words 0 .. 3 of tile 4Q + b, row n
-      // this lane's A scale (tile q = 4Q + g, row n) is held by lane n + 16 (q / 3), in byte
+      const u32x4_t wrow = {p01[0], p01[1], p23[0], p23[1]};   // group b: words 0 .. 3 of tile 4Q + b, row n
+      // this lane's weight scale (tile q = 4Q + g, row n) is held by lane n + 16 (q / 3), in byte
       // 1 + q % 3 of its first piece's last word
       const int q = min(4 * Q + g, kDnTpw - 1);
       const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
-      const uint32_t asc = (sw >> (8 + 8 * (q % 3))) & 0xffu;
-      f32x4_t dd = mfma_fp4_fp8<0>(arow, blo, bhi, asc, bsc, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      const uint32_t bsc = (sw >> (8 + 8 * (q % 3))) & 0xffu;
+      f32x4_t dd = mfma_fp8_fp4(alo, ahi, wrow, asc, bsc, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
       mfma_result(dd);
-      // lane (g, n) holds rows 4g .. 4g+3 of tile 4Q + bq for token mt: it stores rows 4g + dup + D s
+      const int rt = wave + kWaves * (4 * Q + g);
 #pragma unroll
-      for (int t = 0; t < MP; ++t) {
-        const int el = dup + D * t;
-        const float v = el == 0 ? dd[0] : (el == 1 ? dd[1] : (el == 2 ? dd[2] : dd[3]));
-        outv[Q * MP + t] = first ? v : outv[Q * MP + t] + v;
-        const int qt = 4 * Q + bq, rt = wave + kWaves * qt;
-        if (last && tok && qt < kDnTpw && rt < ntile)
-          st_coherent(pdst + rt * 16 + 4 * g + el, tagged(tag, __float_as_uint(wt * outv[Q * MP + t])));
+      for (int m = 0; m < M; ++m) {
+        outv[Q * M + m] = first ? dd[m] : outv[Q * M + m] + dd[m];
+        if (last && (M == 1 || ((mask >> m) & 1u)) && 4 * Q + g < kDnTpw && rt < ntile)
+          st_coherent(pdst[m] + rt * 16 + n, tagged(tag, __float_as_uint(wt[m] * outv[Q * M + m])));
       }
     }
   } else {
