@@ -195,6 +195,7 @@ class DecodeStep:
         import torch
         import synth
         self.qws, self.M, self.dev = qws, M, dev
+        self.w4a8 = False   # True: the layers run moe_layers_w4a8 (MXFP8 activations)
         log(f"building {n_layers} layers (M={M})")
         self.layers = []
         for l in range(n_layers):
@@ -211,7 +212,7 @@ class DecodeStep:
             self.vout = qws.lmhead_verify_greedy_fp8(head, self.xh, self.draft, self.vws, logits=self.logits)
 
     def layers_call(self):
-        self.seq.run(self.ws)
+        self.seq.run(self.ws, w4a8=self.w4a8)
 
     def head_call(self):
         if self.M == 1:
@@ -458,6 +459,15 @@ def main():
                                            "GBps": round(sb / (rf["step_ms_median"] * 1e-3) / 1e9, 1),
                                            "back_to_back_ms": round(r["gpu_ms"], 4)}
     log("decode_step_m1_flushed", breakdown["decode_step_m1_flushed"])
+    # the same step with MXFP8 activations in the MoE layers (W4A8)
+    step.w4a8 = True
+    rw8 = step.timed(args.steps, args.warmup)
+    step.w4a8 = False
+    breakdown["decode_step_m1_w4a8"] = {"ms_wall": round(rw8["wall_ms"], 4), "GBps": round(sb / (rw8["wall_ms"] * 1e-3) / 1e9, 1),
+                                        "moe_us_per_layer": round(rw8["moe_us_mean"] / args.layers, 3),
+                                        "bf16_activations_moe_us_per_layer": round(r["moe_us_mean"] / args.layers, 3),
+                                        "in_kernel_wait_timeouts": step.errors()}
+    log("decode_step_m1_w4a8", breakdown["decode_step_m1_w4a8"])
 
     if not args.no_breakdown:
         breakdown["probe_read_ceiling"] = probe_ceiling(qws, dev)
@@ -496,6 +506,15 @@ def main():
         L2 = lay["moe_layer_m1_seed0"]
         t = time_cold(lambda: L2.run_two_call(wsr1, wse1), dev, flush=flush)
         breakdown["moe_layer_m1_seed0_two_call_path"] = {"median_us": t["median_us"]}
+        # the same layers with MXFP8 activations (W4A8: moe_layer_w4a8), cold
+        for name in ("moe_layer_m1_seed0", "moe_layer_m4_disjoint"):
+            Lw = lay[name]
+            t = time_cold(lambda: qws.moe_layer_w4a8(Lw.fused, workspace=wsf[Lw.M]), dev, flush=flush)
+            nb = breakdown[name]["bytes"]
+            t.update({"bytes": nb, "GBps": round(nb / (t["median_us"] * 1e-6) / 1e9, 1),
+                      "bf16_activations_median_us": round(breakdown[name]["median_us"], 2)})
+            breakdown[name + "_w4a8"] = t
+            log(name + "_w4a8", t)
         t1 = breakdown["moe_layer_m1_seed0"]["median_us"]
         breakdown["verify_cost_ratio"] = {reg: round(breakdown[f"moe_layer_m4_{reg}"]["median_us"] / t1, 3)
                                           for reg in synth.REGIMES}
@@ -616,6 +635,13 @@ def main():
                                        "moe_layers_traffic": traffic_for("moe_fused.hip", "moe_layers_kernel_m4"),
                                        "moe_layers_algorithmic_bytes": b4 - head_bytes(4)}
         log("decode_step_m4", breakdown["decode_step_m4"])
+        step4.w4a8 = True
+        r48 = step4.timed(max(5, args.steps // 2), 2)
+        breakdown["decode_step_m4_w4a8"] = {"ms_wall": round(r48["wall_ms"], 4),
+                                            "moe_us_per_layer": round(r48["moe_us_mean"] / args.layers, 3),
+                                            "GBps": round(b4 / (r48["wall_ms"] * 1e-3) / 1e9, 1),
+                                            "in_kernel_wait_timeouts": step4.errors()}
+        log("decode_step_m4_w4a8", breakdown["decode_step_m4_w4a8"])
         del step4
         # speculation priced from these steps: a draft step taken as one MoE layer plus the shared
         # head at M = 1 (the draft is the model's one extra NEXTN layer; attention is not modelled)
