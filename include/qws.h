@@ -20,7 +20,9 @@
 #ifndef QWS_H
 #define QWS_H
 
+#ifndef __HIPCC_RTC__   /* hipRTC (run-time compilation of the kernels) has size_t built in */
 #include <stddef.h>
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -378,10 +380,15 @@ int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, 
  * builds in seconds (runbyai.xyz/posts/593 paragraph 4; Netics post, "Humming MXFP4 kernels
  * compile at run time for the model's real shapes"). Here: the FP8 head GEMV, compiled from the
  * same source as lmhead_gemv_fp8 with rows and cols as constants, for the current device's
- * architecture (gcnArchName) and M. Key: (M, rows, cols, architecture, source hash); the disk
- * cache is `cache_dir` (NULL: $QWS_RTC_CACHE, else $HOME/.cache/qws_rtc), one file per key,
- * written whole (rename) so that concurrent processes never read half a file. Cache files are
- * loaded as device code: the directory must be writable by trusted users only.
+ * architecture (gcnArchName) and M; and the fused MoE layers with the layer shape as constants.
+ * Key: the kernel and its constants, the architecture, a hash of the sources, and a digest of the
+ * compile options and the hipRTC version. The disk cache is `cache_dir` (NULL: $QWS_RTC_CACHE,
+ * else $XDG_CACHE_HOME/qws_rtc, else $HOME/.cache/qws_rtc; none of these set: no disk cache),
+ * created with mode 0700 and used only while it is a directory owned by the calling user that no
+ * one else may write; one file per key, written to a fresh temporary file (mkstemp) and renamed,
+ * so that concurrent processes never read half a file; a file is read only if it is a regular file
+ * owned by the user (not followed through a link) whose stored code hash matches. Any failed check
+ * means a compile instead.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   unsigned long long compiles;    /* hipRTC compilations */
@@ -402,6 +409,22 @@ int lmhead_gemv_fp8_rtc(const qws_lmhead* head, const void* x_bf16, int M, float
  * arch name not of that form, QWS_ERR_SHAPE as lmhead_gemv_fp8, QWS_ERR_COMPILE (e.g. an
  * architecture without the gfx950 conversions the kernel uses). */
 int qws_rtc_compile_head_fp8(int M, long long rows, long long cols, const char* arch, const char* cache_dir);
+/* The fused MoE layers (moe_layers_mxfp4, or moe_layers_w4a8 when w4a8 = 1) compiled at run time
+ * for the layers' shape: the same kernel source with E, K, hidden, inter and the shared expert as
+ * constants and M and the precision as template arguments, for the current device's
+ * architecture. Key: (M, precision, E, hidden, inter, K, shared, architecture, source hash, options
+ * and hipRTC version). Same arguments, validation, workspace and results as the template entry
+ * points, bit for bit; QWS_ERR_ARG for w4a8 outside {0, 1}, plus the errors of
+ * lmhead_gemv_fp8_rtc. A compile takes seconds: the first call for a key blocks the calling
+ * thread until it is done (qws_rtc_compile_moe builds the cache ahead of time). */
+int moe_layers_rtc(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers, int M,
+                   int K, int w4a8, void* workspace, size_t workspace_bytes, const char* cache_dir,
+                   qws_stream_t stream);
+/* Compile (or find in the disk cache) the fused MoE kernel for a shape and an architecture name,
+ * without a device. QWS_ERR_ARG for a bad arch name or w4a8 outside {0, 1}; QWS_ERR_SHAPE for M,
+ * K, E, hidden, inter or has_shared outside the ranges of moe_layer_mxfp4. */
+int qws_rtc_compile_moe(int M, int K, int E, int hidden, int inter, int has_shared, int w4a8, const char* arch,
+                        const char* cache_dir);
 /* Counters since load or the last qws_rtc_reset (stats_out: host memory). */
 int qws_rtc_stats_get(qws_rtc_stats* stats_out);
 /* Unload the modules and zero the counters; the disk cache is kept. */

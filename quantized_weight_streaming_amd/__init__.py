@@ -30,7 +30,7 @@ __all__ = ["selfcheck", "moe_route_topk", "moe_expert_gemv_mxfp4", "ExpertBank",
            "lmhead_bf16",
            "moe_layer_mxfp4", "moe_layers_mxfp4", "moe_layer_w4a8", "moe_layers_w4a8", "MoeLayer", "moe_layer_workspace", "moe_workspace_errors",
            "lmhead_quantize_fp8", "lmhead_fp8_codes_bytes", "fp8_codes_rowmajor", "lmhead_gemv_fp8", "lmhead_gemv_bf16",
-           "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8", "lmhead_gemv_fp8_rtc", "rtc_compile_head_fp8",
+           "lmhead_verify_greedy_fp8", "lmhead_verify_sample_fp8", "lmhead_gemv_fp8_rtc", "rtc_compile_head_fp8", "rtc_compile_moe",
            "rtc_stats", "rtc_reset",
            "verify_workspace", "debug_dequant_mxfp4", "debug_dequant_fp8",
            "probe_read", "probe_read_nt", "probe_copy", "route_workspace", "expert_workspace", "QwsError", "lib"]
@@ -262,8 +262,15 @@ class MoeLayers:
         raw = torch.frombuffer(bytearray(C.string_at(C.addressof(self.host), C.sizeof(self.host))), dtype=torch.uint8)
         self.dev = raw.to(layers[0].x.device)
 
-    def run(self, workspace, w4a8: bool = False) -> None:
+    def run(self, workspace, w4a8: bool = False, rtc: bool = False, cache_dir=None) -> None:
+        """One launch of all the layers: moe_layers_mxfp4 (or _w4a8); with rtc, the kernel compiled
+        at run time for this shape (moe_layers_rtc; code objects cached in `cache_dir`)."""
         L0 = self.layers[0]
+        if rtc:
+            st = lib().moe_layers_rtc(self.host, _p(self.dev), len(self.layers), L0.M, L0.K, int(w4a8), _p(workspace),
+                                      workspace.numel(), _enc(cache_dir), _stream(L0.x.device))
+            check("moe_layers_rtc", st)
+            return
         name = "moe_layers_w4a8" if w4a8 else "moe_layers_mxfp4"
         st = getattr(lib(), name)(self.host, _p(self.dev), len(self.layers), L0.M, L0.K, _p(workspace),
                                   workspace.numel(), _stream(L0.x.device))
@@ -400,6 +407,13 @@ def lmhead_gemv_fp8_rtc(head: LMHead, x: torch.Tensor, out=None, cache_dir=None)
 def rtc_compile_head_fp8(M: int, rows: int, cols: int, arch: str = "gfx950", cache_dir=None) -> None:
     """Compile (or find cached) the run-time-specialised FP8 head GEMV without a device."""
     check("qws_rtc_compile_head_fp8", lib().qws_rtc_compile_head_fp8(M, rows, cols, arch.encode(), _enc(cache_dir)))
+
+
+def rtc_compile_moe(M: int, K: int, E: int, hidden: int, inter: int, has_shared: bool = True, w4a8: bool = False,
+                    arch: str = "gfx950", cache_dir=None) -> None:
+    """Compile (or find in the disk cache) the fused MoE kernel for a shape; needs no GPU."""
+    check("qws_rtc_compile_moe", lib().qws_rtc_compile_moe(M, K, E, hidden, inter, int(has_shared), int(w4a8),
+                                                           arch.encode(), _enc(cache_dir)))
 
 
 def rtc_stats() -> dict:

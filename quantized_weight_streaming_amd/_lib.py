@@ -82,6 +82,8 @@ SIGNATURES = {
     "lmhead_gemv_bf16": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, _P]),
     "lmhead_gemv_fp8_rtc": (_I, [C.POINTER(LMHeadDesc), _P, _I, _P, C.c_char_p, _P]),
     "qws_rtc_compile_head_fp8": (_I, [_I, _LL, _LL, C.c_char_p, C.c_char_p]),
+    "moe_layers_rtc": (_I, [C.POINTER(MoeLayerDesc), _P, _I, _I, _I, _I, _P, _SZ, C.c_char_p, _P]),
+    "qws_rtc_compile_moe": (_I, [_I, _I, _I, _I, _I, _I, _I, C.c_char_p, C.c_char_p]),
     "qws_rtc_stats_get": (_I, [C.POINTER(RtcStats)]),
     "qws_rtc_reset": (_I, []),
     "qws_debug_dequant_mxfp4": (_I, [_P, _P, _LL, _I, _I, _P, _P]),

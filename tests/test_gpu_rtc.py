@@ -77,3 +77,73 @@ def test_rtc_refuses_a_bf16_head():
     with pytest.raises(qws.QwsError) as e:
         qws.lmhead_gemv_fp8_rtc(hb, bf16(synth.token_vectors(16, 0, 1, 64)))
     assert e.value.status == _lib.QWS_ERR_FORMAT
+
+
+# ------------------------------------------------------------------------------ fused MoE layers
+def _rtc_layers(M, shape, seed, n=3):
+    from .helpers import Layer
+    from .test_gpu_fused import _packed
+    layers = [Layer(seed, l, shape, M) for l in range(n)]
+    return layers, [qws.MoeLayer(t.x_t, t.wr_t, _packed(t), shape.topk) for t in layers]
+
+
+@pytest.mark.parametrize("M,w4a8", [(1, False), (1, True), (4, False), (4, True), (2, False)])
+def test_moe_rtc_equals_template(tmp_path, M, w4a8):
+    """The run-time-compiled fused kernel (shape as constants) gives the template build's outputs
+    bit for bit, three layers in one launch; its first layer also against the oracle."""
+    from .test_gpu_fused import _check_layer
+    from .test_gpu_w4a8 import _act_buffer, _check_w4a8
+    say("rtc moe M", M, "w4a8", w4a8)
+    shape = synth.LayerShape()
+    layers, Ls = _rtc_layers(M, shape, 60 + M)
+    _, Lt = _rtc_layers(M, shape, 60 + M)
+    ws = qws.moe_layer_workspace(M, 8, 512, 2560, 768, "cuda")
+    qws.MoeLayers(Lt).run(ws, w4a8=w4a8)
+    qws.MoeLayers(Ls).run(ws, w4a8=w4a8, rtc=True, cache_dir=str(tmp_path))
+    torch.cuda.synchronize()
+    for a, b in zip(Lt, Ls):
+        assert np.array_equal(a.y_f32.cpu().numpy().view(np.uint32), b.y_f32.cpu().numpy().view(np.uint32))
+        assert np.array_equal(a.topk_idx.cpu().numpy(), b.topk_idx.cpu().numpy())
+        assert np.array_equal(a.topk_w.cpu().numpy().view(np.uint32), b.topk_w.cpu().numpy().view(np.uint32))
+    assert qws.moe_workspace_errors(ws, M, 8, 512, 768) == 0
+    # the first layer alone through the run-time path, against the oracle (W4A8: with the
+    # activation record, as in the template tests)
+    L0 = qws.MoeLayer(layers[0].x_t, layers[0].wr_t, Ls[0].bank, 8,
+                      logits_out=torch.empty((M, 512), dtype=torch.float32, device="cuda"))
+    buf = _act_buffer(shape, M) if w4a8 else None
+    qws.debug_w4a8_act_buffer(buf)
+    try:
+        qws.MoeLayers([L0]).run(ws, w4a8=w4a8, rtc=True, cache_dir=str(tmp_path))
+        torch.cuda.synchronize()
+    finally:
+        qws.debug_w4a8_act_buffer(None)
+    if w4a8:
+        _check_w4a8(layers[0], L0, buf.cpu().numpy())
+    else:
+        _check_layer(layers[0], L0)
+
+
+def test_moe_rtc_small_shape_and_cache_levels(tmp_path):
+    """A small shape (64 experts, H 544, I 1024, top-8) through the run-time path: oracle parity,
+    then the loaded module serves the next call, and after the modules are dropped the disk."""
+    from .test_gpu_fused import _check_layer
+    say("rtc moe small shape, cache levels")
+    shape = synth.LayerShape(hidden=544, inter=1024, n_routed=64)
+    layers, Ls = _rtc_layers(2, shape, 70, n=1)
+    ws = qws.moe_layer_workspace(2, 8, 64, 544, 1024, "cuda")
+    qws.rtc_reset()
+    seq = qws.MoeLayers(Ls)
+    for expect in ((1, 0, 0), (1, 0, 1)):
+        seq.run(ws, rtc=True, cache_dir=str(tmp_path))
+        torch.cuda.synchronize()
+        s = qws.rtc_stats()
+        assert (s["compiles"], s["disk_hits"], s["memory_hits"]) == expect
+    qws.rtc_reset()
+    L1 = qws.MoeLayer(layers[0].x_t, layers[0].wr_t, Ls[0].bank, 8,
+                      logits_out=torch.empty((2, 64), dtype=torch.float32, device="cuda"))
+    qws.MoeLayers([L1]).run(ws, rtc=True, cache_dir=str(tmp_path))
+    torch.cuda.synchronize()
+    s = qws.rtc_stats()
+    assert (s["compiles"], s["disk_hits"], s["memory_hits"]) == (0, 1, 0)
+    _check_layer(layers[0], L1)
+    assert qws.moe_workspace_errors(ws, 2, 8, 64, 1024) == 0
