@@ -576,9 +576,41 @@ def main():
         qws.lmhead_gemv_fp8_rtc(head8, x4, out=lg4, cache_dir=rtc_dir)
         torch.cuda.synchronize(dev)
         rtc["disk_cache_first_call_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
-        shutil.rmtree(rtc_dir, ignore_errors=True)
         breakdown["lmhead_fp8_rtc"] = rtc
         log("lmhead_fp8_rtc", rtc)
+        # the fused MoE kernel compiled at run time for the layer shape: the 42-layer launch of the
+        # decode step (M = 1), first call into an empty cache, then back-to-back launches against
+        # the template build, then a first call served by the disk cache
+        qws.rtc_reset()
+        mrtc = {}
+        for w8 in (False, True):
+            tag = "w4a8" if w8 else "bf16"
+            t0 = time.perf_counter()
+            step.seq.run(step.ws, w4a8=w8, rtc=True, cache_dir=rtc_dir)
+            torch.cuda.synchronize(dev)
+            mrtc[f"{tag}_first_call_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+            for name_, use in (("template", False), ("rtc", True)):
+                for _ in range(3):
+                    step.seq.run(step.ws, w4a8=w8, rtc=use, cache_dir=rtc_dir)
+                evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+                for a_, b_ in evr:
+                    a_.record()
+                    step.seq.run(step.ws, w4a8=w8, rtc=use, cache_dir=rtc_dir)
+                    b_.record()
+                torch.cuda.synchronize(dev)
+                tr = sorted(a_.elapsed_time(b_) * 1e3 for a_, b_ in evr)
+                mrtc[f"{tag}_{name_}_us_per_layer"] = round(tr[len(tr) // 2] / args.layers, 3)
+        st = qws.rtc_stats()
+        mrtc["compiles"], mrtc["compile_ms_total"] = st["compiles"], round(st["compile_ms"], 1)
+        qws.rtc_reset()
+        t0 = time.perf_counter()
+        step.seq.run(step.ws, rtc=True, cache_dir=rtc_dir)
+        torch.cuda.synchronize(dev)
+        mrtc["disk_cache_first_call_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        mrtc["in_kernel_wait_timeouts"] = step.errors()
+        shutil.rmtree(rtc_dir, ignore_errors=True)
+        breakdown["moe_layers_m1_rtc"] = mrtc
+        log("moe_layers_m1_rtc", mrtc)
         # the same M = 1 step captured once in a HIP graph (the 42-layer launch and the head) and
         # replayed: the host's per-step launch work leaves the loop
         graph = torch.cuda.CUDAGraph()
