@@ -164,16 +164,88 @@ __global__ __launch_bounds__(kFinishThreads) void greedy_finish_kernel(const uns
 // per position from the caller), then the accepted prefix of the drafts. Runs after
 // head_fp8_kernel<M, kKeys>, which leaves the logits and, per head workgroup and token, the largest
 // 64-bit key (ordered logit, ~row) of the workgroup's rows. One workgroup per position:
-//  1. t = the k-th largest of those G keys. Every key of the token's top k is at least t (the k
-//     largest workgroup maxima are k keys >= t), and so lies in one of the exactly k workgroups
-//     whose maximum reaches t (every workgroup when G <= k).
-//  2. Candidates: the keys >= t among those workgroups' rows (at most k x tiles x 16), read back
-//     from the logits; the top k of them, in order, by a radix select and a wave sort.
+//  1. t = a lower bound of the k-th largest of those G keys: the k-th largest of the eight waves'
+//     ceil(k / 8) largest (rounds of a wave maximum, lane exchanges by DPP and lane-group swaps,
+//     no LDS), so that every key of the token's top k is at least t and lies in one of the
+//     workgroups whose maximum reaches t: k of them when the waves split the top k evenly, a few
+//     more otherwise (more than 64: t becomes the exact k-th largest by radix select).
+//  2. Candidates: the keys >= t among those workgroups' rows, read back from the logits. They are
+//     the top k and a few other keys >= t (k to k + 3 in simulations of normal logits), so one
+//     wave sorts them; more than 64 go through a radix select first.
+// Tried and slower: sorting each wave's 256 keys and merging the waves' top 64 (6.2 us for step 1
+// against 1.8); each wave reading its top workgroups' rows ahead of t (the extra rounds of a wave
+// maximum cost more than the reads they overlap).
 //  3. Softmax at the temperature, the shortest prefix reaching top_p, inversion at u.
 constexpr int kSampleThreads = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxTilesPerGroup = 8;   // rows <= kHeadGrid x 16 x 8 = 262,144
-constexpr int kCandMax = kMaxTopK * kMaxTilesPerGroup * 16;
+constexpr int kCandWg = 64;                     // candidate workgroups the fast path holds
+constexpr int kCandMax = kCandWg * kMaxTilesPerGroup * 16;
+
+// The value of lane (lane ^ S) for a constant S, without the LDS: DPP for S = 1, 2 (quad
+// permutes) and 8 (rotation by 8 inside a row of 16), the swizzle unit for S = 4, and the
+// lane-group swaps for S = 16 and 32.
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false);
+  else if constexpr (S == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (4 << 10));
+  else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // {(r0, r0, r2, r2), (r1, r1, r3, r3)}
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(S == 32, "strides 1 .. 32");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // {(r0, r1, r0, r1), (r2, r3, r2, r3)}
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, int lane) {
+  return (unsigned long long)xor_lane<S>((uint32_t)v, lane) | ((unsigned long long)xor_lane<S>((uint32_t)(v >> 32), lane) << 32);
+}
+
+// One compare-exchange stage of a bitonic network at a constant stride S: lanes whose keep_max
+// holds take the larger of their key and lane (lane ^ S)'s.
+template <int S>
+__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long key, bool keep_max, int lane) {
+  const unsigned long long o = xor_lane64<S>(key, lane);
+  return keep_max ? (o > key ? o : key) : (o < key ? o : key);
+}
+template <int S>
+__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int size, int lane) {
+  // the strides S, S/2, .. 1 of merging blocks of `size` (descending where lane & size is 0)
+  key = bitonic_step<S>(key, ((lane & S) == 0) == ((lane & size) == 0), lane);
+  if constexpr (S > 1) key = bitonic_merge_desc<S / 2>(key, size, lane);
+  return key;
+}
+
+// Bitonic sort of one 64-bit key per lane across a wave, descending (lane 0 the largest).
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key, int lane) {
+  key = bitonic_merge_desc<1>(key, 2, lane);
+  key = bitonic_merge_desc<2>(key, 4, lane);
+  key = bitonic_merge_desc<4>(key, 8, lane);
+  key = bitonic_merge_desc<8>(key, 16, lane);
+  key = bitonic_merge_desc<16>(key, 32, lane);
+  key = bitonic_merge_desc<32>(key, 64, lane);   // lane & 64 is 0: descending throughout
+  return key;
+}
+
+// The largest of one 64-bit key per lane, in every lane.
+__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v, int lane) {
+  unsigned long long o = xor_lane64<1>(v, lane);
+  v = o > v ? o : v;
+  o = xor_lane64<2>(v, lane);
+  v = o > v ? o : v;
+  o = xor_lane64<4>(v, lane);
+  v = o > v ? o : v;
+  o = xor_lane64<8>(v, lane);
+  v = o > v ? o : v;
+  o = xor_lane64<16>(v, lane);
+  v = o > v ? o : v;
+  o = xor_lane64<32>(v, lane);
+  return o > v ? o : v;
+}
 
 // The k-th largest (1 <= k <= n) of the n 64-bit keys a[0 .. n) in LDS, by radix select on 8-bit
 // digits from the top (a histogram per digit; the digit where the count from above reaches k).
@@ -238,76 +310,115 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     float temperature, int top_k, float top_p, const float* __restrict__ u, const int* __restrict__ draft,
     int* __restrict__ token_out, int* __restrict__ topk_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
     int* __restrict__ tokens, unsigned* __restrict__ counter) {
+  constexpr int kWavesS = kSampleThreads / kWave;
+  constexpr int kPer = kHeadGrid / kSampleThreads;   // keys per thread
+  static_assert(kPer == 4, "four keys per lane: a wave's maxima fit its four rounds");
   __shared__ unsigned long long s_a[kHeadGrid];
   __shared__ unsigned long long s_c[kCandMax];
   __shared__ unsigned long long s_top[kMaxTopK];
+  __shared__ unsigned long long s_w[kWavesS][kPer];
   __shared__ unsigned s_hist[2][256];
-  __shared__ unsigned long long s_sel;
+  __shared__ unsigned long long s_sel, s_t;
   __shared__ int s_need, s_nwg, s_nc, s_ntop;
-  __shared__ int s_wg[kMaxTopK];
+  __shared__ int s_wg[kCandWg];
   __shared__ bool s_last;
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const long long ntiles = (rows + 15) >> 4;
   const int tpg = (int)((ntiles + G - 1) / G);   // tiles per head workgroup (host: <= 8)
   const int k = (int)(top_k < rows ? top_k : rows);
   const float* lg = logits + (size_t)m * rows;
-  {
-    // all loads first (addresses past G repeat the last key), then the LDS stores
-    constexpr int kPer = kHeadGrid / kSampleThreads;
-    unsigned long long kv[kPer];
+  // 1. t = a lower bound of the k-th largest of the G workgroup keys (keys are distinct and
+  // nonzero; 0 pads past G): each wave takes its j = ceil(k / 8) largest keys (j rounds of a wave
+  // maximum), and t is the k-th largest of those 8j. They are 8j >= k keys, so at least k keys
+  // reach t; and t is at most the k-th largest of all G. Every key of the token's top k is then
+  // >= t and lies in a workgroup whose maximum reaches t; there are k of those when the waves
+  // split the top k evenly, a few more otherwise. More than kCandWg: t becomes the exact k-th
+  // largest (radix select), and exactly k workgroups reach it.
+  const int jw = (k + kWavesS - 1) / kWavesS;   // <= 4
+  unsigned long long kv[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) kv[j] = keys[(size_t)m * G + min(tid + j * kSampleThreads, G - 1)];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (tid + j * kSampleThreads < G) s_a[tid + j * kSampleThreads] = kv[j];
+  for (int q = 0; q < kPer; ++q) {
+    const int i = tid + q * kSampleThreads;
+    kv[q] = keys[(size_t)m * G + min(i, G - 1)];
+    if (i >= G) kv[q] = 0ull;
   }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) s_a[tid + q * kSampleThreads] = kv[q];
   if (tid == 0) {
     s_nwg = 0;
     s_nc = 0;
     s_ntop = 0;
   }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    if (r < jw) {
+      unsigned long long mx = kv[0];
+#pragma unroll
+      for (int q = 1; q < kPer; ++q) mx = kv[q] > mx ? kv[q] : mx;
+      mx = wave_max64(mx, lane);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (kv[q] == mx) kv[q] = 0ull;   // keys are distinct: one lane, one register (or all zeros)
+      if (lane == 0) s_w[wave][r] = mx;
+    }
+  }
   __syncthreads();
-  // 1. the workgroups that can hold the top k (keys are distinct and nonzero)
-  const unsigned long long t = G > k ? block_kth_largest(s_a, G, k, s_hist, &s_sel, &s_need) : 0ull;
+  if (wave == 0) {
+    const int w = lane >> 2, r = lane & 3;
+    const unsigned long long key = wave_sort_desc(w < kWavesS && r < jw ? s_w[w][r] : 0ull, lane);
+    const unsigned long long kth = __shfl(key, k - 1, kWave);
+    if (lane == 0) s_t = G > k ? kth : 0ull;
+  }
+  __syncthreads();
+  unsigned long long t = s_t;
   for (int b = tid; b < G; b += kSampleThreads)
-    if (s_a[b] >= t) s_wg[atomicAdd(&s_nwg, 1)] = b;
+    if (s_a[b] >= t) {
+      const int at = atomicAdd(&s_nwg, 1);
+      if (at < kCandWg) s_wg[at] = b;
+    }
   __syncthreads();
-  // 2. their rows' keys that reach t, then the k largest of those
+  if (s_nwg > kCandWg) {
+    // the waves' maxima were too uneven: the exact k-th largest, reached by exactly k workgroups
+    t = block_kth_largest(s_a, G, k, s_hist, &s_sel, &s_need);
+    if (tid == 0) s_nwg = 0;
+    __syncthreads();
+    for (int b = tid; b < G; b += kSampleThreads)
+      if (s_a[b] >= t) s_wg[atomicAdd(&s_nwg, 1)] = b;
+    __syncthreads();
+  }
+  // 2. their rows' keys that reach t (at least k; a few more at most, in practice), then the k
+  // largest of those: one wave sort when they fit in a wave, else a radix select first
   const int nwg = s_nwg, per = tpg * 16;
   {
-    constexpr int kPer = kCandMax / kSampleThreads;
-    long long row[kPer];
-    float v[kPer];
+    constexpr int kPerC = kCandMax / kSampleThreads;
+    long long row[kPerC];
+    float v[kPerC];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kPerC; ++j) {
       const int i = tid + j * kSampleThreads;
       const long long tile = i < nwg * per ? s_wg[i / per] + (long long)((i % per) >> 4) * G : ntiles;
       row[j] = tile < ntiles && tile * 16 + (i & 15) < rows ? tile * 16 + (i & 15) : -1;
-      v[j] = lg[row[j] < 0 ? 0 : row[j]];
+      v[j] = row[j] >= 0 ? lg[row[j]] : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kPerC; ++j) {
       const unsigned long long key = rank_key(sel_key(v[j]), (int)row[j]);
       if (row[j] >= 0 && key >= t) s_c[atomicAdd(&s_nc, 1)] = key;
     }
   }
   __syncthreads();
   const int nc = s_nc;   // >= k
-  const unsigned long long tk = block_kth_largest(s_c, nc, k, s_hist, &s_sel, &s_need);
-  for (int i = tid; i < nc; i += kSampleThreads)
-    if (s_c[i] >= tk) s_top[atomicAdd(&s_ntop, 1)] = s_c[i];
-  __syncthreads();
+  const unsigned long long* top = s_c;
+  if (nc > kWave) {
+    const unsigned long long tk = block_kth_largest(s_c, nc, k, s_hist, &s_sel, &s_need);
+    for (int i = tid; i < nc; i += kSampleThreads)
+      if (s_c[i] >= tk) s_top[atomicAdd(&s_ntop, 1)] = s_c[i];
+    __syncthreads();
+    top = s_top;
+  }
   // 3. wave 0: the k keys in order (bitonic sort across the lanes, descending), then the sample
   if (wave == 0) {
-    unsigned long long key = lane < k ? s_top[lane] : 0ull;
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1)
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const unsigned long long o = __shfl_xor(key, stride, kWave);
-        const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
-        key = keep_max ? (o > key ? o : key) : (o < key ? o : key);
-      }
+    const unsigned long long key = wave_sort_desc(lane < (nc > kWave ? k : nc) ? top[lane] : 0ull, lane);
     const int row = (int)(0xffffffffu - (uint32_t)key);
     const float v = key_to_float((uint32_t)(key >> 32));
     const float v0 = __shfl(v, 0, kWave);
@@ -659,3 +770,4 @@ extern "C" int lmhead_gemv_bf16(const qws_lmhead* head, const void* x_bf16, int 
   }
   return qws_host::check_launch();
 }
+
