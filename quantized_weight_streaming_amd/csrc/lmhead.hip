@@ -231,15 +231,21 @@ __device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long 
   return key;
 }
 
-// The largest of one 64-bit key per lane, in every lane.
+// The largest of one 64-bit key per lane, in every lane: quad swaps, then the mirrors inside
+// half-rows and rows (each lane then holds the maximum of its 8, then 16), then the lane-group
+// swaps; all without the LDS.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  return (unsigned long long)dpp<CTRL>((uint32_t)v) | ((unsigned long long)dpp<CTRL>((uint32_t)(v >> 32)) << 32);
+}
 __device__ __forceinline__ unsigned long long wave_max64(unsigned long long v, int lane) {
-  unsigned long long o = xor_lane64<1>(v, lane);
+  unsigned long long o = dpp64<0xB1>(v);
   v = o > v ? o : v;
-  o = xor_lane64<2>(v, lane);
+  o = dpp64<0x4E>(v);
   v = o > v ? o : v;
-  o = xor_lane64<4>(v, lane);
+  o = dpp64<0x141>(v);
   v = o > v ? o : v;
-  o = xor_lane64<8>(v, lane);
+  o = dpp64<0x140>(v);
   v = o > v ? o : v;
   o = xor_lane64<16>(v, lane);
   v = o > v ? o : v;
@@ -389,7 +395,28 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   // 2. their rows' keys that reach t (at least k; a few more at most, in practice), then the k
   // largest of those: one wave sort when they fit in a wave, else a radix select first
   const int nwg = s_nwg, per = tpg * 16;
-  {
+  if ((rows & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) {
+    // four rows per load: slot i = quarter i % 4 of tile i / 4 of the candidates' tiles (16-byte
+    // aligned: the logits are, and every position's start at a multiple of 4 rows; a quarter is
+    // whole rows or none, since rows is a multiple of 4)
+    constexpr int kPerQ = kCandMax / 4 / kSampleThreads;
+    long long r0[kPerQ];
+    f32x4_t v[kPerQ];
+#pragma unroll
+    for (int j = 0; j < kPerQ; ++j) {
+      const int i = tid + j * kSampleThreads, ti = i >> 2;
+      const long long tile = ti < nwg * tpg ? s_wg[ti / tpg] + (long long)(ti % tpg) * G : ntiles;
+      r0[j] = tile < ntiles && tile * 16 + 4 * (i & 3) < rows ? tile * 16 + 4 * (i & 3) : -1;
+      v[j] = r0[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(lg + r0[j]) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int j = 0; j < kPerQ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned long long key = rank_key(sel_key(v[j][e]), (int)(r0[j] + e));
+        if (r0[j] >= 0 && key >= t) s_c[atomicAdd(&s_nc, 1)] = key;
+      }
+  } else {
     constexpr int kPerC = kCandMax / kSampleThreads;
     long long row[kPerC];
     float v[kPerC];
