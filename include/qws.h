@@ -53,7 +53,7 @@ enum qws_format {
   QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634, /* e2m1 nibbles + one E8M0 scale per 32 elements */
   QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845, /* E4M3 (OCP "FN") codes, row-major, + one fp32 scale per row */
   QWS_FMT_BF16 = 0x42463136,                /* plain bf16 */
-  QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654, /* MXFP4 experts, task-major (moe_pack_mxfp4) */
+  QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584655, /* MXFP4 experts, task-major (moe_pack_mxfp4) */
   QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 = 0x46503854 /* E4M3 codes in 16-row tiles (below) + fp32 row scales */
 };
 
@@ -153,13 +153,15 @@ int moe_expert_gemv_mxfp4(const qws_mxfp4_experts* w, const void* x_bf16, int M,
  * bytes:
  *   out[(e * I/32 + j) * QWS_TASK_BYTES + ((p * 16 + w) * 64 + l) * 16 + b],  p < 8 pieces,
  * with w = 4 rg + ks, l = 16 g + i:
- *   p 0     bytes 0..7: 4-byte words q = 8, 9 (below); bytes 8..12: the scales of the five
- *           gate/up chunks of p 1..5; bytes 13 + k, k < 3: the scale of down row
- *           16 (w + 16 q) + i in block j for q = 3 g + k (zero for q > 9);
+ * The down projection is cut into the 16-row tiles q = 0 .. 9 of each wave: tile q of wave w is
+ * down rows 16 (w + 16 q) .. +15, and "row i of tile q" means those rows' 16 bytes (32 codes) in
+ * columns 32j .. 32j+31:
+ *   p 0     bytes 0..7: bytes 8 (g >> 1) .. 8 (g >> 1) + 7 of row i of tile 8 + (g & 1); bytes
+ *           8..12: the scales of the five gate/up chunks of p 1..5; byte 13 + Q, Q < 3: the
+ *           scale of row i of tile 4 Q + g in block j (zero for 4 Q + g > 9);
  *   p 1..5  gate/up codes: row i of row group rg (gate 32j + 16 rg + i for rg < 2, else up
  *           I + 32j + 16 (rg - 2) + i), 16-byte chunk 20 ks + 4 (p - 1) + g of the row;
- *   p 6, 7  4-byte words q = 4 (p - 6) .. +3: word q is bytes 4g .. 4g+3 of down row
- *           16 (w + 16 q) + i in its columns 32j .. 32j+31.
+ *   p 6, 7  row i of tile 4 (p - 6) + g.
  * Chunks, rows and scales past H are zero. n = n_routed + has_shared; H <= 2560 (16 x 5 x 32
  * elements per row), I a multiple of 32. desc_out receives `src` with format
  * QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR, gate_up_q = out and the other three pointers NULL.
@@ -182,10 +184,13 @@ int moe_pack_mxfp4(const qws_mxfp4_experts* src, unsigned char* out, size_t out_
  * cores: gate/up on the scaled FP4 x FP8 instruction, the e2m1 codes and E8M0 scales as stored
  * against x written as two E4M3 parts per element with one E8M0 scale per 32 (exact for every
  * element within 2^13 of its block's largest magnitude, smaller ones rounded at 2^-16 of it);
- * down on bf16 operands, the fp32 SwiGLU activation entering as the exact sum of three bf16
- * parts. The instruction's internal accumulation is a little coarser than float32 (about 1e-4 of
- * one op's largest output, measured), so results agree with moe_expert_gemv_mxfp4 to ~1e-5 of
- * max|y|, not bit for bit; the order is fixed, so repeated launches agree bit for bit.
+ * down on the same instruction with the formats swapped, the codes as stored against the fp32
+ * SwiGLU activation written as four E4M3 parts per element (the next four significant bits each,
+ * the last rounded; one E8M0 scale per part and 32 activations: the sum is the activation to
+ * ~2^-16 of its block's largest). The instruction's internal accumulation is a little coarser
+ * than float32 (about 1e-4 of one op's largest output, measured), so results agree with
+ * moe_expert_gemv_mxfp4 to ~1e-5 of max|y|, not bit for bit; the order is fixed, so repeated
+ * launches agree bit for bit. Non-finite activations are not supported.
  * -------------------------------------------------------------------------------------------*/
 typedef struct {
   const void* x_bf16;         /* [M, H] bf16, ready before the launch                               */

@@ -20,7 +20,7 @@ QWS_ERR_COMPILE = -8
 QWS_FMT_MXFP4_E2M1_E8M0_B32 = 0x4D584634
 QWS_FMT_FP8_E4M3FN_ROWSCALE = 0x46503845
 QWS_FMT_BF16 = 0x42463136
-QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584654
+QWS_FMT_MXFP4_E2M1_E8M0_B32_TASKMAJOR = 0x4D584655
 QWS_FMT_FP8_E4M3FN_ROWSCALE_T16 = 0x46503854
 QWS_TASK_BYTES = 131072
 

@@ -26,26 +26,27 @@ __global__ void pack_tasks_kernel(const uint8_t* __restrict__ gq, const uint8_t*
     // gate/up row of this lane and its chunk for step t
     const long long grow = e * 2 * I + (rg >= 2 ? I : 0) + (long long)kBlk * j + 16 * (rg & 1) + i;
     auto gu_chunk = [&](int t) { return kGuCpk * ks + 4 * t + g; };
-    // word g of down row 16 (w + 16 q) + i in block j (0 past H)
-    auto down_word = [&](int q) -> uint32_t {
+    // 4-byte word d (bytes 4d .. 4d+3) of down row 16 (w + 16 q) + i in block j (0 past H)
+    auto down_word = [&](int q, int d) -> uint32_t {
       const int row = 16 * (w + kWaves * q) + i;
-      if (row >= H) return 0u;
-      const uint8_t* src = dq + (e * H + row) * dn_row + 16 * j + 4 * g;
+      if (q >= kDnTpw || row >= H) return 0u;
+      const uint8_t* src = dq + (e * H + row) * dn_row + 16 * j + 4 * d;
       return (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) | ((uint32_t)src[3] << 24);
     };
     uint32_t v[4] = {0u, 0u, 0u, 0u};
     if (p == 0) {
-      v[0] = down_word(8);
-      v[1] = down_word(9);
+      // tiles 8, 9: lane group g holds half g >> 1 (bytes 8 (g >> 1) ..) of tile 8 + (g & 1)
+      v[0] = down_word(8 + (g & 1), 2 * (g >> 1));
+      v[1] = down_word(8 + (g & 1), 2 * (g >> 1) + 1);
       uint8_t tail[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int t = 0; t < kGuCpl; ++t) {
         const int c = gu_chunk(t);
         tail[t] = c < nch ? gs[grow * gu_srow + c] : 0;
       }
-      for (int k = 0; k < 3; ++k) {
-        const int q = 3 * g + k;       // down scale of tile q, row i
+      for (int Q = 0; Q < 3; ++Q) {
+        const int q = 4 * Q + g;       // down scale of tile q, row i
         const int row = 16 * (w + kWaves * q) + i;
-        tail[5 + k] = (q < kDnTpw && row < H) ? ds[(e * H + row) * dn_srow + j] : 0;
+        tail[5 + Q] = (q < kDnTpw && row < H) ? ds[(e * H + row) * dn_srow + j] : 0;
       }
       for (int b = 0; b < 8; ++b) v[2 + (b >> 2)] |= (uint32_t)tail[b] << (8 * (b & 3));
     } else if (p <= kGuCpl) {
@@ -55,7 +56,8 @@ __global__ void pack_tasks_kernel(const uint8_t* __restrict__ gq, const uint8_t*
         for (int b = 0; b < 16; ++b) v[b >> 2] |= (uint32_t)src[b] << (8 * (b & 3));
       }
     } else {
-      for (int d = 0; d < 4; ++d) v[d] = down_word(4 * (p - kGuCpl - 1) + d);
+      // row i of tile 4 (p - 6) + g, all 16 bytes
+      for (int d = 0; d < 4; ++d) v[d] = down_word(4 * (p - kGuCpl - 1) + g, d);
     }
     *reinterpret_cast<u32x4_t*>(out + x * 16) = u32x4_t{v[0], v[1], v[2], v[3]};
   }

@@ -437,9 +437,9 @@ __device__ __forceinline__ uint32_t ldb_stream(const uint8_t* p) {
 constexpr int kGuCpk = 4 * kGuCpl;            // chunks of a row per k-slice: H <= 4 * 20 * 32
 constexpr int kDnTpw = kHMax / 16 / kWaves;   // down-projection row tiles (16 rows) per wave
 constexpr int kPieces = 8;                    // 16-byte pieces per lane of a task record
-// a lane's down sums kept across a task group: 10 tiles (bf16 down) or 3 ops x up to 4 tokens (W4A8)
+// a lane's down sums kept across a task group: 3 ops x up to 4 tokens (W4A8) or up to 3 x 4 ops
 template <bool A8>
-constexpr int kOutv = A8 ? 12 : kDnTpw;
+constexpr int kOutv = 12;
 // At M = 1 the shared expert's J tasks run before selection on the last J workgroups (the routed
 // tasks leave them idle). With more tokens the union needs most workgroups for several tasks, so
 // the shared expert joins the grouped task pool after selection instead.
@@ -528,11 +528,6 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
   // the next task's (nrec) gate/up pieces load into these registers during this task's down
   // projection, its down pieces after it; the down-phase words of piece 0 are kept first
   const uint32_t dn8 = r.p[0][0], dn9 = r.p[0][1], dsw = r.p[0][3];
-  u32x4_t dq0 = {0u, 0u, 0u, 0u}, dq1 = dq0;
-  if constexpr (A8) {
-    dq0 = r.p[6];
-    dq1 = r.p[7];
-  }
   if (nrec) task_load<0, kPieces - 2>(nrec, r);
   __syncthreads();
 
@@ -544,36 +539,48 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
   // line of memory, and a row owner reads its R consecutive words of every line)
   const int nsm = kEarlyShared<M> && sh.has_shared ? M : 0;
   const int ntile = H >> 4;
-  if constexpr (A8) {
-    // a = silu(gate) * up in fp32, then MXFP8 per token: the block of 32 is this task's (the down
-    // weights' MX block), its scale 2^(e - 127 - 8) for the largest exponent field e of the 32
-    // (byte e - 8, at least 0), each code the nearest E4M3 value of a / scale (ties to even,
-    // clamped at 448). Lanes 32m .. 32m+31 hold token m's activations.
-    uint8_t* a8 = reinterpret_cast<uint8_t*>(gu_s + 4 * M * 64);   // [M][32] codes, then [M] scale bytes
-    if (tid < 32 * M) {
-      const int am = tid >> 5, k = tid & 31;
-      const float* gp = gu_s + am * 64 + k;
-      float gate = gp[0], up = gp[32];
+  // The activations of the slot's tokens go to LDS as E4M3 codes with E8M0 scales per (token,
+  // part): one part (W4A8: the MXFP8 value), or four parts whose sum is the float32 activation to
+  // ~2^-16 of the block's largest (each part the next four significant bits, truncated, the last
+  // rounded; scale byte e - 7 - 4p for the block's largest exponent field e: parts of every
+  // activation within 2^13 of the largest are E4M3 values exactly). Lanes 32m .. 32m+31 hold
+  // token m's 32 activations.
+  constexpr int NP = A8 ? 1 : 4;
+  uint8_t* a8 = reinterpret_cast<uint8_t*>(gu_s + 4 * M * 64);   // [M][NP][32] codes, then [M][NP] scale bytes
+  constexpr int kScaleAt = M * NP * 32;   // M * 132 bytes in all, within the M * 256 the layout reserves
+  if (tid < 32 * M) {
+    const int am = tid >> 5, k = tid & 31;
+    const float* gp = gu_s + am * 64 + k;
+    float gate = gp[0], up = gp[32];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        gate += gp[q * M * 64];
-        up += gp[q * M * 64 + 32];
+    for (int q = 1; q < 4; ++q) {
+      gate += gp[q * M * 64];
+      up += gp[q * M * 64 + 32];
+    }
+    const bool in = M == 1 || ((mask >> am) & 1u);
+    const float av = in ? silu(gate) * up : 0.0f;
+    uint32_t e = (__float_as_uint(av) >> 23) & 0xffu;
+    e = max(e, dpp<0xB1>(e));    // lanes 8k .. 8k+7
+    e = max(e, dpp<0x4E>(e));
+    e = max(e, dpp<0x141>(e));
+    e = max(e, dpp<0x140>(e));   // row mirror: lanes 16k .. 16k+15
+    const auto pr = __builtin_amdgcn_permlane16_swap(e, e, false, false);   // rows 2k and 2k+1
+    e = max(pr[0], pr[1]);
+    float rem = av;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      // W4A8: 2^(e - 127 - 8), the OCP MX scale; parts: 2^(e - 127 - 7 - 4p)
+      const uint32_t sb = A8 ? (e >= 8u ? e - 8u : 0u) : (e >= 7u + 4u * p ? e - 7u - 4u * p : 0u);
+      float part = rem;
+      if (p + 1 < NP) {
+        part = __uint_as_float(__float_as_uint(rem) & 0xfff00000u);   // the top four significant bits
+        rem -= part;                                                   // exact
       }
-      const bool in = M == 1 || ((mask >> am) & 1u);
-      const float av = in ? silu(gate) * up : 0.0f;
-      uint32_t e = (__float_as_uint(av) >> 23) & 0xffu;
-      e = max(e, dpp<0xB1>(e));    // lanes 8k .. 8k+7
-      e = max(e, dpp<0x4E>(e));
-      e = max(e, dpp<0x141>(e));
-      e = max(e, dpp<0x140>(e));   // row mirror: lanes 16k .. 16k+15
-      const auto pr = __builtin_amdgcn_permlane16_swap(e, e, false, false);   // rows 2k and 2k+1
-      e = max(pr[0], pr[1]);
-      const uint32_t sb = e >= 8u ? e - 8u : 0u;
-      const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb)
-      const uint8_t code = (uint8_t)(f32x2_to_e4m3x2<false>(av * inv, 0.0f, 0u) & 0xffu);
-      a8[am * 32 + k] = code;
-      if (k == 0) a8[kMaxM * 32 + am] = (uint8_t)sb;
-      if (w.act && in) {
+      const float inv = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb): exact, normal for sb <= 247
+      const uint8_t code = (uint8_t)(f32x2_to_e4m3x2<false>(part * inv, 0.0f, 0u) & 0xffu);
+      a8[(am * NP + p) * 32 + k] = code;
+      if (k == 0) a8[kScaleAt + am * NP + p] = (uint8_t)sb;
+      if (A8 && w.act && in) {
         // diagnostics: this token's activation, code and scale of expert un.id[u], block jblk
         const size_t na = (size_t)(sh.E + 1) * M * sh.I, at = ((size_t)un.id[u] * M + am) * sh.I + kBlk * jblk + k;
         w.act[at] = av;
@@ -581,22 +588,27 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
         if (k == 0) reinterpret_cast<uint8_t*>(w.act + na)[na + at / kBlk] = (uint8_t)sb;
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
 
-    // down on the scaled instruction, 64 rows per op, activations as A (FP8) and weights as B
-    // (FP4). B block b = 16-row tile 4Q + b of this wave's tiles w + 16 q (q < 10: ops Q = 0, 1
-    // take q 0 .. 7, op 2 takes q 8, 9 in blocks 0, 1), column n = tile row n, the task's 32 codes.
-    // A row 4 bq + c holds token c's 32 codes in block bq and zeros elsewhere, so D row 4 bq + c,
-    // column n is row n of tile 4Q + bq for token c: lane (g, n) holds it in register c for bq = g,
-    // and one store instruction per token writes four whole 16-row lines. The record gives lane
-    // (g, n) word g (codes 8g .. 8g+7) of row n of each tile; two lane-group swaps per register
-    // pair turn four such words into one row's 16 bytes.
+  // down on the scaled instruction: activations as A (FP8), weights as B (FP4), 64 output rows
+  // per op. B block b = row n of tile 4Q + b of this wave's tiles w + 16 q, exactly as the record
+  // holds it (Q = 0, 1: pieces 6 and 7; Q = 2: tiles 8 and 9, whose second halves come from lane
+  // groups 2 and 3 by one lane-group swap), its scale the lane's byte 13 + Q of piece 0. A row i
+  // holds one (tile slot, token, part)'s 32 codes in that tile slot's block and zeros elsewhere,
+  // so D row i, column n is that tile row for that token and part.
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const uint32_t sw8 = __builtin_amdgcn_permlane32_swap(dn8, dn8, false, false)[1];
+  const uint32_t sw9 = __builtin_amdgcn_permlane32_swap(dn9, dn9, false, false)[1];
+  const u32x4_t wq[3] = {r.p[6], r.p[7], u32x4_t{dn8, dn9, sw8, sw9}};
+  if constexpr (A8) {
+    // A row 4 bq + c: token c's codes in block bq (T = 4 tiles per op, all tokens in one op);
+    // lane (g, n) register c of D is token c's sum for row n of tile 4Q + g
     const int ca = n & 3, ba = n >> 2;
     const bool toka = ca < M && (M == 1 || ((mask >> ca) & 1u));
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
     const u32x4_t av16 = toka ? *reinterpret_cast<const u32x4_t*>(a8 + min(ca, M - 1) * 32 + 16 * (g & 1)) : zero;
     const u32x4_t alo = ba == (g >> 1) ? av16 : zero, ahi = ba == 2 + (g >> 1) ? av16 : zero;
-    const uint32_t asc = a8[kMaxM * 32 + min(ca, M - 1)];
+    const uint32_t asc = a8[kScaleAt + min(ca, M - 1)];
     unsigned long long* pdst[M];
     float wt[M];
 #pragma unroll
@@ -607,105 +619,64 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
     }
 #pragma unroll
     for (int Q = 0; Q < 3; ++Q) {
-      uint32_t v0 = Q == 0 ? dq0[0] : (Q == 1 ? dq1[0] : dn8), v1 = Q == 0 ? dq0[1] : (Q == 1 ? dq1[1] : dn9);
-      uint32_t v2 = Q == 0 ? dq0[2] : (Q == 1 ? dq1[2] : 0u), v3 = Q == 0 ? dq0[3] : (Q == 1 ? dq1[3] : 0u);
-      // 4 x 4 transpose of (lane group, register): register t of group g = word g of tile 4Q + t
-      const auto p02 = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
-      const auto p13 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
-      const auto p01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
-      const auto p23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
-      const u32x4_t wrow = {p01[0], p01[1], p23[0], p23[1]};   // group b: words 0 .. 3 of tile 4Q + b, row n
-      // this lane's weight scale (tile q = 4Q + g, row n) is held by lane n + 16 (q / 3), in byte
-      // 1 + q % 3 of its first piece's last word
-      const int q = min(4 * Q + g, kDnTpw - 1);
-      const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
-      const uint32_t bsc = (sw >> (8 + 8 * (q % 3))) & 0xffu;
-      f32x4_t dd = mfma_fp8_fp4(alo, ahi, wrow, asc, bsc, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      f32x4_t dd = mfma_fp8_fp4(alo, ahi, wq[Q], asc, (dsw >> (8 + 8 * Q)) & 0xffu, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
       mfma_result(dd);
-      const int rt = wave + kWaves * (4 * Q + g);
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        outv[Q * M + m] = first ? dd[m] : outv[Q * M + m] + dd[m];
-        if (last && (M == 1 || ((mask >> m) & 1u)) && 4 * Q + g < kDnTpw && rt < ntile)
-          st_coherent(pdst[m] + rt * 16 + n, tagged(tag, __float_as_uint(wt[m] * outv[Q * M + m])));
+      for (int m = 0; m < M; ++m) outv[Q * M + m] = first ? dd[m] : outv[Q * M + m] + dd[m];
+    }
+    // the stores after every product: a use of the record's registers after a store would make the
+    // compiler wait for the store's acknowledgement too (vector memory counts both)
+    if (last) {
+#pragma unroll
+      for (int Q = 0; Q < 3; ++Q) {
+        const int rt = wave + kWaves * (4 * Q + g);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          if ((M == 1 || ((mask >> m) & 1u)) && 4 * Q + g < kDnTpw && rt < ntile)
+            st_coherent(pdst[m] + rt * 16 + n, tagged(tag, __float_as_uint(wt[m] * outv[Q * M + m])));
       }
     }
   } else {
-    // a = silu(gate) * up in fp32, once per (token, activation), split exactly into three bf16 parts
-    // (hi + mid + lo, each truncated from the remainder), so the down products below stay exact fp32
-    // products of a. a_s holds them as the down MFMA's A rows: row 4m + s = part s of token m (s = 3
-    // and tokens outside the slot: zero), 32 activations each.
-    uint16_t* a_s = reinterpret_cast<uint16_t*>(gu_s + 4 * M * 64);
-    if (tid < 32 * M) {
-      const int am = tid >> 5, k = tid & 31;
-      const float* gp = gu_s + am * 64 + k;
-      float gate = gp[0], up = gp[32];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        gate += gp[q * M * 64];
-        up += gp[q * M * 64 + 32];
-      }
-      const bool in = M == 1 || ((mask >> am) & 1u);
-      const float av = in ? silu(gate) * up : 0.0f;
-      const float hi = __uint_as_float(__float_as_uint(av) & 0xffff0000u);
-      const float r1 = av - hi;
-      const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
-      const float r2 = r1 - mid;
-      uint16_t* ap = a_s + am * 4 * 32 + k;
-      ap[0] = (uint16_t)(__float_as_uint(hi) >> 16);
-      ap[32] = (uint16_t)(__float_as_uint(mid) >> 16);
-      ap[64] = (uint16_t)(__float_as_uint(r2) >> 16);
-      ap[96] = 0;
-    }
-    __syncthreads();
-
-    // down: A = the activation parts (lane (g, n): row n = 4m + s, k = 8g .. 8g+7), B = 16 down rows
-    // of the block (column n = tile row n); lane (g, n) of D then holds token g's three parts of
-    // tile row n.
-    const u32x4_t ab = n < 4 * M ? *reinterpret_cast<const u32x4_t*>(a_s + n * 32 + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
-    // D lane (g, n) holds token g's three parts of tile row n. With fewer than four tokens the D
-    // rows of absent tokens are empty, so the results of T = 4 / MP tiles are gathered into one
-    // register first: lane (g, n) then holds token g % MP of tile slot g / MP, and one store
-    // instruction per T tiles has every row of lanes busy.
+    // A row i = (tile slot i / (4 MP), token (i / 4) % MP, part i % 4): T = 4 / MP tiles per op, MP
+    // ops per group of four tiles. Lane (g, n) of D holds the four parts of (tile slot g / MP,
+    // token g % MP) for row n: their sum is that token's partial for the row.
     constexpr int T = 4 / MP;
-    const int mt = g % MP;
-    const bool tok = mt < M && (M == 1 || ((mask >> mt) & 1u));
-    const float wt = un.w[u][min(mt, M - 1)];
-    const int pm = un.pair0[u] + __popc(mask & ((1u << mt) - 1u));
+    const int bl = n / (4 * MP), ma = (n >> 2) % MP, pa = n & 3;
+    const bool toka = ma < M && (M == 1 || ((mask >> ma) & 1u));
+    const u32x4_t av16 =
+        toka ? *reinterpret_cast<const u32x4_t*>(a8 + (min(ma, M - 1) * NP + pa) * 32 + 16 * (g & 1)) : zero;
+    const uint32_t asc = a8[kScaleAt + min(ma, M - 1) * NP + pa];
+    const int mg = g % MP, bg = g / MP;
+    const bool tokg = mg < M && (M == 1 || ((mask >> mg) & 1u));
+    const float wt = un.w[u][min(mg, M - 1)];
+    const int pm = un.pair0[u] + __popc(mask & ((1u << mg) - 1u));
     unsigned long long* pdst =
         w.partial + (size_t)(pm < nsm ? pm * J + line_shared : line_routed + (pm - nsm) * sh.jg) * H;
 #pragma unroll
-    for (int q0 = 0; q0 < kDnTpw; q0 += T) {
-      float vt[T];
+    for (int Q = 0; Q < 3; ++Q)
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int q = q0 + t;
-        if (q < kDnTpw) {
-          // this lane's down scale (tile q, row n) is held by lane n + 16 (q / 3), in byte
-          // 13 + q % 3 of its first piece
-          const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((n + 16 * (q / 3)) << 2, (int)dsw);
-          const uint32_t code = q < 8 ? r.p[6 + q / 4][q % 4] : (q == 8 ? dn8 : dn9);
-          const float dsc = e8m0_normal_to_f32((sw >> (8 + 8 * (q % 3))) & 0xffu);
-          const f32x4_t dd = mfma_16x16x32(ab, fp4x8_to_bf16x8(code, dsc), f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-          vt[t] = (dd[0] + dd[1]) + dd[2];
-        } else {
-          vt[t] = 0.0f;
+      for (int o = 0; o < MP; ++o) {
+        if (Q == 2 && T * o >= 2) continue;   // tiles 10, 11 do not exist
+        const int blk = T * o + bl;            // this A row's block
+        const u32x4_t alo = blk == (g >> 1) ? av16 : zero, ahi = blk == 2 + (g >> 1) ? av16 : zero;
+        f32x4_t dd = mfma_fp8_fp4(alo, ahi, wq[Q], asc, (dsw >> (8 + 8 * Q)) & 0xffu, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+        mfma_result(dd);
+        const float v = (dd[0] + dd[1]) + (dd[2] + dd[3]);
+        // a workgroup's tasks of one group (same slot, consecutive blocks) add up in registers and
+        // store once, after the last
+        outv[Q * MP + o] = first ? v : outv[Q * MP + o] + v;
+      }
+    // the stores after every product (see above)
+    if (last) {
+#pragma unroll
+      for (int Q = 0; Q < 3; ++Q)
+#pragma unroll
+        for (int o = 0; o < MP; ++o) {
+          if (Q == 2 && T * o >= 2) continue;
+          const int qt = 4 * Q + T * o + bg, rt = wave + kWaves * qt;
+          if (tokg && qt < kDnTpw && rt < ntile)
+            st_coherent(pdst + rt * 16 + n, tagged(tag, __float_as_uint(wt * outv[Q * MP + o])));
         }
-      }
-      float v = vt[0];
-      if constexpr (T == 2) {
-        v = __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[1]), false, false)[0]);
-      } else if constexpr (T == 4) {
-        const uint32_t lo = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[0]), __float_as_uint(vt[2]), false, false)[0];
-        const uint32_t hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(vt[1]), __float_as_uint(vt[3]), false, false)[0];
-        v = __uint_as_float(__builtin_amdgcn_permlane16_swap(lo, hi, false, false)[0]);
-      }
-      // a workgroup's tasks of one group (same slot, consecutive blocks) add up in registers and
-      // store once, after the last
-      outv[q0 / T] = first ? v : outv[q0 / T] + v;
-      const int q = q0 + g / MP, rt = wave + kWaves * q;
-      if (last && tok && q < kDnTpw && rt < ntile)
-        st_coherent(pdst + rt * 16 + n, tagged(tag, __float_as_uint(wt * outv[q0 / T])));
     }
   }
   if (nrec) task_load<kPieces - 2, kPieces>(nrec, r);
