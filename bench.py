@@ -269,7 +269,19 @@ class DecodeStep:
 
 
 # ------------------------------------------------------------------------------------ traffic
-def traffic_for(kernel_src: str, name: str):
+def source_sha256(kernel_src) -> str:
+    """sha256 of a kernel's source file, or of several concatenated in the order given."""
+    h = hashlib.sha256()
+    for f in ([kernel_src] if isinstance(kernel_src, str) else kernel_src):
+        h.update(open(os.path.join(ROOT, "quantized_weight_streaming_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+# the fused MoE kernel: its device code and the host file that packs the records it reads
+MOE_SRC = ("moe_fused_kernel.hpp", "moe_fused.hip")
+
+
+def traffic_for(kernel_src, name: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was
     taken on the current source of the kernel (else None)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
@@ -280,8 +292,7 @@ def traffic_for(kernel_src: str, name: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "quantized_weight_streaming_amd", "csrc", kernel_src)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = source_sha256(kernel_src)
     if kv.get("source_sha256") != sha:
         return None
     try:
@@ -429,9 +440,9 @@ def main():
     # the dominant kernel of the step is the 42-layer MoE launch; the FP8 head follows in "breakdown"
     moe_bytes = sb - head_bytes(1)
     moe_gbs = moe_bytes / (r["moe_us_mean"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": f"moe_layers_kernel<1> ({args.layers} MoE layers, one launch)",
+    roofline = {"bound": "hbm", "kernel": f"qws_moe::moe_layers_kernel<1, false> ({args.layers} MoE layers, one launch)",
                 "achieved": round(moe_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(moe_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("moe_fused.hip", "moe_layers_kernel"),
+                "frac": round(moe_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for(MOE_SRC, "moe_layers_kernel"),
                 "algorithmic_bytes_per_launch": moe_bytes, "launch_us_mean": round(r["moe_us_mean"], 2)}
     head_launch_bytes = head_bytes(1)
     head_gbs = head_launch_bytes / (r["head_us_mean"] * 1e-6) / 1e9
@@ -500,7 +511,7 @@ def main():
             t["frac_of_peak"] = round(t["GBps"] / PEAK_HBM_GBS, 4)
             t["frac_of_nt_probe"] = round(t["GBps"] / breakdown["probe_read_nt_ceiling"]["GBps"], 4)
             if name == "moe_layer_m1_seed0":
-                t["traffic"] = traffic_for("moe_fused.hip", "moe_layers_kernel_single_layer")
+                t["traffic"] = traffic_for(MOE_SRC, "moe_layers_kernel_single_layer")
             breakdown[name] = t
             log(name, t)
         L2 = lay["moe_layer_m1_seed0"]
@@ -664,7 +675,7 @@ def main():
                                        "moe_us_per_layer": round(r4["moe_us_mean"] / args.layers, 3),
                                        "GBps": round(b4 / (r4["wall_ms"] * 1e-3) / 1e9, 1),
                                        "mean_union": round(float(np.mean([L.union() for L in step4.layers])), 2),
-                                       "moe_layers_traffic": traffic_for("moe_fused.hip", "moe_layers_kernel_m4"),
+                                       "moe_layers_traffic": traffic_for(MOE_SRC, "moe_layers_kernel_m4"),
                                        "moe_layers_algorithmic_bytes": b4 - head_bytes(4)}
         log("decode_step_m4", breakdown["decode_step_m4"])
         step4.w4a8 = True
