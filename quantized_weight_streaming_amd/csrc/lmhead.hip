@@ -182,55 +182,6 @@ constexpr int kMaxTilesPerGroup = 8;   // rows <= kHeadGrid x 16 x 8 = 262,144
 constexpr int kCandWg = 64;                     // candidate workgroups the fast path holds
 constexpr int kCandMax = kCandWg * kMaxTilesPerGroup * 16;
 
-// The value of lane (lane ^ S) for a constant S, without the LDS: DPP for S = 1, 2 (quad
-// permutes) and 8 (rotation by 8 inside a row of 16), the swizzle unit for S = 4, and the
-// lane-group swaps for S = 16 and 32.
-template <int S>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
-  if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false);
-  else if constexpr (S == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (4 << 10));
-  else if constexpr (S == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // {(r0, r0, r2, r2), (r1, r1, r3, r3)}
-    return (lane & 16) ? p[0] : p[1];
-  } else {
-    static_assert(S == 32, "strides 1 .. 32");
-    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // {(r0, r1, r0, r1), (r2, r3, r2, r3)}
-    return (lane & 32) ? p[0] : p[1];
-  }
-}
-template <int S>
-__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, int lane) {
-  return (unsigned long long)xor_lane<S>((uint32_t)v, lane) | ((unsigned long long)xor_lane<S>((uint32_t)(v >> 32), lane) << 32);
-}
-
-// One compare-exchange stage of a bitonic network at a constant stride S: lanes whose keep_max
-// holds take the larger of their key and lane (lane ^ S)'s.
-template <int S>
-__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long key, bool keep_max, int lane) {
-  const unsigned long long o = xor_lane64<S>(key, lane);
-  return keep_max ? (o > key ? o : key) : (o < key ? o : key);
-}
-template <int S>
-__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int size, int lane) {
-  // the strides S, S/2, .. 1 of merging blocks of `size` (descending where lane & size is 0)
-  key = bitonic_step<S>(key, ((lane & S) == 0) == ((lane & size) == 0), lane);
-  if constexpr (S > 1) key = bitonic_merge_desc<S / 2>(key, size, lane);
-  return key;
-}
-
-// Bitonic sort of one 64-bit key per lane across a wave, descending (lane 0 the largest).
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key, int lane) {
-  key = bitonic_merge_desc<1>(key, 2, lane);
-  key = bitonic_merge_desc<2>(key, 4, lane);
-  key = bitonic_merge_desc<4>(key, 8, lane);
-  key = bitonic_merge_desc<8>(key, 16, lane);
-  key = bitonic_merge_desc<16>(key, 32, lane);
-  key = bitonic_merge_desc<32>(key, 64, lane);   // lane & 64 is 0: descending throughout
-  return key;
-}
-
 // The largest of one 64-bit key per lane, in every lane: quad swaps, then the mirrors inside
 // half-rows and rows (each lane then holds the maximum of its 8, then 16), then the lane-group
 // swaps; all without the LDS.
@@ -370,8 +321,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   }
   __syncthreads();
   if (wave == 0) {
+    // the waves' maxima sit in lanes 4w + r < 32
+    static_assert(kWavesS * 4 <= 32, "one lane group of 32 holds the waves' maxima");
     const int w = lane >> 2, r = lane & 3;
-    const unsigned long long key = wave_sort_desc(w < kWavesS && r < jw ? s_w[w][r] : 0ull, lane);
+    const unsigned long long key = wave_sort_desc<32>(w < kWavesS && r < jw ? s_w[w][r] : 0ull, lane);
     const unsigned long long kth = __shfl(key, k - 1, kWave);
     if (lane == 0) s_t = G > k ? kth : 0ull;
   }
@@ -445,7 +398,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   }
   // 3. wave 0: the k keys in order (bitonic sort across the lanes, descending), then the sample
   if (wave == 0) {
-    const unsigned long long key = wave_sort_desc(lane < (nc > kWave ? k : nc) ? top[lane] : 0ull, lane);
+    const int n = nc > kWave ? k : nc;
+    const unsigned long long key = sort_candidates(lane < n ? top[lane] : 0ull, n, lane);
     const int row = (int)(0xffffffffu - (uint32_t)key);
     const float v = key_to_float((uint32_t)(key >> 32));
     const float v0 = __shfl(v, 0, kWave);

@@ -68,8 +68,15 @@ constexpr int kMaxRows = 16;    // output rows owned by one workgroup
 constexpr int kMaxGrid = 512;
 constexpr int kPollBatch = 8;   // tagged words per thread in flight while reading partials
 constexpr int kLine = 16;       // 64-bit words per 128-byte line: hand-off words of one writer share no line
+                                // (the one-token logits aside)
 static_assert(kMaxRows <= kLine, "an owner's rows of one (pair, block) share one line");
 static_assert(kMaxM <= kLine, "an expert's logits of all tokens share one line");
+// Words between the tagged logits of consecutive experts: one token packs 16 experts' logits into
+// a line (each workgroup polls a sixteenth of the lines: 0.01-0.12 us per layer faster than a line
+// per expert over three runs); several tokens keep an expert's logits in a line of their own
+// (packing was 0.1 us per layer slower at M = 4).
+template <int M>
+constexpr int kLgStride = M == 1 ? 1 : kLine;
 constexpr int kSyncCounters = 16;
 constexpr int kSyncStride = 16;             // 64-bit words: 128 bytes apart
 constexpr unsigned kSpinLimit = 1u << 20;   // polls before a wait gives up (~1 s)
@@ -118,9 +125,11 @@ struct Work {
   unsigned long long launch1;    // this launch's number + 1 (set in the kernel)
   float* act;                    // NULL, or the W4A8 activations of a one-layer launch (diagnostics):
                                  // a [E+1][M][I] fp32, then codes [E+1][M][I] u8, then scale bytes [E+1][M][I/32]
-  // Hand-off buffers. Each 128-byte line is written by one workgroup only: on MI355X an exchange
-  // among all workgroups takes ~1.8 us that way and ~3 us when writers share lines.
-  unsigned long long* logits;    // [E][kLine] tagged logits: expert e, token m at e*kLine + m (one line per router row)
+  // Hand-off buffers. Each 128-byte line of the partial sums, y and the done words is written by
+  // one workgroup only: on MI355X an exchange among all workgroups takes ~1.8 us that way and ~3 us
+  // when writers share lines (the 256 done words packed into 16 lines: 1.7 us per layer slower).
+  // The one-token logits are the exception (16 routers' words per line; see kLgStride).
+  unsigned long long* logits;    // tagged logits: expert e, token m at e * kLgStride<M> + m
   unsigned long long* ytag;      // [G][y_stride] tagged bf16 pairs of y (chained sequences): owner b, token m, pair q at b*y_stride + m*R/2 + q
   unsigned long long* done;      // [G][kLine] tagged "layer finished" words (layers that are not chained)
   unsigned long long* partial;   // [P * J][H] tagged, gate-weighted partial sums: line (pair, block or block group), row
@@ -687,9 +696,13 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
 // Every workgroup selects the top-K of each token from the tagged logits (the same result in every
 // workgroup). A lane holds experts lane + 64 q. A candidate must reach T = the smallest of the
 // maxima of the 8 lane groups (lanes 8g .. 8g+7) when at least K groups hold experts (then >= K
-// logits reach T, so all of the top K do); otherwise T admits every expert. A candidate's rank is
-// the number of candidates that beat it (larger logit, or equal logit and lower index); ranks < K
-// are the selection, in order.
+// logits reach T, so all of the top K do); otherwise T admits every expert. Candidates are ordered
+// by the key (logit desc, index asc) and the first K are the selection, in order: a candidate's
+// rank is the number of candidates that beat it, counted by all waves with one ballot per 64 of
+// them (one token), or, with several tokens, each token's candidates (~19, p99 48) are sorted by
+// one bitonic sort across the wave that found them when they fit in it. (A wave's sort is a chain
+// of 10-21 dependent compare-exchange stages; with one token the 16 waves' ballots finish
+// ~0.2 us sooner, with four tokens the four waves' sorts ~0.3 us sooner than ranking them all.)
 
 // One token: wave 0 polls the logits (fewer polling waves make the exchange faster), finds T and
 // writes the candidates to LDS in (q, lane) order with straight-line code; then every wave ranks
@@ -712,7 +725,7 @@ __device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, u
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int e = lane + kWave * q;
-      idx[q] = e < E ? e * kLine : -1;
+      idx[q] = e < E ? e * kLgStride<1> : -1;
     }
     poll_tagged<kQ>(w, w.logits, idx, tag, v);
     stamp(w, l, 4);
@@ -853,7 +866,8 @@ __device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int 
 // M words of a line are read by adjacent lanes of one instruction and every line is requested
 // once) and the keys go to LDS; wave m < M then finds token m's T and writes its candidates as in
 // the one-token case (token m's region: E candidates, 64 slots for the lanes without one, the
-// count); every wave ranks its share of all tokens' candidates; then wave 0 forms the union while
+// count) and sorts them when they fit in the wave (otherwise every wave ranks its share of that
+// token's candidates after the barrier); then wave 0 forms the union while
 // wave 1 + m forms token m's weights, and a barrier publishes both (the weights go into the union
 // after it: a task reads them only past its own first barrier).
 template <int M, int kQ>
@@ -873,7 +887,7 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       const int i = tid + kThreads * k, e = i / M, m = i - e * M;
-      idx[k] = e < E ? e * kLine + m : -1;
+      idx[k] = e < E ? e * kLgStride<M> + m : -1;
     }
     poll_tagged<N>(w, w.logits, idx, tag, v);
 #pragma unroll
@@ -917,34 +931,46 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
     }
     if (lane == 0) cm[E + kWave] = (unsigned long long)nc;
     stamp(w, l, 11);
-  }
-  __syncthreads();
-  {
-    // every token's count and first 64 candidates are read before any ballot
-    int nc[M];
-    unsigned long long o0[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) nc[m] = (int)cand[(size_t)m * stride + E + kWave];
-#pragma unroll
-    for (int m = 0; m < M; ++m) o0[m] = lane < nc[m] ? cand[(size_t)m * stride + lane] : 0ull;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const unsigned long long* cm = cand + (size_t)m * stride;
-      for (int c = wave; c < nc[m]; c += kWaves) {
-        const unsigned long long cc = cm[c];
-        int rank = __popcll(__ballot(o0[m] > cc));
-        for (int j0 = kWave; j0 < nc[m] && rank < K; j0 += kWave) {
-          const unsigned long long o = j0 + lane < nc[m] ? cm[j0 + lane] : 0ull;
-          rank += __popcll(__ballot(o > cc));
-        }
-        if (rank < K && lane == 0) {
-          s_sel[m][rank] = (uint32_t)(cc >> 32);
-          s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)cc);
-        }
+    if (nc <= kWave) {
+      // this token's candidates, one per lane, sorted across the wave: lane r holds rank r
+      const unsigned long long c = sort_candidates(lane < nc ? cm[lane] : 0ull, nc, lane);
+      if (lane < K) {
+        s_sel[m][lane] = (uint32_t)(c >> 32);
+        s_idx[m][lane] = (int)(0xffffffffu - (uint32_t)c);
       }
     }
   }
   __syncthreads();
+  {
+    // tokens with more candidates than a wave holds: every wave ranks its share of them
+    int nc[M];
+    bool many = false;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      nc[m] = (int)cand[(size_t)m * stride + E + kWave];
+      many |= nc[m] > kWave;
+    }
+    if (many) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (nc[m] <= kWave) continue;
+        const unsigned long long* cm = cand + (size_t)m * stride;
+        for (int c = wave; c < nc[m]; c += kWaves) {
+          const unsigned long long cc = cm[c];
+          int rank = 0;
+          for (int j0 = 0; j0 < nc[m] && rank < K; j0 += kWave) {
+            const unsigned long long o = j0 + lane < nc[m] ? cm[j0 + lane] : 0ull;
+            rank += __popcll(__ballot(o > cc));
+          }
+          if (rank < K && lane == 0) {
+            s_sel[m][rank] = (uint32_t)(cc >> 32);
+            s_idx[m][rank] = (int)(0xffffffffu - (uint32_t)cc);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
   stamp(w, l, 12);
   float wr = 0.0f;
   if (wave == 0) {
@@ -1188,7 +1214,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       if (lane == 0) {
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          st_coherent(w.logits + (size_t)r_row * kLine + m, tagged(tag_lg, __float_as_uint(lg[m])));
+          st_coherent(w.logits + (size_t)r_row * kLgStride<M> + m, tagged(tag_lg, __float_as_uint(lg[m])));
         if (L.logits_out)
 #pragma unroll
           for (int m = 0; m < M; ++m) stg(L.logits_out + (size_t)m * E + r_row, lg[m]);

@@ -167,6 +167,73 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// The value of lane (lane ^ S) for a constant S, without the LDS: DPP for S = 1, 2 (quad
+// permutes), 4 (the half-row mirror, then the quad reversal: lane 8a + 4c + d reads 8a + 4(1-c) + d)
+// and 8 (rotation by 8 inside a row of 16), the lane-group swaps for S = 16 and 32. Every source
+// lane of these DPP moves exists, so no lane keeps an old value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  if constexpr (S == 1) return dpp_mov<0xB1>(v);
+  else if constexpr (S == 2) return dpp_mov<0x4E>(v);
+  else if constexpr (S == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+  else if constexpr (S == 8) return dpp_mov<0x128>(v);
+  else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // {(r0, r0, r2, r2), (r1, r1, r3, r3)}
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(S == 32, "strides 1 .. 32");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // {(r0, r1, r0, r1), (r2, r3, r2, r3)}
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, int lane) {
+  return (unsigned long long)xor_lane<S>((uint32_t)v, lane) | ((unsigned long long)xor_lane<S>((uint32_t)(v >> 32), lane) << 32);
+}
+
+// One compare-exchange stage of a bitonic network at a constant stride S: lanes whose keep_max
+// holds take the larger of their key and lane (lane ^ S)'s, the others the smaller (one compare:
+// the partner's key is taken when "it is larger" agrees with keep_max).
+template <int S>
+__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long key, bool keep_max, int lane) {
+  const unsigned long long o = xor_lane64<S>(key, lane);
+  return (o > key) == keep_max ? o : key;
+}
+template <int S>
+__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int size, int lane) {
+  // the strides S, S/2, .. 1 of merging blocks of `size` (descending where lane & size is 0)
+  key = bitonic_step<S>(key, ((lane & S) == 0) == ((lane & size) == 0), lane);
+  if constexpr (S > 1) key = bitonic_merge_desc<S / 2>(key, size, lane);
+  return key;
+}
+
+// Bitonic sort of one 64-bit key per lane inside aligned groups of N lanes (N = 16, 32 or 64): lanes
+// 0 .. N-1 end descending (lane 0 the largest); with N < 64 the other groups end sorted too, in
+// either direction.
+template <int N = 64>
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key, int lane) {
+  static_assert(N == 16 || N == 32 || N == 64, "groups of 16, 32 or 64 lanes");
+  key = bitonic_merge_desc<1>(key, 2, lane);
+  key = bitonic_merge_desc<2>(key, 4, lane);
+  key = bitonic_merge_desc<4>(key, 8, lane);
+  key = bitonic_merge_desc<8>(key, 16, lane);
+  if constexpr (N >= 32) key = bitonic_merge_desc<16>(key, 32, lane);
+  if constexpr (N == 64) key = bitonic_merge_desc<32>(key, 64, lane);   // lane & 64 is 0: descending throughout
+  return key;
+}
+
+// Keys, one per lane (0 past the first n <= 64), sorted descending in lanes 0 .. n-1 by the
+// smallest lane group of 16, 32 or 64 that holds them (n is wave-uniform).
+__device__ __forceinline__ unsigned long long sort_candidates(unsigned long long c, int n, int lane) {
+  if (n <= 16) return wave_sort_desc<16>(c, lane);
+  if (n <= 32) return wave_sort_desc<32>(c, lane);
+  return wave_sort_desc<64>(c, lane);
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------------------ selection keys

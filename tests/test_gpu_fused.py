@@ -152,13 +152,17 @@ def test_fused_all_logits_tied(M):
     assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"all tied M={M}")
 
 
+@pytest.mark.parametrize("n_tied", [40, 100])
 @pytest.mark.parametrize("M", [1, 3])
-def test_fused_many_tied_candidates(M):
-    """Zero router weights and a bias of 1.0 on 100 seeded experts: those 100 tie above the rest
-    (two waves' worth of candidates) and the K lowest indices among them are selected."""
-    say("fused 100 tied", M)
+def test_fused_many_tied_candidates(M, n_tied):
+    """Zero router weights and a bias of 1.0 on n_tied seeded experts: those tie above the rest and
+    the K lowest indices among them are selected. Every lane group (experts with lane // 8 = g,
+    lane = e % 64) holds one of them, so the candidates are exactly the tied experts: 40 fit in one
+    wave (the in-wave sort), 100 do not (the ranking across waves)."""
+    say("fused tied", n_tied, M)
     shape = synth.LayerShape()
-    top = np.random.default_rng(11).choice(shape.n_routed, 100, replace=False)
+    top = np.random.default_rng(11).choice(shape.n_routed, n_tied, replace=False)
+    assert len(set(((top % 64) // 8).tolist())) == 8
     bias = np.zeros(shape.n_routed, dtype=np.float32)
     bias[top] = 1.0
     layer = _zero_router(Layer(0, 0, shape, M, bias=bias))
@@ -167,7 +171,7 @@ def test_fused_many_tied_candidates(M):
     want = np.sort(top)[:shape.topk]
     assert np.array_equal(ridx, np.tile(want, (M, 1)))
     assert L.topk_idx.cpu().numpy().tolist() == ridx.tolist()
-    assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"100 tied M={M}")
+    assert_close(L.y_f32.cpu().numpy(), layer.oracle_y(ridx, rw), what=f"{n_tied} tied M={M}")
 
 
 def test_fused_matches_two_call_routing():
