@@ -205,7 +205,7 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   const int nrw = (E + G - 1) / G;
   // rows per owner: even, so that a thread writes a bf16 pair of one token
   const int R_all = ((H + G - 1) / G + 1) & ~1;   // every workgroup owns rows
-  if (G > kMaxGrid || G < J || nrw > kWaves || R_all > kMaxRows) return QWS_ERR_SHAPE;
+  if (G > kMaxGrid || G < J || nrw > kCopyWaves || R_all > kMaxRows) return QWS_ERR_SHAPE;
   const int P = M * (K + 1);
   const size_t lds = lds_bytes(M, E, H, P, J, nrw);
   if (lds > kMaxDynLds) return QWS_ERR_SHAPE;

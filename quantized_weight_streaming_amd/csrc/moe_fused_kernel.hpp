@@ -77,6 +77,7 @@ static_assert(kMaxM <= kLine, "an expert's logits of all tokens share one line")
 // (packing was 0.1 us per layer slower at M = 4).
 template <int M>
 constexpr int kLgStride = M == 1 ? 1 : kLine;
+constexpr int kCopyWaves = kWaves - 2;   // waves that copy the next layer's x during the barrier
 constexpr int kSyncCounters = 16;
 constexpr int kSyncStride = 16;             // 64-bit words: 128 bytes apart
 constexpr unsigned kSpinLimit = 1u << 20;   // polls before a wait gives up (~1 s)
@@ -279,19 +280,22 @@ __device__ __forceinline__ void router_row_to_lds(const uint16_t* row, uint16_t*
 
 // Between layers that are not chained: every workgroup publishes a tagged word once all of its
 // stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
-// round trip to a counter before the wait starts. Meanwhile the router waves copy the next
-// layer's router rows (next_row: this wave's row, or NULL) into LDS and the last wave polls: it
-// issues none of these copies, which a wait for its loads would also wait for.
+// round trip to a counter before the wait starts. Meanwhile waves 0 .. kCopyWaves-1 copy the next
+// layer's x and the router waves its router rows (next_row: this wave's row, or NULL) into LDS,
+// wave kWaves-2 stores the word and the last wave polls: neither issues any of the copies, which a
+// wait for its loads would also wait for.
 __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, const uint16_t* next_x, uint16_t* xs,
                                int n_x, const uint16_t* next_row, uint16_t* row_dst, int H) {
   wait_mem();
   __syncthreads();
   stamp(w, l, 14);
-  if (tid == 0) st_coherent(w.done + (size_t)blockIdx.x * kLine, tagged(tag, 0u));
-  if (next_x) {
+  // the word is stored by a wave that neither copies nor polls: the next wait of the storing wave
+  // also waits for the store's acknowledgement, slow while every workgroup polls these lines
+  if (tid == (kWaves - 2) * kWave) st_coherent(w.done + (size_t)blockIdx.x * kLine, tagged(tag, 0u));
+  if (next_x && tid < kCopyWaves * kWave) {
     // the next layer's x (written before this launch) -> LDS, in flight while the barrier waits
     const int lane = tid % kWave, c0 = tid - lane;
-    for (int c = c0; c < n_x / 8; c += kThreads)
+    for (int c = c0; c < n_x / 8; c += kCopyWaves * kWave)
       if (c + lane < n_x / 8)
         __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(next_x + (size_t)(c + lane) * 8),
                                          (__attribute__((address_space(3))) void*)(xs + (size_t)c * 8), 16, 0, 0);
@@ -1131,6 +1135,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     const bool shared_task = kEarlyShared<M> && sh.has_shared && b >= G - J;
     const int r_row = b + G * wave;                       // this wave's router row
     const bool is_router = wave < sh.nrw && r_row < E;
+    uint16_t* const my_wr_s = wr_s + (size_t)wave * H;    // its LDS copy (router waves only)
     // descriptor of layer l: layer 0 from the kernel arguments, later ones from the LDS copy made
     // during the previous layer
     Layer L = first;
@@ -1161,7 +1166,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       for (int q = 0; q < kXw; ++q)
         if (tid + q * kThreads < n) reinterpret_cast<uint32_t*>(xs)[tid + q * kThreads] = (uint32_t)v[q];
     } else if (sh.x_fresh) {
-      wait_mem();   // this thread's copy of x into LDS, issued during the barrier, has landed
+      // the copy of x into LDS issued during the barrier has landed (only the waves that issued
+      // part of it wait: another wait would also wait for the barrier word's store)
+      if (wave < kCopyWaves && wave * kWave < M * H / 8) wait_mem();
     } else {
       // x may have been written earlier in this launch: device-coherent loads
       const unsigned long long* src = reinterpret_cast<const unsigned long long*>(L.x);
@@ -1187,17 +1194,23 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       // every operand read is issued before the first product: chunks past the row end read the
       // last chunk and use a zero router operand (their products add exact zeros, so the sum and
       // its order equal those of the two-call router kernel)
-      const uint16_t* wrow = wr_s + (size_t)wave * H;
+      const uint16_t* wrow = my_wr_s;
       const int nrc = H >> 3;
       u32x4_t rv[kRtCpl], xv[M][kRtCpl];
 #pragma unroll
       for (int t = 0; t < kRtCpl; ++t) {
-        const int c = lane + t * kWave, cc = min(c, nrc - 1);
-        const uint32_t keep = 0u - (uint32_t)(c < nrc);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wrow + cc * 8);
-        rv[t] = u32x4_t{v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep};
+        const int cc = min(lane + t * kWave, nrc - 1);
+        rv[t] = *reinterpret_cast<const u32x4_t*>(wrow + cc * 8);
 #pragma unroll
         for (int m = 0; m < M; ++m) xv[m][t] = *reinterpret_cast<const u32x4_t*>(xs + m * H + cc * 8);
+      }
+      // keeps the scheduler from moving any use of the reads between them: the reads were issued
+      // one or two at a time otherwise, each waiting for the previous one's products
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < kRtCpl; ++t) {
+        const uint32_t keep = 0u - (uint32_t)(lane + t * kWave < nrc);
+        rv[t] = u32x4_t{rv[t][0] & keep, rv[t][1] & keep, rv[t][2] & keep, rv[t][3] & keep};
       }
       float acc[M];
 #pragma unroll
@@ -1304,7 +1317,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       next_row = reinterpret_cast<const uint16_t*>(
                      uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8])) +
                  (size_t)r_row * H;
-    if (next_row && sh.chained) router_row_to_lds(next_row, wr_s + (size_t)wave * H, H, lane);
+    if (next_row && sh.chained) router_row_to_lds(next_row, my_wr_s, H, lane);
 
     stamp(w, l, 6);
 
@@ -1397,7 +1410,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       const uint16_t* next_x = nullptr;
       if (sh.x_fresh)
         next_x = reinterpret_cast<const uint16_t*>(uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, x_bf16) / 8]));
-      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H, next_row, wr_s + (size_t)wave * H, H);
+      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H, next_row, my_wr_s, H);
       stamp(w, l, 9);
     } else {
       __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer
