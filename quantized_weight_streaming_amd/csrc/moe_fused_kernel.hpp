@@ -988,16 +988,17 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
         if ((u.mask >> m) & 1u) un.ptok[u.pair0 + __popc(u.mask & ((1u << m) - 1u))] = m;
     }
     if (u.e >= 0) un.sel_slot[lane] = u.slot;   // slot of selection (lane / kMaxK, lane % kMaxK)
+    // the shared slot's weight and token of pair m from lane m (a vector of M ones written by one
+    // lane was kept in scratch memory across the layer loop and reloaded here)
+    if (ns && lane < M) {
+      un.w[0][lane] = 1.0f;
+      un.ptok[lane] = lane;
+    }
     if (lane == 0) {
       if (ns) {
         un.id[0] = E;
         un.mask[0] = (1u << M) - 1u;
         un.pair0[0] = 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          un.w[0][m] = 1.0f;
-          un.ptok[m] = m;
-        }
       }
       un.n = u.n;
       un.n_pairs = u.n_pairs;
@@ -1204,9 +1205,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 #pragma unroll
         for (int m = 0; m < M; ++m) xv[m][t] = *reinterpret_cast<const u32x4_t*>(xs + m * H + cc * 8);
       }
-      // keeps the scheduler from moving any use of the reads between them: the reads were issued
-      // one or two at a time otherwise, each waiting for the previous one's products
-      __builtin_amdgcn_sched_barrier(0);
+      // one token: keeps the scheduler from moving any use of the reads between them (the reads
+      // were issued one or two at a time otherwise, each waiting for the previous one's products);
+      // with several tokens all reads at once need more registers than the kernel has (spills)
+      if constexpr (M == 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < kRtCpl; ++t) {
         const uint32_t keep = 0u - (uint32_t)(lane + t * kWave < nrc);
