@@ -94,7 +94,7 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
   (void)E;
   const size_t lg = qws_host::align256((size_t)kMaxE * kLine * 8);
   const size_t yt = qws_host::align256((size_t)kMaxGrid * line_words(M * kMaxRows / 2) * 8);
-  const size_t dn = qws_host::align256((size_t)kMaxGrid * kLine * 8);
+  const size_t dn = qws_host::align256((size_t)kReplicas * kMaxGrid * kLine * 8);
   const size_t part = qws_host::align256((size_t)M * (K + 1) * (I / kBlk) * H * 8);
   if (w) {
     w->trace = nullptr;
