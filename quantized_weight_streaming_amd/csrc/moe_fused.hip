@@ -93,7 +93,7 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
   // rows); the partial sums for every (pair, block) line of H rows
   (void)E;
   const size_t lg = qws_host::align256((size_t)kMaxE * kLine * 8);
-  const size_t yt = qws_host::align256((size_t)kMaxGrid * line_words(M * kMaxRows / 2) * 8);
+  const size_t yt = qws_host::align256((size_t)kMaxGrid * line_words(M * kMaxRows / 2) * 8);   // one copy
   const size_t dn = qws_host::align256((size_t)kReplicas * kMaxGrid * kLine * 8);
   const size_t part = qws_host::align256((size_t)M * (K + 1) * (I / kBlk) * H * 8);
   if (w) {
@@ -107,8 +107,9 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
     w->ytag = reinterpret_cast<unsigned long long*>(base + sync + misc + lg);
     w->done = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt);
     w->partial = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn);
+    w->ytag_more = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn + part);
   }
-  return sync + misc + lg + yt + dn + part;
+  return sync + misc + lg + yt + dn + part + (kReplicas - 1) * yt;
 }
 
 int grid_for_device(int* G) {

@@ -77,10 +77,11 @@ static_assert(kMaxM <= kLine, "an expert's logits of all tokens share one line")
 // (packing was 0.1 us per layer slower at M = 4).
 template <int M>
 constexpr int kLgStride = M == 1 ? 1 : kLine;
-// Copies of the words every workgroup polls (the one-token logits, the layer-done words): each is
-// written kReplicas times, by lanes 0 .. kReplicas-1 of one store instruction, and workgroup b
-// polls copy b % kReplicas, so that a line is polled by a 32nd of the grid instead of all of it
-// (measured: 13.93 -> 13.68 us per layer at M = 1; 16 or 32 copies were slower again).
+// Copies of the words every workgroup polls (the one-token logits, the layer-done words, the tagged
+// y of a chained sequence): each is written kReplicas times by as many lanes of the same stores,
+// and workgroup b polls copy b % kReplicas, so that a line is polled by a 32nd of the grid instead
+// of all of it (logits and done words: 13.93 -> 13.68 us per layer at M = 1; 16 or 32 copies were
+// slower again).
 constexpr int kReplicas = 8;
 static_assert(kReplicas <= kLine, "the one-token logit copies fit the logits area (kMaxE x kLine words)");
 constexpr int kCopyWaves = kWaves - 2;   // waves that copy the next layer's x during the barrier
@@ -138,11 +139,19 @@ struct Work {
   // The one-token logits are the exception (16 routers' words per line; see kLgStride).
   unsigned long long* logits;    // tagged logits: expert e, token m at e * kLgStride<M> + m (one token:
                                  // copy r at r * kMaxE + e)
-  unsigned long long* ytag;      // [G][y_stride] tagged bf16 pairs of y (chained sequences): owner b, token m, pair q at b*y_stride + m*R/2 + q
+  unsigned long long* ytag;      // [kMaxGrid][y_stride] tagged bf16 pairs of y (chained sequences), copy 0:
+                                 // owner b, token m, pair q at b*y_stride + m*R/2 + q
+  unsigned long long* ytag_more; // copies 1 .. kReplicas-1, [kReplicas-1][kMaxGrid][y_stride] (after the
+                                 // partial sums: the other buffers keep their places)
   unsigned long long* done;      // [kReplicas][kMaxGrid][kLine] tagged "layer finished" words (layers that
                                  // are not chained): copy r of workgroup b's word at (r * kMaxGrid + b) * kLine
   unsigned long long* partial;   // [P * J][H] tagged, gate-weighted partial sums: line (pair, block or block group), row
 };
+// Copy c of the tagged y words of a chained sequence.
+__device__ __forceinline__ unsigned long long* ytag_copy(const Work& w, const Shape& sh, int c) {
+  return c == 0 ? w.ytag : w.ytag_more + (size_t)(c - 1) * kMaxGrid * sh.y_stride;
+}
+
 
 // Routing of the current layer, shared by the workgroup (LDS).
 struct Union {
@@ -1118,7 +1127,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     const size_t n_part = (size_t)sh.P * J * H;
     for (size_t i = (size_t)b * kThreads + tid; i < n_part; i += (size_t)G * kThreads) st_coherent(w.partial + i, 0ull);
     for (int i = b * kThreads + tid; i < kMaxE * kLine; i += G * kThreads) st_coherent(w.logits + i, 0ull);
-    for (int i = tid; i < sh.y_stride; i += kThreads) st_coherent(w.ytag + (size_t)b * sh.y_stride + i, 0ull);
+    for (int i = tid; i < kReplicas * sh.y_stride; i += kThreads)
+      st_coherent(ytag_copy(w, sh, i / sh.y_stride) + (size_t)b * sh.y_stride + i % sh.y_stride, 0ull);
     if (tid < kReplicas * kLine) st_coherent(w.done + ((size_t)(tid / kLine) * kMaxGrid + b) * kLine + tid % kLine, 0ull);
     grid_sync(w, sync);
   }
@@ -1171,7 +1181,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
         const int owner = (int)(((float)qq + 0.5f) * (2.0f * sh.inv_r));
         idx[q] = i < n ? owner * sh.y_stride + m * half_r + (qq - owner * half_r) : -1;
       }
-      poll_tagged<kXw>(w, w.ytag, idx, tag_y - 4u, v);
+      poll_tagged<kXw>(w, ytag_copy(w, sh, b % kReplicas), idx, tag_y - 4u, v);
 #pragma unroll
       for (int q = 0; q < kXw; ++q)
         if (tid + q * kThreads < n) reinterpret_cast<uint32_t*>(xs)[tid + q * kThreads] = (uint32_t)v[q];
@@ -1400,22 +1410,26 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
       __syncthreads();
       stamp(w, l, 13);
-      // outputs: a thread takes two adjacent rows of one token (the tagged copy holds a bf16 pair)
-      for (int t = tid; t < (my_rows / 2) * M; t += kThreads) {
-        const int rp = t / M, m = t - rp * M;
+      // outputs: a thread takes two adjacent rows of one token (the tagged copy holds a bf16 pair);
+      // chained, threads n_out .. kReplicas * n_out - 1 write the other copies of the tagged pairs
+      const int n_out = (my_rows / 2) * M;
+      const int n_thr = sh.chained && l + 1 < n_layers ? kReplicas * n_out : n_out;
+      for (int t = tid; t < n_thr; t += kThreads) {
+        const int c = t / n_out, tt = t - c * n_out, rp = tt / M, m = tt - rp * M;
         const float y0 = s_y[m][2 * rp], y1 = s_y[m][2 * rp + 1];
         const size_t o = (size_t)m * H + row0 + 2 * rp;
         const uint16_t h0 = f32_to_bf16_rne(y0), h1 = f32_to_bf16_rne(y1);
-        if (L.y32) {
+        if (c == 0 && L.y32) {
           st_coherent(L.y32 + o, y0);
           st_coherent(L.y32 + o + 1, y1);
         }
-        if (L.y16) {
+        if (c == 0 && L.y16) {
           st_coherent(L.y16 + o, h0);
           st_coherent(L.y16 + o + 1, h1);
         }
         if (sh.chained && l + 1 < n_layers)
-          st_coherent(w.ytag + (size_t)b * sh.y_stride + m * (R / 2) + rp, tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
+          st_coherent(ytag_copy(w, sh, c) + (size_t)b * sh.y_stride + m * (R / 2) + rp,
+                      tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
       }
     }
     flush_stamps(w, l, false);
