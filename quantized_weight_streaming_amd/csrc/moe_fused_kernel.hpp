@@ -15,29 +15,29 @@
 // activations never cross workgroups -- and writes H partial sums per token, already multiplied by
 // the token's gate weight. Experts are stored task-major (moe_pack_mxfp4): a task is one 128 KB
 // record in the order its 16 waves read it, so each of a lane's eight loads is part of a 1 KB
-// run per wave. On MI355X one compute unit streams ~20 GB/s however its loads are shaped, but
-// many narrow or scattered loads per lane lower that further. Weights are read with
+// run per wave. On MI355X one compute unit streams ~50 GB/s alone and ~27 GB/s while 192 stream
+// at once, and many narrow or scattered loads per lane lower that further. Weights are read with
 // non-temporal loads: each byte is used once per step, and a burst of such loads streams ~2x
 // faster than cached loads when the caches hold dirty lines.
 //
 // Hand-offs between workgroups carry their own validity: a 64-bit word holds a 32-bit value and a
 // 32-bit tag unique to (launch, layer, kind), written with one device-coherent store and polled
 // with device-coherent loads (64-bit accesses are single-copy atomic), so a reader needs no
-// separate signal, fence or counter; a poll reloads only the words that are not yet valid. Per
-// layer:
+// separate signal, fence or counter; a poll reloads only the words that are not yet valid. Words
+// that every workgroup polls are written in several copies (kReplicas). Per layer:
 //   1  x into LDS: layer 0 from the caller's buffer; in a chained sequence (x of layer l+1 is y of
 //      layer l) from the tagged copy of y the previous layer published.
 //   2  router dots of this workgroup's rows (prefetched into LDS during the previous layer) ->
 //      tagged logits; workgroups G-J .. G-1 then run the shared expert's J tasks (they need no
 //      routing).
 //   3  every workgroup selects top-K itself from the tagged logits, in parallel: a threshold from
-//      the per-wave maxima leaves a few candidates, each of which counts the candidates that beat
-//      it (logit descending, index ascending) to find its rank; softmax over the selected; union of
-//      the window's selections (first-occurrence order).
+//      lane-group maxima leaves a few candidates, ranked by the candidates that beat them (logit
+//      descending, index ascending; with several tokens sorted within a wave); softmax over the
+//      selected; union of the window's selections (first-occurrence order).
 //   4  routed tasks, round-robin over workgroups (at M = 1 one task per workgroup).
 //   5  workgroup b owns output rows [b*R, b*R + R): it polls their tagged partial sums, sums them in
 //      a fixed order (deterministic), writes y and, in a chained sequence, a tagged copy.
-// Layers that are not chained are separated by a counter barrier instead.
+// Layers that are not chained are separated instead by a barrier on tagged per-workgroup words.
 #pragma once
 #include "qws_common.hpp"
 #ifdef __HIPCC_RTC__
