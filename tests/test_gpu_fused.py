@@ -409,3 +409,49 @@ def test_earlier_timeouts_do_not_end_later_launches():
         assert torch.equal(L.y_f32.view(torch.int32), ref.view(torch.int32)), f"launch {i + 1}"
         assert qws.moe_workspace_errors(ws, 1, 8, 512, 768) == 7
         ws[off + 64:off + 72].view(torch.int64).fill_(i + 2)   # as if this launch had timed out
+
+
+@pytest.mark.parametrize("mode,M", [("single", 1), ("single", 4), ("independent", 1), ("chained", 1), ("chained", 4)])
+def test_tag_wraparound_clears_stale_words(mode, M):
+    """The 32-bit tags repeat after 2^20 launches on one workspace; the launch that starts the new
+    cycle clears every tagged word (all copies of the polled words included) before any use. The
+    launch counter is set from the host so that the next launch is number 2^20, whose tags equal
+    launch 0's, after a launch 0 on other inputs whose words would otherwise pass for the new
+    launch's: the outputs equal those of a fresh workspace, bit for bit, and nothing times out."""
+    say("tag wrap-around", mode, M)
+    shape = synth.LayerShape()
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def make(seed):
+        if mode == "single":
+            t = Layer(seed, 0, shape, M)
+            L = qws.MoeLayer(t.x_t, t.wr_t, _packed(t), shape.topk)
+            return [L], (lambda ws: qws.moe_layer_mxfp4(L, workspace=ws))
+        if mode == "independent":
+            Ls = [qws.MoeLayer(t.x_t, t.wr_t, _packed(t), shape.topk) for t in (Layer(seed, l, shape, M) for l in range(3))]
+        else:
+            _, Ls, _ = _chain(3, M, shape, seed)
+        seq = qws.MoeLayers(Ls)
+        return Ls, (lambda ws: seq.run(ws))
+
+    def outputs(Ls):
+        return [L.y_f32.clone() for L in Ls]
+
+    La, run_a = make(70)
+    Lb, run_b = make(71)
+    fresh = qws.moe_layer_workspace(M, shape.topk, shape.n_routed, shape.hidden, shape.inter, "cuda")
+    run_b(fresh)
+    torch.cuda.synchronize()
+    ref = outputs(Lb)
+    ws = qws.moe_layer_workspace(M, shape.topk, shape.n_routed, shape.hidden, shape.inter, "cuda")
+    off = _error_word_offset(ws)
+    run_a(ws)                                              # launch 0
+    torch.cuda.synchronize()
+    assert int(ws[off - 128:off - 120].view(torch.int64).item()) == G
+    ws[off - 128:off - 120].view(torch.int64).fill_((1 << 20) * G)   # 2^20 launches started
+    for i in range(2):                                     # launches 2^20 (clears) and 2^20 + 1
+        run_b(ws)
+        torch.cuda.synchronize()
+        for l, (L, y) in enumerate(zip(Lb, ref)):
+            assert torch.equal(L.y_f32.view(torch.int32), y.view(torch.int32)), f"launch {i}, layer {l}"
+        assert qws.moe_workspace_errors(ws, M, shape.topk, shape.n_routed, shape.inter) == 0
