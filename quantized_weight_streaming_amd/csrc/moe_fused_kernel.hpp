@@ -847,7 +847,8 @@ struct UnionLane {
 };
 
 template <int M>
-__device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int K, int ns, int lane) {
+__device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int K, int ns, int lane, uint32_t* tab,
+                                                int E) {
   constexpr int N = M * kMaxK;
   static_assert(N <= kWave, "one wave holds every selection");
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -855,17 +856,22 @@ __device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int 
   const bool valid = lane < N && rj < K;
   UnionLane u;
   u.e = valid ? s_idx[lane / kMaxK][rj] : -1;
-  // every selection against every other, from registers (descending: fl ends at the first lane
-  // with this expert)
-  unsigned mask = 0u;
-  int fl = lane;
-#pragma unroll
-  for (int i = N - 1; i >= 0; --i) {
-    const int ei = __builtin_amdgcn_readlane(u.e, i);
-    const bool same = valid && ei == u.e;
-    mask |= same ? 1u << (i / kMaxK) : 0u;
-    fl = same ? i : fl;
+  // per selected expert, through LDS tables indexed by expert (this wave's LDS operations complete
+  // in order): the first lane that selects it (atomic minimum) and its tokens (atomic or). Against
+  // comparing every selection with every other through lane reads (N rounds): 0.6 us per layer
+  // faster at M = 4.
+  uint32_t* const first_lane = tab;   // [E]
+  uint32_t* const tok_mask = tab + E;   // [E]
+  if (valid) {
+    first_lane[u.e] = 0xffffffffu;
+    tok_mask[u.e] = 0u;
   }
+  if (valid) {
+    atomicMin(first_lane + u.e, (uint32_t)lane);
+    atomicOr(tok_mask + u.e, 1u << (lane / kMaxK));
+  }
+  const int fl = valid ? (int)first_lane[u.e] : lane;
+  const unsigned mask = valid ? tok_mask[u.e] : 0u;
   u.first = valid && fl == lane;
   const unsigned long long firsts = __ballot(u.first);
   u.slot = __builtin_amdgcn_ds_bpermute(fl << 2, ns + (int)__popcll(firsts & lt));
@@ -996,7 +1002,8 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
   stamp(w, l, 12);
   float wr = 0.0f;
   if (wave == 0) {
-    const UnionLane u = union_lanes<M>(s_idx, K, ns, lane);
+    // the candidate area is free again: its tables serve the union
+    const UnionLane u = union_lanes<M>(s_idx, K, ns, lane, reinterpret_cast<uint32_t*>(cand), E);
     if (u.first) {
       un.id[u.slot] = u.e;
       un.mask[u.slot] = u.mask;
