@@ -1085,6 +1085,32 @@ __device__ __forceinline__ void spec_shape(Shape& sh) {
 #endif
 }
 
+// One lane's part of a router row's product with one token's x (both bf16 in LDS), summed in the
+// order of the two-call router kernel; the caller reduces it across the wave. Every operand read
+// is issued before the first product (a scheduling barrier keeps the compiler from interleaving
+// them with the products, which made it issue them one or two at a time, each waiting for the
+// previous products). Chunks past the row end read the last chunk and use a zero router operand:
+// their products add exact zeros, so the sum and its order equal the two-call router's.
+__device__ __forceinline__ float router_dot(const uint16_t* wrow, const uint16_t* xm, int H, int lane) {
+  const int nrc = H >> 3;
+  u32x4_t rv[kRtCpl], xv[kRtCpl];
+#pragma unroll
+  for (int t = 0; t < kRtCpl; ++t) {
+    const int cc = min(lane + t * kWave, nrc - 1);
+    rv[t] = *reinterpret_cast<const u32x4_t*>(wrow + cc * 8);
+    xv[t] = *reinterpret_cast<const u32x4_t*>(xm + cc * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float acc = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kRtCpl; ++t) {
+    const uint32_t keep = 0u - (uint32_t)(lane + t * kWave < nrc);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc = dot2(as_bf16x2(rv[t][d] & keep), as_bf16x2(xv[t][d]), acc);
+  }
+  return acc;
+}
+
 template <int M, bool A8>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
                                                               int n_layers, Shape sh_arg, Work w_arg) {
@@ -1201,6 +1227,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       const unsigned long long* src = reinterpret_cast<const unsigned long long*>(L.x);
       for (int v = tid; v < M * H / 4; v += kThreads) reinterpret_cast<unsigned long long*>(xs)[v] = ld_coherent(src + v);
     }
+    // the router rows copied into LDS by waves 0 .. nrw-1 have landed before this barrier, so that
+    // any wave may read them
+    if (wave < sh.nrw) wait_mem();
     __syncthreads();
     stamp(w, l, 1);
     // the next layer's descriptor -> registers now (after the x wait: a load issued before it would
@@ -1210,48 +1239,30 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       next_desc = ldg(reinterpret_cast<const unsigned long long*>(rest + (l + 1)) + lane);
 
     // ------------------------------------------------------------------ 2: router, shared task
-    if (is_router) {
-      wait_mem();   // this wave's router-row copy into LDS has landed
+    // One token (or too many rows per workgroup): wave r takes router row r for every token.
+    // Several tokens: wave r * M + m takes row r for token m, so that each wave issues one token's
+    // operand reads at once (a wave with four tokens' reads in flight runs out of registers and
+    // issues them two at a time).
+    if (M > 1 && sh.nrw * M <= kWaves) {
+      const int rs = wave / M, mt = wave - rs * M, row = b + G * rs;
+      if (rs < sh.nrw && row < E) {
+        const float bias = L.bias ? ldg(L.bias + (size_t)mt * L.bias_stride + row) : 0.0f;
+        const float lg = wave_sum(router_dot(wr_s + (size_t)rs * H, xs + (size_t)mt * H, H, lane)) + bias;
+        if (lane == 0) {
+          st_coherent(w.logits + (size_t)row * kLgStride<M> + mt, tagged(tag_lg, __float_as_uint(lg)));
+          if (L.logits_out) stg(L.logits_out + (size_t)mt * E + row, lg);
+        }
+      }
+    } else if (is_router) {
       // bias loads first (their latency overlaps the dot products), and before any store: a wait
       // for a load between the stores would also wait for the previous store's acknowledgement,
       // slow while other workgroups poll these lines
       float bias[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) bias[m] = L.bias ? ldg(L.bias + (size_t)m * L.bias_stride + r_row) : 0.0f;
-      // every operand read is issued before the first product: chunks past the row end read the
-      // last chunk and use a zero router operand (their products add exact zeros, so the sum and
-      // its order equal those of the two-call router kernel)
-      const uint16_t* wrow = my_wr_s;
-      const int nrc = H >> 3;
-      u32x4_t rv[kRtCpl], xv[M][kRtCpl];
-#pragma unroll
-      for (int t = 0; t < kRtCpl; ++t) {
-        const int cc = min(lane + t * kWave, nrc - 1);
-        rv[t] = *reinterpret_cast<const u32x4_t*>(wrow + cc * 8);
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m][t] = *reinterpret_cast<const u32x4_t*>(xs + m * H + cc * 8);
-      }
-      // one token: keeps the scheduler from moving any use of the reads between them (the reads
-      // were issued one or two at a time otherwise, each waiting for the previous one's products);
-      // with several tokens all reads at once need more registers than the kernel has (spills)
-      if constexpr (M == 1) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < kRtCpl; ++t) {
-        const uint32_t keep = 0u - (uint32_t)(lane + t * kWave < nrc);
-        rv[t] = u32x4_t{rv[t][0] & keep, rv[t][1] & keep, rv[t][2] & keep, rv[t][3] & keep};
-      }
-      float acc[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[m] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kRtCpl; ++t)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) acc[m] = dot2(as_bf16x2(rv[t][d]), as_bf16x2(xv[m][t][d]), acc[m]);
-      }
       float lg[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) lg[m] = wave_sum(acc[m]) + bias[m];
+      for (int m = 0; m < M; ++m) lg[m] = wave_sum(router_dot(my_wr_s, xs + (size_t)m * H, H, lane)) + bias[m];
       if constexpr (M == 1) {
         if (lane < kReplicas) st_coherent(w.logits + (size_t)lane * kMaxE + r_row, tagged(tag_lg, __float_as_uint(lg[0])));
       }
