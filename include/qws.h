@@ -416,18 +416,19 @@ int lmhead_gemv_fp8_rtc(const qws_lmhead* head, const void* x_bf16, int M, float
 int qws_rtc_compile_head_fp8(int M, long long rows, long long cols, const char* arch, const char* cache_dir);
 /* The fused MoE layers (moe_layers_mxfp4, or moe_layers_w4a8 when w4a8 = 1) compiled at run time
  * for the layers' shape: the same kernel source with E, K, hidden, inter and the shared expert as
- * constants and M and the precision as template arguments, for the current device's
- * architecture. Key: (M, precision, E, hidden, inter, K, shared, architecture, source hash, options
- * and hipRTC version). Same arguments, validation, workspace and results as the template entry
+ * constants and M, the precision and the kind of sequence (chained or not) as template arguments,
+ * for the current device's architecture. Key: (M, precision, E, hidden, inter, K, shared, chained,
+ * architecture, source hash, options and hipRTC version). Same arguments, validation, workspace and results as the template entry
  * points, bit for bit; QWS_ERR_ARG for w4a8 outside {0, 1}, plus the errors of
  * lmhead_gemv_fp8_rtc. A compile takes seconds: the first call for a key blocks the calling
  * thread until it is done (qws_rtc_compile_moe builds the cache ahead of time). */
 int moe_layers_rtc(const qws_moe_layer* layers_host, const qws_moe_layer* layers_device, int n_layers, int M,
                    int K, int w4a8, void* workspace, size_t workspace_bytes, const char* cache_dir,
                    qws_stream_t stream);
-/* Compile (or find in the disk cache) the fused MoE kernel for a shape and an architecture name,
- * without a device. QWS_ERR_ARG for a bad arch name or w4a8 outside {0, 1}; QWS_ERR_SHAPE for M,
- * K, E, hidden, inter or has_shared outside the ranges of moe_layer_mxfp4. */
+/* Compile (or find in the disk cache) the fused MoE kernels for a shape and an architecture name,
+ * without a device: the kernel for separate layers and the one for chained sequences. QWS_ERR_ARG
+ * for a bad arch name or w4a8 outside {0, 1}; QWS_ERR_SHAPE for M, K, E, hidden, inter or
+ * has_shared outside the ranges of moe_layer_mxfp4. */
 int qws_rtc_compile_moe(int M, int K, int E, int hidden, int inter, int has_shared, int w4a8, const char* arch,
                         const char* cache_dir);
 /* Counters since load or the last qws_rtc_reset (stats_out: host memory). */

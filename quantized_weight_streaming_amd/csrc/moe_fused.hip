@@ -108,8 +108,14 @@ size_t ws_layout(int M, int K, int E, int H, int I, char* base, Work* w) {
     w->done = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt);
     w->partial = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn);
     w->ytag_more = reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn + part);
+    // the odd layers' logits of a chained sequence: one token's copies fill half of the logits area
+    // (kReplicas x kMaxE words of kMaxE x kLine), the other half takes them; several tokens need a
+    // second area, after the rest (the other buffers keep their places either way)
+    w->logits_odd = M == 1 ? w->logits + (size_t)kReplicas * kMaxE
+                           : reinterpret_cast<unsigned long long*>(base + sync + misc + lg + yt + dn + part + (kReplicas - 1) * yt);
   }
-  return sync + misc + lg + yt + dn + part + (kReplicas - 1) * yt;
+  static_assert(2 * kReplicas * kMaxE <= kMaxE * kLine, "both one-token logits buffers fit the logits area");
+  return sync + misc + lg + yt + dn + part + (kReplicas - 1) * yt + (M == 1 ? 0 : lg);
 }
 
 int grid_for_device(int* G) {
@@ -139,25 +145,32 @@ int check_layer(const qws_moe_layer& d, int E, int H, int I, int has_shared) {
   return QWS_OK;
 }
 
-template <int M, bool A8>
+template <int M, bool A8, bool CH>
 int launch(const Layer& first, const qws_moe_layer* rest, int n, const Shape& sh, const Work& w, int G, size_t lds,
            hipStream_t s) {
   static bool configured[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (!configured[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layers_kernel<M, A8>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_layers_kernel<M, A8, CH>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e != hipSuccess) return qws_host::set_device_error(e);
     configured[dev] = true;
   }
   // the in-kernel hand-offs need every workgroup resident at once: one per compute unit
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layers_kernel<M, A8>, kThreads, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_layers_kernel<M, A8, CH>, kThreads, lds);
   if (e != hipSuccess) return qws_host::set_device_error(e);
   if (per_cu < 1) return QWS_ERR_SHAPE;
-  hipLaunchKernelGGL((moe_layers_kernel<M, A8>), dim3(G), dim3(kThreads), lds, s, first, rest, n, sh, w);
+  hipLaunchKernelGGL((moe_layers_kernel<M, A8, CH>), dim3(G), dim3(kThreads), lds, s, first, rest, n, sh, w);
   return qws_host::check_launch();
+}
+
+template <int M, bool A8>
+int launch_kind(const Layer& first, const qws_moe_layer* rest, int n, const Shape& sh, const Work& w, int G,
+                size_t lds, hipStream_t s) {
+  return sh.chained ? launch<M, A8, true>(first, rest, n, sh, w, G, lds, s)
+                    : launch<M, A8, false>(first, rest, n, sh, w, G, lds, s);
 }
 
 // The run-time-compiled kernel for this launch's M, precision and layer shape, launched with the
@@ -165,7 +178,7 @@ int launch(const Layer& first, const qws_moe_layer* rest, int n, const Shape& sh
 int launch_rtc(const Layer& first, const qws_moe_layer* rest, int n, const Shape& sh, const Work& w, int G,
                size_t lds, hipStream_t s, int M, bool a8, const char* cache_dir) {
   void* fn = nullptr;
-  int st = qws_host::moe_rtc_function(M, a8, sh.K, sh.E, sh.H, sh.I, sh.has_shared, cache_dir, &fn);
+  int st = qws_host::moe_rtc_function(M, a8, sh.chained != 0, sh.K, sh.E, sh.H, sh.I, sh.has_shared, cache_dir, &fn);
   if (st != QWS_OK) return st;
   int per_cu = 0;
   hipError_t e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, static_cast<hipFunction_t>(fn), kThreads,
@@ -211,14 +224,15 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   const size_t lds = lds_bytes(M, E, H, P, J, nrw);
   if (lds > kMaxDynLds) return QWS_ERR_SHAPE;
   // Chained: layer l+1 reads y of layer l. Then the layers need no barrier, provided every
-  // workgroup computes router rows and owns output rows, so that no workgroup can fall a layer
-  // behind the others (each layer waits for every workgroup's logits and every owner's y).
-  bool chained = n_layers > 1 && E >= G && (size_t)(G - 1) * R_all < (size_t)H;
+  // workgroup computes router rows, so that no workgroup can fall a layer behind the others (each
+  // layer waits for every workgroup's logits); the logits alternate between two buffers, so that
+  // a workgroup that owns no rows may still read layer l's while the others write layer l+1's.
+  bool chained = n_layers > 1 && E >= G;
   for (int l = 0; chained && l + 1 < n_layers; ++l)
     chained = host[l].y_bf16 != nullptr && host[l + 1].x_bf16 == host[l].y_bf16;
-  // Otherwise an owner takes one whole 128-byte line of every partial-sum vector (kLine rows,
-  // when the grid has owners for all of them): it reads no line another owner also reads.
-  const int R = !chained && (size_t)G * kLine >= (size_t)H ? kLine : R_all;
+  // An owner takes one whole 128-byte line of every partial-sum vector (kLine rows, when the grid
+  // has owners for all of them): it reads no line another owner also reads.
+  const int R = (size_t)G * kLine >= (size_t)H ? kLine : R_all;
   Work w;
   ws_layout(M, K, E, H, I, static_cast<char*>(workspace), &w);
   {
@@ -257,17 +271,17 @@ int run_layers(const qws_moe_layer* host, const qws_moe_layer* dev_copy, int n_l
   if (rtc) return launch_rtc(first, dev_copy, n_layers, sh, w, G, lds, s, M, a8, rtc_dir);
   if (a8) {
     switch (M) {
-      case 1: return launch<1, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
-      case 2: return launch<2, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
-      case 3: return launch<3, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
-      default: return launch<4, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      case 1: return launch_kind<1, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      case 2: return launch_kind<2, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      case 3: return launch_kind<3, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
+      default: return launch_kind<4, true>(first, dev_copy, n_layers, sh, w, G, lds, s);
     }
   }
   switch (M) {
-    case 1: return launch<1, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    case 2: return launch<2, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    case 3: return launch<3, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
-    default: return launch<4, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 1: return launch_kind<1, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 2: return launch_kind<2, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    case 3: return launch_kind<3, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
+    default: return launch_kind<4, false>(first, dev_copy, n_layers, sh, w, G, lds, s);
   }
 }
 

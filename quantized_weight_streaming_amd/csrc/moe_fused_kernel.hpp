@@ -139,6 +139,8 @@ struct Work {
   // The one-token logits are the exception (16 routers' words per line; see kLgStride).
   unsigned long long* logits;    // tagged logits: expert e, token m at e * kLgStride<M> + m (one token:
                                  // copy r at r * kMaxE + e)
+  unsigned long long* logits_odd;  // the same for the odd layers of a chained sequence (one token:
+                                   // logits + kReplicas * kMaxE, inside the logits area)
   unsigned long long* ytag;      // [kMaxGrid][y_stride] tagged bf16 pairs of y (chained sequences), copy 0:
                                  // owner b, token m, pair q at b*y_stride + m*R/2 + q
   unsigned long long* ytag_more; // copies 1 .. kReplicas-1, [kReplicas-1][kMaxGrid][y_stride] (after the
@@ -733,7 +735,8 @@ __device__ __forceinline__ void task_compute(const Shape& sh, const Work& w, Tas
 // wave 0 after the final barrier: a task reads them only after its own first barrier, so the other
 // waves issue their task loads meanwhile.
 template <int kQ>
-__device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, uint32_t tag, int wave, int lane,
+__device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, const unsigned long long* lgs,
+                                               uint32_t tag, int wave, int lane,
                                                unsigned long long* cand, Union& un, int (*s_idx)[kMaxK],
                                                float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK], int l) {
   const int E = sh.E, K = sh.K;
@@ -749,7 +752,7 @@ __device__ __forceinline__ void select_top_one(const Shape& sh, const Work& w, u
       const int e = lane + kWave * q;
       idx[q] = e < E ? e * kLgStride<1> : -1;
     }
-    poll_tagged<kQ>(w, w.logits + (size_t)(blockIdx.x % kReplicas) * kMaxE, idx, tag, v);
+    poll_tagged<kQ>(w, lgs + (size_t)(blockIdx.x % kReplicas) * kMaxE, idx, tag, v);
     stamp(w, l, 4);
     // absent experts (past E) get key 0 by a mask rather than a branch per q
     uint32_t key[kQ];
@@ -899,7 +902,8 @@ __device__ __forceinline__ UnionLane union_lanes(const int (*s_idx)[kMaxK], int 
 // wave 1 + m forms token m's weights, and a barrier publishes both (the weights go into the union
 // after it: a task reads them only past its own first barrier).
 template <int M, int kQ>
-__device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, const Layer& L, uint32_t tag, int tid,
+__device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, const unsigned long long* lgs,
+                                             const Layer& L, uint32_t tag, int tid,
                                              int wave, int lane, unsigned long long* cand, Union& un,
                                              int (*s_idx)[kMaxK], float (*s_w)[kMaxK], uint32_t (*s_sel)[kMaxK],
                                              int l) {
@@ -917,7 +921,7 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
       const int i = tid + kThreads * k, e = i / M, m = i - e * M;
       idx[k] = e < E ? e * kLgStride<M> + m : -1;
     }
-    poll_tagged<N>(w, w.logits, idx, tag, v);
+    poll_tagged<N>(w, lgs, idx, tag, v);
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       const int i = tid + kThreads * k, e = i / M, m = i - e * M;
@@ -1111,7 +1115,11 @@ __device__ __forceinline__ float router_dot(const uint16_t* wrow, const uint16_t
   return acc;
 }
 
-template <int M, bool A8>
+// CH: a chained sequence (x of layer l+1 is layer l's bf16 y), whose layers hand x over through
+// tagged y words with no barrier between them; otherwise layers are separated by the tagged
+// barrier. (A template parameter rather than a flag: the chained-only work, the logits buffers
+// alternating by layer parity, cost the other kind 0.1 us per layer when selected at run time.)
+template <int M, bool A8, bool CH>
 __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const qws_moe_layer* __restrict__ rest,
                                                               int n_layers, Shape sh_arg, Work w_arg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -1159,7 +1167,10 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     // tags repeat from here on: clear every tagged word (tag 0 is never valid) before any use
     const size_t n_part = (size_t)sh.P * J * H;
     for (size_t i = (size_t)b * kThreads + tid; i < n_part; i += (size_t)G * kThreads) st_coherent(w.partial + i, 0ull);
-    for (int i = b * kThreads + tid; i < kMaxE * kLine; i += G * kThreads) st_coherent(w.logits + i, 0ull);
+    for (int i = b * kThreads + tid; i < kMaxE * kLine; i += G * kThreads) {
+      st_coherent(w.logits + i, 0ull);
+      if constexpr (M > 1) st_coherent(w.logits_odd + i, 0ull);   // one token: inside the area above
+    }
     for (int i = tid; i < kReplicas * sh.y_stride; i += kThreads)
       st_coherent(ytag_copy(w, sh, i / sh.y_stride) + (size_t)b * sh.y_stride + i % sh.y_stride, 0ull);
     if (tid < kReplicas * kLine) st_coherent(w.done + ((size_t)(tid / kLine) * kMaxGrid + b) * kLine + tid % kLine, 0ull);
@@ -1195,6 +1206,12 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     if (l > 0) L = desc_from_lds(s_desc[l & 1]);
     // tags never 0: a zero-filled workspace holds tag 0
     const uint32_t tag_lg = tag_base + 4u * (uint32_t)l + 1u, tag_pt = tag_lg + 1u, tag_y = tag_lg + 2u;
+    // a chained sequence alternates two logits buffers: a workgroup with no task and no rows may
+    // still read layer l's while the others write layer l+1's (they cannot reach layer l+2's,
+    // whose logits need this workgroup's router rows of layer l+1); one token's odd buffer is the
+    // upper half of the logits area
+    unsigned long long* const lgs =
+        CH && (l & 1) ? (M == 1 ? w.logits + (size_t)kReplicas * kMaxE : w.logits_odd) : w.logits;
     const bool has_next = l + 1 < n_layers;
     stamp(w, l, 0);
 
@@ -1202,7 +1219,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     if (l == 0) {
       for (int v = tid; v < M * H / 8; v += kThreads)
         *reinterpret_cast<u32x4_t*>(xs + v * 8) = ld16(L.x + (size_t)v * 8);
-    } else if (sh.chained) {
+    } else if (CH) {
       // y of the previous layer, as its owners published it: bf16 pair i = (m, row 2q) of x
       const int n = M * H / 2, half_r = R / 2;
       constexpr int kXw = (M * kHMax / 2 + kThreads - 1) / kThreads;
@@ -1249,7 +1266,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
         const float bias = L.bias ? ldg(L.bias + (size_t)mt * L.bias_stride + row) : 0.0f;
         const float lg = wave_sum(router_dot(wr_s + (size_t)rs * H, xs + (size_t)mt * H, H, lane)) + bias;
         if (lane == 0) {
-          st_coherent(w.logits + (size_t)row * kLgStride<M> + mt, tagged(tag_lg, __float_as_uint(lg)));
+          st_coherent(lgs + (size_t)row * kLgStride<M> + mt, tagged(tag_lg, __float_as_uint(lg)));
           if (L.logits_out) stg(L.logits_out + (size_t)mt * E + row, lg);
         }
       }
@@ -1264,13 +1281,13 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 #pragma unroll
       for (int m = 0; m < M; ++m) lg[m] = wave_sum(router_dot(my_wr_s, xs + (size_t)m * H, H, lane)) + bias[m];
       if constexpr (M == 1) {
-        if (lane < kReplicas) st_coherent(w.logits + (size_t)lane * kMaxE + r_row, tagged(tag_lg, __float_as_uint(lg[0])));
+        if (lane < kReplicas) st_coherent(lgs + (size_t)lane * kMaxE + r_row, tagged(tag_lg, __float_as_uint(lg[0])));
       }
       if (lane == 0) {
         if constexpr (M > 1)
 #pragma unroll
           for (int m = 0; m < M; ++m)
-            st_coherent(w.logits + (size_t)r_row * kLgStride<M> + m, tagged(tag_lg, __float_as_uint(lg[m])));
+            st_coherent(lgs + (size_t)r_row * kLgStride<M> + m, tagged(tag_lg, __float_as_uint(lg[m])));
         if (L.logits_out)
 #pragma unroll
           for (int m = 0; m < M; ++m) stg(L.logits_out + (size_t)m * E + r_row, lg[m]);
@@ -1306,8 +1323,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
     // ------------------------------------------------------------------ 3: top-K and union
     // a lane holds experts lane + 64 q for q < kQ: 8 registers suffice up to 512 experts
     if constexpr (M == 1) {
-      if (E <= 8 * kWave) select_top_one<8>(sh, w, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-      else select_top_one<kMaxE / kWave>(sh, w, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      if (E <= 8 * kWave) select_top_one<8>(sh, w, lgs, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      else select_top_one<kMaxE / kWave>(sh, w, lgs, tag_lg, wave, lane, cand, un, s_idx, s_w, s_sel, l);
       // no barrier: the gate weights (wave 0, just formed) are read only past a task's first
       // barrier; wave 0 wrote s_idx and s_w itself
       if (b == 0 && tid < sh.K) {
@@ -1316,8 +1333,8 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       }
     } else {
       // the union is in LDS (its weights are read only past a task's first barrier)
-      if (E <= 8 * kWave) select_multi<M, 8>(sh, w, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
-      else select_multi<M, kMaxE / kWave>(sh, w, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      if (E <= 8 * kWave) select_multi<M, 8>(sh, w, lgs, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
+      else select_multi<M, kMaxE / kWave>(sh, w, lgs, L, tag_lg, tid, wave, lane, cand, un, s_idx, s_w, s_sel, l);
     }
     stamp(w, l, 5);
 
@@ -1360,7 +1377,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       next_row = reinterpret_cast<const uint16_t*>(
                      uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8])) +
                  (size_t)r_row * H;
-    if (next_row && sh.chained) router_row_to_lds(next_row, my_wr_s, H, lane);
+    if (next_row && CH) router_row_to_lds(next_row, my_wr_s, H, lane);
 
     stamp(w, l, 6);
 
@@ -1431,7 +1448,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       // outputs: a thread takes two adjacent rows of one token (the tagged copy holds a bf16 pair);
       // chained, threads n_out .. kReplicas * n_out - 1 write the other copies of the tagged pairs
       const int n_out = (my_rows / 2) * M;
-      const int n_thr = sh.chained && l + 1 < n_layers ? kReplicas * n_out : n_out;
+      const int n_thr = CH && l + 1 < n_layers ? kReplicas * n_out : n_out;
       for (int t = tid; t < n_thr; t += kThreads) {
         const int c = t / n_out, tt = t - c * n_out, rp = tt / M, m = tt - rp * M;
         const float y0 = s_y[m][2 * rp], y1 = s_y[m][2 * rp + 1];
@@ -1445,14 +1462,14 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
           st_coherent(L.y16 + o, h0);
           st_coherent(L.y16 + o + 1, h1);
         }
-        if (sh.chained && l + 1 < n_layers)
+        if (CH && l + 1 < n_layers)
           st_coherent(ytag_copy(w, sh, c) + (size_t)b * sh.y_stride + m * (R / 2) + rp,
                       tagged(tag_y, (uint32_t)h0 | ((uint32_t)h1 << 16)));
       }
     }
     flush_stamps(w, l, false);
     stamp(w, l, 8);
-    if (!sh.chained && l + 1 < n_layers) {
+    if (!CH && l + 1 < n_layers) {
       // layer l's output is written before layer l+1 starts
       const uint16_t* next_x = nullptr;
       if (sh.x_fresh)

@@ -326,7 +326,7 @@ namespace qws_host {
 int set_device_error(hipError_t e);  // records the message, returns QWS_ERR_DEVICE
 int set_error_text(int status, const char* text);  // records `text` for qws_strerror, returns status
 int head_fp8_rtc_function(int M, long long rows, long long cols, const char* cache_dir, void** fn_out);
-int moe_rtc_function(int M, bool a8, int K, int E, int H, int I, int has_shared, const char* cache_dir,
+int moe_rtc_function(int M, bool a8, bool chained, int K, int E, int H, int I, int has_shared, const char* cache_dir,
                      void** fn_out);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

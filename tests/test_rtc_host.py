@@ -75,14 +75,17 @@ def test_moe_compile_then_cache_hit(tmp_path):
     qws.rtc_compile_moe(1, 8, 512, 2560, 768, True, False, "gfx950", d)
     qws.rtc_compile_moe(4, 8, 512, 2560, 768, True, True, "gfx950", d)
     files = sorted(os.listdir(d))
-    assert len(files) == 2
-    assert files[0].startswith("moe_layers_m1_bf16_e512_h2560_i768_k8_s1_gfx950_")
-    assert files[1].startswith("moe_layers_m4_w4a8_e512_h2560_i768_k8_s1_gfx950_")
+    # one kernel for separate layers and one for chained sequences, per shape
+    assert len(files) == 4
+    assert files[0].startswith("moe_layers_m1_bf16_e512_h2560_i768_k8_s1_chain_gfx950_")
+    assert files[1].startswith("moe_layers_m1_bf16_e512_h2560_i768_k8_s1_gfx950_")
+    assert files[2].startswith("moe_layers_m4_w4a8_e512_h2560_i768_k8_s1_chain_gfx950_")
+    assert files[3].startswith("moe_layers_m4_w4a8_e512_h2560_i768_k8_s1_gfx950_")
     assert oct(os.stat(d).st_mode & 0o777) == "0o700"
     assert all(os.stat(os.path.join(d, f)).st_mode & 0o077 == 0 for f in files)
     qws.rtc_compile_moe(1, 8, 512, 2560, 768, True, False, "gfx950", d)
     s = qws.rtc_stats()
-    assert (s["compiles"], s["disk_hits"]) == (2, 1)
+    assert (s["compiles"], s["disk_hits"]) == (4, 2)
 
 
 @pytest.mark.parametrize("args,status", [
