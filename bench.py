@@ -440,7 +440,7 @@ def main():
     # the dominant kernel of the step is the 42-layer MoE launch; the FP8 head follows in "breakdown"
     moe_bytes = sb - head_bytes(1)
     moe_gbs = moe_bytes / (r["moe_us_mean"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": f"qws_moe::moe_layers_kernel<1, false> ({args.layers} MoE layers, one launch)",
+    roofline = {"bound": "hbm", "kernel": f"qws_moe::moe_layers_kernel<1, false, false> ({args.layers} MoE layers, one launch)",
                 "achieved": round(moe_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(moe_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for(MOE_SRC, "moe_layers_kernel"),
                 "algorithmic_bytes_per_launch": moe_bytes, "launch_us_mean": round(r["moe_us_mean"], 2)}
