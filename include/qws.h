@@ -371,7 +371,8 @@ int lmhead_verify_greedy_fp8_noalloc(const qws_lmhead* head, const void* x_bf16,
  *   emitted_out int32 [M], n_out int32 [1]; all device memory owned by the caller.
  *   workspace: lmhead_verify_workspace_bytes(M) bytes, shared with lmhead_verify_greedy_fp8 (the
  *   same conditions: zero-filled before first use, calls that share it must not overlap).
- * Two launches: the head GEMV (logits and per-workgroup maxima), then one workgroup per position.
+ * Two launches: the head GEMV (logits and each head workgroup's four largest keys per position),
+ * then one workgroup per position.
  * Errors: as lmhead_verify_greedy_fp8, plus QWS_ERR_ARG for u or logits_out missing, temperature or
  * top_p out of range, QWS_ERR_SHAPE for top_k outside 1 .. 32 or more than 262,144 rows. */
 int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf16, int M, const int* draft,

@@ -34,8 +34,27 @@ constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x
 constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
 
 // kMode: kGemv (logits), kKeys (logits optional, and each workgroup's largest (logit, lower row)
-// key per token, for the verification epilogues: greedy_finish_kernel and sample_kernel).
-enum HeadMode { kGemv = 0, kKeys = 1 };
+// key per token, for greedy_finish_kernel), kKeys4 (logits, and each workgroup's four largest keys
+// per token in descending order, zero where it has fewer rows, for sample_kernel).
+enum HeadMode { kGemv = 0, kKeys = 1, kKeys4 = 2 };
+constexpr int kListKeys = 4;   // keys per workgroup and token in kKeys4
+constexpr int kListTiles = 8;  // sample_kernel: tiles per workgroup at most (rows <= kHeadGrid x 16 x 8)
+
+// The four largest of two descending lists of four: the pairwise maxima of one list against the
+// other reversed hold them (as a bitonic sequence), which two compare rounds put in order.
+__device__ __forceinline__ void cas_desc(unsigned long long& a, unsigned long long& b) {
+  const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+__device__ __forceinline__ void merge_top4(unsigned long long (&a)[kListKeys], const unsigned long long (&b)[kListKeys]) {
+#pragma unroll
+  for (int j = 0; j < kListKeys; ++j) a[j] = a[j] > b[kListKeys - 1 - j] ? a[j] : b[kListKeys - 1 - j];
+  cas_desc(a[0], a[2]);
+  cas_desc(a[1], a[3]);
+  cas_desc(a[0], a[1]);
+  cas_desc(a[2], a[3]);
+}
 
 template <int M, int kMode>
 __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
@@ -68,6 +87,9 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
   const bool ep = tid < 16 * M;
   float sc = ep ? scale[min(tile * 16 + er, rows - 1)] : 0.0f;
   unsigned long long best = 0ull;   // below every key
+  // kKeys4, descending. (Ranked tile by tile: staging the values and ranking them after the last
+  // tile measured 2 us slower, since a workgroup's tail delays the next one on its compute unit.)
+  unsigned long long top4[kListKeys] = {0ull, 0ull, 0ull, 0ull};
   // x (bf16) into LDS, zero past the row end
   for (int e = tid; e < M * (kXsStride / 8); e += kHeadWaves * kWave) {
     const int m = e / (kXsStride / 8), c = (e % (kXsStride / 8)) * 8;
@@ -113,10 +135,20 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
       v *= sc;
       const long long row = tile * 16 + er;
       if (row < rows) {
-        if (kMode == kGemv || out) out[(size_t)em * rows + row] = v;
+        if (kMode != kKeys || out) out[(size_t)em * rows + row] = v;
         if constexpr (kMode == kKeys) {
           const unsigned long long k = rank_key(sel_key(v), (int)row);
           best = k > best ? k : best;
+        }
+        if constexpr (kMode == kKeys4) {
+          // insert into the descending list (the smallest falls off)
+          unsigned long long k = rank_key(sel_key(v), (int)row);
+#pragma unroll
+          for (int j = 0; j < kListKeys; ++j) {
+            const unsigned long long hi = top4[j] > k ? top4[j] : k;
+            k = top4[j] > k ? k : top4[j];
+            top4[j] = hi;
+          }
         }
       }
     }
@@ -135,6 +167,24 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
         best = k > best ? k : best;
       }
       if (er == 0) keys[(size_t)em * gridDim.x + blockIdx.x] = best;
+    }
+  }
+  if constexpr (kMode == kKeys4) {
+    // the workgroup's four largest keys per token: the 16 lists of token m's epilogue threads
+    // merged pairwise; [token][workgroup][4], for sample_kernel
+    if (ep) {
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        unsigned long long other[kListKeys];
+#pragma unroll
+        for (int j = 0; j < kListKeys; ++j) other[j] = __shfl_xor(top4[j], o, kWave);
+        merge_top4(top4, other);
+      }
+      if (er == 0) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(keys + ((size_t)em * gridDim.x + blockIdx.x) * kListKeys);
+        dst[0] = u32x4_t{(uint32_t)top4[0], (uint32_t)(top4[0] >> 32), (uint32_t)top4[1], (uint32_t)(top4[1] >> 32)};
+        dst[1] = u32x4_t{(uint32_t)top4[2], (uint32_t)(top4[2] >> 32), (uint32_t)top4[3], (uint32_t)(top4[3] >> 32)};
+      }
     }
   }
 }

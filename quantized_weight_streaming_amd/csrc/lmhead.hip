@@ -162,46 +162,52 @@ __global__ __launch_bounds__(kFinishThreads) void greedy_finish_kernel(const uns
 // --------------------------------------------------------------------------- sampled verification
 // The window's positions sampled from the FP8 head's logits (temperature, top_k, top_p, a uniform u
 // per position from the caller), then the accepted prefix of the drafts. Runs after
-// head_fp8_kernel<M, kKeys>, which leaves the logits and, per head workgroup and token, the largest
-// 64-bit key (ordered logit, ~row) of the workgroup's rows. One workgroup per position:
-//  1. t = a lower bound of the k-th largest of those G keys: the k-th largest of the eight waves'
-//     ceil(k / 8) largest (rounds of a wave maximum, lane exchanges by DPP and lane-group swaps,
-//     no LDS), so that every key of the token's top k is at least t and lies in one of the
-//     workgroups whose maximum reaches t: k of them when the waves split the top k evenly, a few
-//     more otherwise (more than 64: t becomes the exact k-th largest by radix select).
-//  2. Candidates: the keys >= t among those workgroups' rows, read back from the logits. They are
-//     the top k and a few other keys >= t (k to k + 3 in simulations of normal logits), so one
-//     wave sorts them; more than 64 go through a radix select first.
-// Tried and slower: sorting each wave's 256 keys and merging the waves' top 64 (6.2 us for step 1
-// against 1.8); each wave reading its top workgroups' rows ahead of t (the extra rounds of a wave
-// maximum cost more than the reads they overlap).
+// head_fp8_kernel<M, kKeys4>, which leaves the logits and, per head workgroup and token, the four
+// largest 64-bit keys (ordered logit, ~row) of the workgroup's rows. One workgroup per position;
+// its time is VALU issue (two waves per SIMD, a few dependent lane exchanges per step), so the
+// steps work on as few and as narrow values as they can:
+//  1. t = a lower bound of the k-th largest workgroup maximum, on their upper 32 bits (the ordered
+//     logit): each of the eight waves takes its ceil(k / 8) largest distinct values (rounds of a
+//     32-bit wave maximum), one wave sorts those and takes the k-th. At least k maxima reach it,
+//     so every key of the token's top k is >= t = (that value, 0) and lies in a workgroup whose
+//     maximum reaches t: k of them when the waves split the top k evenly, a few more otherwise
+//     (more than 64, e.g. many equal logits: t becomes the exact k-th largest maximum by radix
+//     select, which exactly k workgroups reach).
+//  2. Candidates: the keys >= t of those workgroups, one listed key per thread. A list holds all
+//     of its workgroup's keys >= t unless its fourth key reaches t too (a "full" list: there may
+//     be more); only a full list's workgroup has its rows read back from the logits (normal
+//     logits: a few positions in a million). They are the top k and a few other keys >= t (k to
+//     k + 3 in simulations of normal logits), so one wave sorts them; more than 64 go through a
+//     radix select first.
 //  3. Softmax at the temperature, the shortest prefix reaching top_p, inversion at u.
+//  4. Arrival on a counter that also collects each position's acceptance bit (draft m equals its
+//     token): the last position's workgroup reads the window's result off the counter.
+// Measured against the earlier form of this kernel (8.1 us; now 6.2 us): 64-bit keys in step 1
+// took 1.0 us against 0.4; reading back every candidate workgroup's rows, ~1 us; the tokens
+// collected through memory after the arrival, ~1.2 us. Tried and slower: every wave sorting the
+// values for t itself (no second barrier), the candidates appended by the threads holding their
+// lists in registers (nested appends: ~500 instructions, 1.7 us), sorting each wave's 256 keys
+// and merging the waves' top 64, each wave reading its top workgroups' rows ahead of t.
 constexpr int kSampleThreads = 512;
 constexpr int kMaxTopK = 32;
-constexpr int kMaxTilesPerGroup = 8;   // rows <= kHeadGrid x 16 x 8 = 262,144
+constexpr int kMaxTilesPerGroup = kListTiles;   // rows <= kHeadGrid x 16 x 8 = 262,144
 constexpr int kCandWg = 64;                     // candidate workgroups the fast path holds
 constexpr int kCandMax = kCandWg * kMaxTilesPerGroup * 16;
 
-// The largest of one 64-bit key per lane, in every lane: quad swaps, then the mirrors inside
-// half-rows and rows (each lane then holds the maximum of its 8, then 16), then the lane-group
-// swaps; all without the LDS.
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
-  return (unsigned long long)dpp<CTRL>((uint32_t)v) | ((unsigned long long)dpp<CTRL>((uint32_t)(v >> 32)) << 32);
+// Inclusive prefix sum over the wave's 64 lanes by DPP: shifts by 1, 2, 4 and 8 lanes inside each
+// row of 16 (lanes without a source add 0), then the row totals (lane 15 into the next row, lane
+// 31 into the upper two).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
-__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v, int lane) {
-  unsigned long long o = dpp64<0xB1>(v);
-  v = o > v ? o : v;
-  o = dpp64<0x4E>(v);
-  v = o > v ? o : v;
-  o = dpp64<0x141>(v);
-  v = o > v ? o : v;
-  o = dpp64<0x140>(v);
-  v = o > v ? o : v;
-  o = xor_lane64<16>(v, lane);
-  v = o > v ? o : v;
-  o = xor_lane64<32>(v, lane);
-  return o > v ? o : v;
+__device__ __forceinline__ float wave_inclusive_sum(float c) {
+  c += dpp_or_zero<0x111>(c);
+  c += dpp_or_zero<0x112>(c);
+  c += dpp_or_zero<0x114>(c);
+  c += dpp_or_zero<0x118>(c);
+  c += dpp_or_zero<0x142, 0xA>(c);
+  return c + dpp_or_zero<0x143, 0xC>(c);
 }
 
 // The k-th largest (1 <= k <= n) of the n 64-bit keys a[0 .. n) in LDS, by radix select on 8-bit
@@ -266,90 +272,112 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     const float* __restrict__ logits, long long rows, const unsigned long long* __restrict__ keys, int G,
     float temperature, int top_k, float top_p, const float* __restrict__ u, const int* __restrict__ draft,
     int* __restrict__ token_out, int* __restrict__ topk_out, int* __restrict__ emitted_out, int* __restrict__ n_out,
-    int* __restrict__ tokens, unsigned* __restrict__ counter) {
+    unsigned* __restrict__ counter) {
   constexpr int kWavesS = kSampleThreads / kWave;
-  constexpr int kPer = kHeadGrid / kSampleThreads;   // keys per thread
-  static_assert(kPer == 4, "four keys per lane: a wave's maxima fit its four rounds");
-  __shared__ unsigned long long s_a[kHeadGrid];
+  constexpr int kPer = kHeadGrid / kSampleThreads;   // workgroup lists per thread
+  static_assert(kPer == 4, "four lists per lane: a wave's maxima fit its four rounds");
+  __shared__ unsigned long long s_l[kHeadGrid][kListKeys];   // the lists (maxima first)
+  __shared__ unsigned long long s_a[kHeadGrid];               // the maxima (for the exact fallback)
   __shared__ unsigned long long s_c[kCandMax];
   __shared__ unsigned long long s_top[kMaxTopK];
-  __shared__ unsigned long long s_w[kWavesS][kPer];
+  __shared__ uint32_t s_w[kWavesS][kPer];
   __shared__ unsigned s_hist[2][256];
   __shared__ unsigned long long s_sel, s_t;
-  __shared__ int s_need, s_nwg, s_nc, s_ntop;
-  __shared__ int s_wg[kCandWg];
-  __shared__ bool s_last;
+  __shared__ int s_need, s_nwg, s_nc, s_ntop, s_nfull;
+  __shared__ int s_wg[kCandWg];    // candidate workgroups
+  __shared__ int s_fwg[kCandWg];   // those whose lists are full
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int my_draft = m < M - 1 ? draft[m] : -1;
   const long long ntiles = (rows + 15) >> 4;
   const int tpg = (int)((ntiles + G - 1) / G);   // tiles per head workgroup (host: <= 8)
   const int k = (int)(top_k < rows ? top_k : rows);
   const float* lg = logits + (size_t)m * rows;
-  // 1. t = a lower bound of the k-th largest of the G workgroup keys (keys are distinct and
-  // nonzero; 0 pads past G): each wave takes its j = ceil(k / 8) largest keys (j rounds of a wave
-  // maximum), and t is the k-th largest of those 8j. They are 8j >= k keys, so at least k keys
-  // reach t; and t is at most the k-th largest of all G. Every key of the token's top k is then
-  // >= t and lies in a workgroup whose maximum reaches t; there are k of those when the waves
-  // split the top k evenly, a few more otherwise. More than kCandWg: t becomes the exact k-th
-  // largest (radix select), and exactly k workgroups reach it.
+  // the lists of workgroups tid + q * 512 (zeros past G): four descending keys each
   const int jw = (k + kWavesS - 1) / kWavesS;   // <= 4
-  unsigned long long kv[kPer];
+  unsigned long long kl[kPer][kListKeys];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int i = tid + q * kSampleThreads;
-    kv[q] = keys[(size_t)m * G + min(i, G - 1)];
-    if (i >= G) kv[q] = 0ull;
-  }
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(keys + ((size_t)m * G + min(i, G - 1)) * kListKeys);
+    const u32x4_t lo = ld16(src), hi = ld16(src + 1);
+    const bool in = i < G;
+    kl[q][0] = in ? (unsigned long long)lo[1] << 32 | lo[0] : 0ull;
+    kl[q][1] = in ? (unsigned long long)lo[3] << 32 | lo[2] : 0ull;
+    kl[q][2] = in ? (unsigned long long)hi[1] << 32 | hi[0] : 0ull;
+    kl[q][3] = in ? (unsigned long long)hi[3] << 32 | hi[2] : 0ull;
+    s_a[i] = kl[q][0];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) s_a[tid + q * kSampleThreads] = kv[q];
+    for (int j = 0; j < kListKeys; ++j) s_l[i][j] = kl[q][j];
+  }
   if (tid == 0) {
     s_nwg = 0;
     s_nc = 0;
     s_ntop = 0;
+    s_nfull = 0;
   }
+  // 1. each wave's jw largest distinct upper words of its maxima (a round clears every copy)
+  uint32_t kh[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) kh[q] = (uint32_t)(kl[q][0] >> 32);
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     if (r < jw) {
-      unsigned long long mx = kv[0];
+      uint32_t mx = max(max(kh[0], kh[1]), max(kh[2], kh[3]));
+      mx = wave_max_u32(mx, lane);
 #pragma unroll
-      for (int q = 1; q < kPer; ++q) mx = kv[q] > mx ? kv[q] : mx;
-      mx = wave_max64(mx, lane);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q)
-        if (kv[q] == mx) kv[q] = 0ull;   // keys are distinct: one lane, one register (or all zeros)
+      for (int q = 0; q < kPer; ++q) kh[q] = kh[q] == mx ? 0u : kh[q];
       if (lane == 0) s_w[wave][r] = mx;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    // the waves' maxima sit in lanes 4w + r < 32
-    static_assert(kWavesS * 4 <= 32, "one lane group of 32 holds the waves' maxima");
+    // the waves' values sit in lanes 4w + r < 32
+    static_assert(kWavesS * 4 <= 32, "one lane group of 32 holds the waves' values");
     const int w = lane >> 2, r = lane & 3;
-    const unsigned long long key = wave_sort_desc<32>(w < kWavesS && r < jw ? s_w[w][r] : 0ull, lane);
-    const unsigned long long kth = __shfl(key, k - 1, kWave);
-    if (lane == 0) s_t = G > k ? kth : 0ull;
+    const uint32_t v = wave_sort_desc<32>(w < kWavesS && r < jw ? s_w[w][r] : 0u, lane);
+    const uint32_t kth = (uint32_t)__builtin_amdgcn_readlane((int)v, k - 1);
+    if (lane == 0) s_t = G > k ? (unsigned long long)kth << 32 : 0ull;
   }
   __syncthreads();
   unsigned long long t = s_t;
-  for (int b = tid; b < G; b += kSampleThreads)
-    if (s_a[b] >= t) {
-      const int at = atomicAdd(&s_nwg, 1);
-      if (at < kCandWg) s_wg[at] = b;
+  // 2. the candidate workgroups (maximum >= t) and those among them whose lists are full
+  auto discover = [&]() {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int b = tid + q * kSampleThreads;
+      if (b < G && kl[q][0] >= t) {
+        const int at = atomicAdd(&s_nwg, 1);
+        if (at < kCandWg) {
+          s_wg[at] = b;
+          if (kl[q][kListKeys - 1] != 0ull && kl[q][kListKeys - 1] >= t) s_fwg[atomicAdd(&s_nfull, 1)] = b;
+        }
+      }
     }
+  };
+  discover();
   __syncthreads();
   if (s_nwg > kCandWg) {
     // the waves' maxima were too uneven: the exact k-th largest, reached by exactly k workgroups
     t = block_kth_largest(s_a, G, k, s_hist, &s_sel, &s_need);
-    if (tid == 0) s_nwg = 0;
+    if (tid == 0) {
+      s_nwg = 0;
+      s_nfull = 0;
+    }
     __syncthreads();
-    for (int b = tid; b < G; b += kSampleThreads)
-      if (s_a[b] >= t) s_wg[atomicAdd(&s_nwg, 1)] = b;
+    discover();
     __syncthreads();
   }
-  // 2. their rows' keys that reach t (at least k; a few more at most, in practice), then the k
-  // largest of those: one wave sort when they fit in a wave, else a radix select first
-  const int nwg = s_nwg, per = tpg * 16;
-  if ((rows & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) {
-    // four rows per load: slot i = quarter i % 4 of tile i / 4 of the candidates' tiles (16-byte
+  // the listed keys >= t of the candidates whose lists are not full, one per thread
+  const int nwg = s_nwg;
+  if (tid < nwg * kListKeys) {
+    const int b = s_wg[tid / kListKeys];
+    const unsigned long long key = s_l[b][tid % kListKeys], last = s_l[b][kListKeys - 1];
+    if (!(last != 0ull && last >= t) && key != 0ull && key >= t) s_c[atomicAdd(&s_nc, 1)] = key;
+  }
+  // the rows of the full lists' workgroups that reach t
+  const int nfl = s_nfull, per = tpg * 16;
+  if (nfl > 0 && (rows & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) {
+    // four rows per load: slot i = quarter i % 4 of tile i / 4 of those workgroups' tiles (16-byte
     // aligned: the logits are, and every position's start at a multiple of 4 rows; a quarter is
     // whole rows or none, since rows is a multiple of 4)
     constexpr int kPerQ = kCandMax / 4 / kSampleThreads;
@@ -358,7 +386,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 #pragma unroll
     for (int j = 0; j < kPerQ; ++j) {
       const int i = tid + j * kSampleThreads, ti = i >> 2;
-      const long long tile = ti < nwg * tpg ? s_wg[ti / tpg] + (long long)(ti % tpg) * G : ntiles;
+      const long long tile = ti < nfl * tpg ? s_fwg[ti / tpg] + (long long)(ti % tpg) * G : ntiles;
       r0[j] = tile < ntiles && tile * 16 + 4 * (i & 3) < rows ? tile * 16 + 4 * (i & 3) : -1;
       v[j] = r0[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(lg + r0[j]) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -369,14 +397,14 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
         const unsigned long long key = rank_key(sel_key(v[j][e]), (int)(r0[j] + e));
         if (r0[j] >= 0 && key >= t) s_c[atomicAdd(&s_nc, 1)] = key;
       }
-  } else {
+  } else if (nfl > 0) {
     constexpr int kPerC = kCandMax / kSampleThreads;
     long long row[kPerC];
     float v[kPerC];
 #pragma unroll
     for (int j = 0; j < kPerC; ++j) {
       const int i = tid + j * kSampleThreads;
-      const long long tile = i < nwg * per ? s_wg[i / per] + (long long)((i % per) >> 4) * G : ntiles;
+      const long long tile = i < nfl * per ? s_fwg[i / per] + (long long)((i % per) >> 4) * G : ntiles;
       row[j] = tile < ntiles && tile * 16 + (i & 15) < rows ? tile * 16 + (i & 15) : -1;
       v[j] = row[j] >= 0 ? lg[row[j]] : 0.0f;
     }
@@ -397,46 +425,43 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     top = s_top;
   }
   // 3. wave 0: the k keys in order (bitonic sort across the lanes, descending), then the sample
-  if (wave == 0) {
-    const int n = nc > kWave ? k : nc;
-    const unsigned long long key = sort_candidates(lane < n ? top[lane] : 0ull, n, lane);
-    const int row = (int)(0xffffffffu - (uint32_t)key);
-    const float v = key_to_float((uint32_t)(key >> 32));
-    const float v0 = __shfl(v, 0, kWave);
-    // probabilities relative to the largest: exp((v - v0) / temperature), their running sums
-    const float p = lane < k ? expf(__fdiv_rn(v - v0, temperature)) : 0.0f;
-    float c = p;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float w = __shfl_up(c, o, kWave);
-      if (lane >= o) c += w;
+  if (wave != 0) return;
+  const int n = nc > kWave ? k : nc;
+  const unsigned long long key = sort_candidates(lane < n ? top[lane] : 0ull, n, lane);
+  const int row = (int)(0xffffffffu - (uint32_t)key);
+  const float v = key_to_float((uint32_t)(key >> 32));
+  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  // probabilities relative to the largest: exp((v - v0) / temperature), their running sums
+  const float p = lane < k ? expf(__fdiv_rn(v - v0, temperature)) : 0.0f;
+  const float c = wave_inclusive_sum(p);
+  const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), k - 1));
+  // the shortest prefix whose share reaches top_p, then the first token of it whose running sum
+  // exceeds u times the prefix's sum
+  const unsigned long long reach = __ballot(lane < k && c >= top_p * total);
+  const int keep = reach ? __builtin_ctzll(reach) + 1 : k;
+  const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), keep - 1));
+  const unsigned long long over = __ballot(lane < keep && c > u[m] * sk);
+  const int pick = over ? __builtin_ctzll(over) : keep - 1;
+  const int token = __builtin_amdgcn_readlane(row, pick);
+  if (topk_out && lane < top_k) topk_out[(size_t)m * top_k + lane] = lane < k ? row : -1;
+  // 4. the window: emitted[i] is token i for every i up to the first rejected draft a (accepted
+  // drafts equal their tokens) and -1 after it. Each position stores its token there and, once
+  // that store is acknowledged, arrives with its acceptance bit: counter += 256 + (bit << m). The
+  // last to arrive has every bit, stores -1 past a (after every other position's token store) and
+  // n = a + 1, and clears the counter for the next call.
+  if (lane == 0) {
+    token_out[m] = token;
+    st_coherent(emitted_out + m, token);
+    wait_mem();
+    const unsigned add = 256u + ((m < M - 1 && my_draft == token ? 1u : 0u) << m);
+    const unsigned now = __hip_atomic_fetch_add(counter, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    if ((now >> 8) == (unsigned)M) {
+      st_coherent(counter, 0u);
+      int a = 0;
+      while (a < M - 1 && ((now >> a) & 1u)) ++a;
+      for (int i = a + 1; i < M; ++i) st_coherent(emitted_out + i, -1);
+      *n_out = a + 1;
     }
-    const float total = __shfl(c, k - 1, kWave);
-    // the shortest prefix whose share reaches top_p, then the first token of it whose running sum
-    // exceeds u times the prefix's sum
-    const unsigned long long reach = __ballot(lane < k && c >= top_p * total);
-    const int keep = reach ? __builtin_ctzll(reach) + 1 : k;
-    const float sk = __shfl(c, keep - 1, kWave);
-    const unsigned long long over = __ballot(lane < keep && c > u[m] * sk);
-    const int pick = over ? __builtin_ctzll(over) : keep - 1;
-    const int token = __shfl(row, pick, kWave);
-    if (topk_out && lane < top_k) topk_out[(size_t)m * top_k + lane] = lane < k ? row : -1;
-    if (lane == 0) {
-      token_out[m] = token;
-      st_coherent(tokens + m, token);
-    }
-  }
-  // 4. the last position's workgroup forms the accepted prefix
-  if (!arrive_last(counter, M, &s_last)) return;
-  if (tid == 0) {
-    int target[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) target[i] = ld_coherent(tokens + i);
-    int a = 0;
-    while (a < M - 1 && draft[a] == target[a]) ++a;
-#pragma unroll
-    for (int i = 0; i < M; ++i) emitted_out[i] = i < a ? draft[i] : (i == a ? target[a] : -1);
-    *n_out = a + 1;
   }
 }
 
@@ -550,9 +575,10 @@ extern "C" int lmhead_fp8_tile_major(const qws_lmhead* src, unsigned char* codes
 }
 
 namespace {
-// One launch of head_fp8_kernel: M tokens; with `keys`, each workgroup's largest key per token too.
+// One launch of head_fp8_kernel: M tokens; with `keys`, each workgroup's largest key per token too
+// (its four largest with `list4`).
 int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* logits_out, unsigned long long* keys,
-                    hipStream_t s) {
+                    hipStream_t s, bool list4 = false) {
   const uint8_t* q = static_cast<const uint8_t*>(head->w);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   const int cols = (int)head->cols;
@@ -568,7 +594,9 @@ int launch_head_fp8(const qws_lmhead* head, const void* x_bf16, int M, float* lo
     case 3: QWS_HEAD(3, VV); break;     \
     default: QWS_HEAD(4, VV); break;    \
   }
-  if (keys) {
+  if (keys && list4) {
+    QWS_HEAD_M(kKeys4)
+  } else if (keys) {
     QWS_HEAD_M(kKeys)
   } else {
     QWS_HEAD_M(kGemv)
@@ -594,9 +622,9 @@ extern "C" int lmhead_gemv_fp8(const qws_lmhead* head, const void* x_bf16, int M
   return launch_head_fp8(head, x_bf16, M, logits_out, nullptr, static_cast<hipStream_t>(stream));
 }
 
-// Verification workspace: per-workgroup keys [M][kHeadGrid] u64, then 256 B for the sampling
-// kernel (its arrival counter, then the M sampled tokens on the next 128-byte line).
-size_t verify_keys_bytes(int M) { return qws_host::align256((size_t)kHeadGrid * M * 8); }
+// Verification workspace: per-workgroup keys, [M][kHeadGrid] u64 for the greedy epilogue and
+// [M][kHeadGrid][4] for the sampled one, then 256 B for the sampling kernel's arrival counter.
+size_t verify_keys_bytes(int M) { return qws_host::align256((size_t)kHeadGrid * M * kListKeys * 8); }
 
 extern "C" size_t lmhead_verify_workspace_bytes(int M) {
   if (M < 1 || M > 4) return 0;
@@ -714,13 +742,12 @@ extern "C" int lmhead_verify_sample_fp8(const qws_lmhead* head, const void* x_bf
   unsigned long long* keys = static_cast<unsigned long long*>(workspace);
   char* tail = static_cast<char*>(workspace) + verify_keys_bytes(M);
   unsigned* counter = reinterpret_cast<unsigned*>(tail);
-  int* tokens = reinterpret_cast<int*>(tail + 128);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_head_fp8(head, x_bf16, M, logits_out, keys, s);
+  st = launch_head_fp8(head, x_bf16, M, logits_out, keys, s, true);
   if (st != QWS_OK) return st;
 #define QWS_SAMPLE(MM)                                                                                             \
   hipLaunchKernelGGL(sample_kernel<MM>, dim3(MM), dim3(kSampleThreads), 0, s, logits_out, head->rows, keys, G,      \
-                     temperature, top_k, top_p, u, draft, token_out, topk_out, emitted_out, n_out, tokens, counter)
+                     temperature, top_k, top_p, u, draft, token_out, topk_out, emitted_out, n_out, counter)
   switch (M) {
     case 1: QWS_SAMPLE(1); break;
     case 2: QWS_SAMPLE(2); break;

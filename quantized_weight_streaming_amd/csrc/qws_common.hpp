@@ -195,27 +195,45 @@ __device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v, i
   return (unsigned long long)xor_lane<S>((uint32_t)v, lane) | ((unsigned long long)xor_lane<S>((uint32_t)(v >> 32), lane) << 32);
 }
 
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane_any(uint32_t v, int lane) { return xor_lane<S>(v, lane); }
+template <int S>
+__device__ __forceinline__ unsigned long long xor_lane_any(unsigned long long v, int lane) {
+  return xor_lane64<S>(v, lane);
+}
+
+// The largest of one 32-bit value per lane, in every lane: quad swaps, then the mirrors inside
+// half-rows and rows (each lane then holds the maximum of its 8, then 16), then the lane-group swaps.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v, int lane) {
+  v = max(v, dpp_mov<0xB1>(v));
+  v = max(v, dpp_mov<0x4E>(v));
+  v = max(v, dpp_mov<0x141>(v));
+  v = max(v, dpp_mov<0x140>(v));
+  v = max(v, xor_lane<16>(v, lane));
+  return max(v, xor_lane<32>(v, lane));
+}
+
 // One compare-exchange stage of a bitonic network at a constant stride S: lanes whose keep_max
 // holds take the larger of their key and lane (lane ^ S)'s, the others the smaller (one compare:
-// the partner's key is taken when "it is larger" agrees with keep_max).
-template <int S>
-__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long key, bool keep_max, int lane) {
-  const unsigned long long o = xor_lane64<S>(key, lane);
+// the partner's key is taken when "it is larger" agrees with keep_max). Keys of 32 or 64 bits.
+template <int S, typename T>
+__device__ __forceinline__ T bitonic_step(T key, bool keep_max, int lane) {
+  const T o = xor_lane_any<S>(key, lane);
   return (o > key) == keep_max ? o : key;
 }
-template <int S>
-__device__ __forceinline__ unsigned long long bitonic_merge_desc(unsigned long long key, int size, int lane) {
+template <int S, typename T>
+__device__ __forceinline__ T bitonic_merge_desc(T key, int size, int lane) {
   // the strides S, S/2, .. 1 of merging blocks of `size` (descending where lane & size is 0)
   key = bitonic_step<S>(key, ((lane & S) == 0) == ((lane & size) == 0), lane);
   if constexpr (S > 1) key = bitonic_merge_desc<S / 2>(key, size, lane);
   return key;
 }
 
-// Bitonic sort of one 64-bit key per lane inside aligned groups of N lanes (N = 16, 32 or 64): lanes
+// Bitonic sort of one key per lane inside aligned groups of N lanes (N = 16, 32 or 64): lanes
 // 0 .. N-1 end descending (lane 0 the largest); with N < 64 the other groups end sorted too, in
 // either direction.
-template <int N = 64>
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key, int lane) {
+template <int N = 64, typename T = unsigned long long>
+__device__ __forceinline__ T wave_sort_desc(T key, int lane) {
   static_assert(N == 16 || N == 32 || N == 64, "groups of 16, 32 or 64 lanes");
   key = bitonic_merge_desc<1>(key, 2, lane);
   key = bitonic_merge_desc<2>(key, 4, lane);

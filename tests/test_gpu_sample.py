@@ -115,6 +115,34 @@ def test_sample_ties_rank_the_lower_row_first():
     assert int(res["token"][0]) == 64
 
 
+@pytest.mark.parametrize("rows", [40000, 40001])
+def test_sample_top_rows_clustered_in_one_workgroup(rows):
+    """12 of the top 29 rows in one head workgroup (tiles 5 and 5 + 2048 of a 2,048-workgroup grid):
+    its list of four keys is full, so its rows are read back from the logits (40,001 rows: the
+    one-row-per-load path). Distinct top logits: each chosen row is +-v aligned with token 0's
+    signs, v a different bf16 value per row (exact in E4M3 with its row scale)."""
+    say(f"sample: clustered top rows, {rows} rows")
+    cols = 256
+    w = synth.bf16_normal(19, 0, synth.HEAD, 0, (rows, cols), 0.02).copy()
+    x = synth.token_vectors(19, 0, 2, cols)
+    rng = np.random.default_rng(19)
+    cluster = sorted(rng.choice(np.r_[80:96, 16 * 2053:16 * 2054], 12, replace=False).tolist())
+    others = rng.choice(np.setdiff1d(np.arange(rows), cluster), 20, replace=False).tolist()
+    chosen = cluster + others
+    order = rng.permutation(len(chosen))   # rank of each chosen row: a larger v for a lower rank
+    for r, o in zip(chosen, order):
+        v = 0x4100 - int(o)                 # bf16 codes 0x40E1 .. 0x4100 (7.0 .. 8.0)
+        w[r] = np.where(x[0] & 0x8000, v | 0x8000, v)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    kw = dict(temperature=0.6, top_k=29, top_p=1.0)
+    u = [0.37, 0.81]
+    res = _run(h8, bf16(x), [0], u, qws.verify_workspace(2, "cuda"), **kw)
+    want = [r for _, r in sorted(zip(order, chosen))][:29]
+    assert res["topk"][0].tolist() == want
+    assert set(cluster) <= set(want)
+    _check(res, [0], u, kw, rows)
+
+
 def test_sample_more_candidates_than_rows():
     say("sample top_k > rows")
     rows, cols = 5, 64
