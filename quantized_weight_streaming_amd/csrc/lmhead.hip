@@ -118,6 +118,10 @@ __global__ __launch_bounds__(kFinishThreads) void greedy_finish_kernel(const uns
   __shared__ unsigned long long s_best[kFinishThreads / kWave][M];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   constexpr int kPer = (kHeadGrid + kFinishThreads - 1) / kFinishThreads;
+  // the drafts, loaded while the keys are (the prefix below would otherwise wait on each in turn)
+  int dr[M > 1 ? M - 1 : 1];
+#pragma unroll
+  for (int m = 0; m < M - 1; ++m) dr[m] = draft[m];
   unsigned long long kk[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) kk[m] = 0ull;
@@ -131,13 +135,21 @@ __global__ __launch_bounds__(kFinishThreads) void greedy_finish_kernel(const uns
       kk[m] = k > kk[m] ? k : kk[m];
     }
   }
+  // each token's wave maximum by DPP and lane-group swaps (no LDS round trips)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long ko = __shfl_xor(kk[m], o, kWave);
-      kk[m] = ko > kk[m] ? ko : kk[m];
-    }
+    unsigned long long o = xor_lane64<1>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
+    o = xor_lane64<2>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
+    o = xor_lane64<4>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
+    o = xor_lane64<8>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
+    o = xor_lane64<16>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
+    o = xor_lane64<32>(kk[m], lane);
+    kk[m] = o > kk[m] ? o : kk[m];
     if (lane == 0) s_best[wave][m] = kk[m];
   }
   __syncthreads();
@@ -151,10 +163,13 @@ __global__ __launch_bounds__(kFinishThreads) void greedy_finish_kernel(const uns
       target[m] = (int)(0xffffffffu - (uint32_t)k);
       target_out[m] = target[m];
     }
+    // accepted drafts equal their targets: emitted is the targets up to the first rejection
     int a = 0;
-    while (a < M - 1 && draft[a] == target[a]) ++a;
 #pragma unroll
-    for (int m = 0; m < M; ++m) emitted_out[m] = m < a ? draft[m] : (m == a ? target[a] : -1);
+    for (int m = 0; m < M - 1; ++m)
+      if (a == m && dr[m] == target[m]) ++a;
+#pragma unroll
+    for (int m = 0; m < M; ++m) emitted_out[m] = m <= a ? target[m] : -1;
     *n_out = a + 1;
   }
 }
