@@ -33,6 +33,17 @@ constexpr int kKbw = kMaxCols / 64 / kHeadWaves;  // k-blocks (64 columns) per w
 constexpr int kXsStride = kMaxCols + 64;          // LDS stride of one token's x (bf16 elements)
 constexpr int kHeadGrid = 2048;   // workgroups (at most one per tile)
 
+// The first tile of workgroup b (then every G-th after it). Tiles 2j and 2j+1 fill the two halves
+// of each 128-byte line of logits (and of row scales); consecutive workgroups run on different
+// XCDs, so with tile b each such line was written half by one XCD's L2 and half by another's. Here
+// the pair goes to workgroups b and b + 8, which share an XCD, when G is a multiple of 16
+// (otherwise tile b): 0.5 us faster at M = 1, 1.2 us at M = 4 on the full head.
+__device__ __forceinline__ long long head_tile0(int b, int G) {
+  if (G % 16) return b;
+  const int x = b % 8, k = b / 8;
+  return 16 * (k >> 1) + 2 * x + (k & 1);
+}
+
 // kMode: kGemv (logits), kKeys (logits optional, and each workgroup's largest (logit, lower row)
 // key per token, for greedy_finish_kernel), kKeys4 (logits, and each workgroup's four largest keys
 // per token in descending order, zero where it has fewer rows, for sample_kernel).
@@ -79,7 +90,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void head_fp8_kernel(
     for (int t = 0; t < kKbw; ++t)
       w[t] = 4 * (kb0 + t) + g < ncs ? ld16_weights(p + (kb0 + t) * 1024) : u32x4_t{0u, 0u, 0u, 0u};
   };
-  long long tile = blockIdx.x;
+  long long tile = head_tile0(blockIdx.x, gridDim.x);
   u32x4_t cur[kKbw], nxt[kKbw];
   load(tile, cur);
   // epilogue thread: tile row er of token em

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 #pragma unroll
     for (int j = 0; j < kPerQ; ++j) {
       const int i = tid + j * kSampleThreads, ti = i >> 2;
-      const long long tile = ti < nfl * tpg ? s_fwg[ti / tpg] + (long long)(ti % tpg) * G : ntiles;
+      const long long tile = ti < nfl * tpg ? head_tile0(s_fwg[ti / tpg], G) + (long long)(ti % tpg) * G : ntiles;
       r0[j] = tile < ntiles && tile * 16 + 4 * (i & 3) < rows ? tile * 16 + 4 * (i & 3) : -1;
       v[j] = r0[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(lg + r0[j]) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
 #pragma unroll
     for (int j = 0; j < kPerC; ++j) {
       const int i = tid + j * kSampleThreads;
-      const long long tile = i < nfl * per ? s_fwg[i / per] + (long long)((i % per) >> 4) * G : ntiles;
+      const long long tile = i < nfl * per ? head_tile0(s_fwg[i / per], G) + (long long)((i % per) >> 4) * G : ntiles;
       row[j] = tile < ntiles && tile * 16 + (i & 15) < rows ? tile * 16 + (i & 15) : -1;
       v[j] = row[j] >= 0 ? lg[row[j]] : 0.0f;
     }
@@ -487,7 +487,11 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_kernel(const uint16_t* __res
   const int lane = threadIdx.x % kWave;
   const int nch = cols >> 3;  // chunks of 8 bf16
   const long long nwaves = (long long)gridDim.x * kWavesPerBlock;
-  long long row = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  // the 8 four-row groups of each 128-byte line of logits go to workgroups of one XCD (b, b + 8,
+  // .. b + 56: consecutive workgroups run on different XCDs) when the grid is a multiple of 64
+  const int b = blockIdx.x, xcd = b % 8, k = b / 8;
+  const long long slot = gridDim.x % 64 ? b : 64 * (k / 8) + 8 * xcd + k % 8;
+  long long row = slot * kWavesPerBlock + threadIdx.x / kWave;
   if (row >= rows) return;
 
   u32x4_t xr[M][kCpl];
