@@ -300,11 +300,10 @@ __device__ __forceinline__ void router_row_to_lds(const uint16_t* row, uint16_t*
 // Between layers that are not chained: every workgroup publishes a tagged word once all of its
 // stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
 // round trip to a counter before the wait starts. Meanwhile waves 0 .. kCopyWaves-1 copy the next
-// layer's x and the router waves its router rows (next_row: this wave's row, or NULL) into LDS,
-// wave kWaves-2 stores the word and the last wave polls: neither issues any of the copies, which a
-// wait for its loads would also wait for.
+// layer's x into LDS, wave kWaves-2 stores the word and the last wave polls: neither issues any of
+// the copies, which a wait for its loads would also wait for.
 __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, const uint16_t* next_x, uint16_t* xs,
-                               int n_x, const uint16_t* next_row, uint16_t* row_dst, int H) {
+                               int n_x) {
   wait_mem();
   __syncthreads();
   stamp(w, l, 14);
@@ -320,7 +319,6 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
         __builtin_amdgcn_global_load_lds((const QWS_GLOBAL void*)(next_x + (size_t)(c + lane) * 8),
                                          (__attribute__((address_space(3))) void*)(xs + (size_t)c * 8), 16, 0, 0);
   }
-  if (next_row) router_row_to_lds(next_row, row_dst, H, tid % kWave);
   if (tid >= kThreads - kWave) {
     constexpr int kPer = kMaxGrid / kWave;
     const int lane = tid - (kThreads - kWave);
@@ -1369,15 +1367,16 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
         }
       }
     }
-    // the next layer's router rows -> LDS: chained layers (no barrier) here, after this layer's task
-    // loads (an LDS DMA pending among them would make every wait for a task load wait for it);
-    // otherwise during the barrier, where the router waves are idle
+    // the next layer's router rows (weights, which no layer's result changes) -> LDS, here, after
+    // this layer's task loads (an LDS DMA pending among them would make every wait for a task load
+    // wait for it). During the barrier instead, the last workgroup to arrive passed it at once and
+    // then waited for its rows' DMA, which held up every workgroup's logits (0.1 us per layer).
     const uint16_t* next_row = nullptr;
     if (has_next && is_router)
       next_row = reinterpret_cast<const uint16_t*>(
                      uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, w_router_bf16) / 8])) +
                  (size_t)r_row * H;
-    if (next_row && CH) router_row_to_lds(next_row, my_wr_s, H, lane);
+    if (next_row) router_row_to_lds(next_row, my_wr_s, H, lane);
 
     stamp(w, l, 6);
 
@@ -1474,7 +1473,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       const uint16_t* next_x = nullptr;
       if (sh.x_fresh)
         next_x = reinterpret_cast<const uint16_t*>(uniform_u64(s_desc[(l + 1) & 1][offsetof(qws_moe_layer, x_bf16) / 8]));
-      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H, next_row, my_wr_s, H);
+      tagged_barrier(w, tag_y, tid, l, next_x, xs, M * H);
       stamp(w, l, 9);
     } else {
       __syncthreads();      // LDS (union, s_y, red) is rewritten by the next layer

@@ -14,8 +14,10 @@ from .helpers import assert_close, bf16, check_argmax, f32, fp8_tile_major, say,
 pytestmark = pytest.mark.gpu
 
 
+# (1021, 96) and (4093, 256): grids of 64 / 256 FP8 workgroups and 256 / 1024 bf16 ones, multiples
+# of 16 and 64, so that both GEMVs pair the rows of a line of logits on one XCD (with ragged tails)
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-@pytest.mark.parametrize("rows,cols", [(1, 32), (999, 96), (2049, 2560), (5000, 544)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (999, 96), (1021, 96), (2049, 2560), (4093, 256), (5000, 544)])
 def test_gemv_small(M, rows, cols):
     say("lmhead small", M, rows, cols)
     w = synth.bf16_normal(1, 0, synth.HEAD, rows + cols, (rows, cols), 0.02)

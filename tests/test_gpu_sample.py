@@ -68,7 +68,7 @@ def _check(res, draft, u, kw, rows):
 
 
 @pytest.mark.parametrize("M", [1, 2, 4])
-@pytest.mark.parametrize("rows,cols", [(1, 32), (40, 96), (999, 96), (5000, 2560)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (40, 96), (999, 96), (4093, 256), (5000, 2560)])
 @pytest.mark.parametrize("kw", [PAGES, dict(temperature=1.0, top_k=32, top_p=1.0),
                                 dict(temperature=2.0, top_k=1, top_p=0.5), dict(temperature=0.6, top_k=5, top_p=0.3)])
 def test_sample_small(M, rows, cols, kw):

@@ -48,7 +48,7 @@ def _drafts(target, rows):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-@pytest.mark.parametrize("rows,cols", [(1, 32), (999, 96), (5000, 2560)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (999, 96), (4093, 256), (5000, 2560)])
 def test_verify_small(M, rows, cols):
     say("verify small", M, rows, cols)
     w = synth.bf16_normal(4, 0, synth.HEAD, rows + cols, (rows, cols), 0.02)
