@@ -143,6 +143,34 @@ def test_sample_top_rows_clustered_in_one_workgroup(rows):
     _check(res, [0], u, kw, rows)
 
 
+def test_sample_at_the_row_limit_reads_back_eight_tiles():
+    """262,144 rows (2,048 head workgroups x 8 tiles, the most the sampled path takes): 20 of the
+    top 29 rows in the eight tiles of one workgroup (its tiles t0 + 2048 i, t0 its first tile:
+    tile 5 for workgroup 10, whose tiles pair with workgroup 2's on one XCD), so its 128 rows are
+    read back."""
+    say("sample: row limit, 8 tiles read back")
+    rows, cols = 2048 * 16 * 8, 64
+    w = synth.bf16_normal(20, 0, synth.HEAD, 0, (rows, cols), 0.02).copy()
+    x = synth.token_vectors(20, 0, 1, cols)
+    rng = np.random.default_rng(20)
+    tiles = [5 + 2048 * i for i in range(8)]
+    cluster = sorted(rng.choice(np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles]), 20,
+                                replace=False).tolist())
+    others = rng.choice(np.setdiff1d(np.arange(rows), cluster), 12, replace=False).tolist()
+    chosen = cluster + others
+    order = rng.permutation(len(chosen))
+    for r, o in zip(chosen, order):
+        v = 0x4100 - int(o)
+        w[r] = np.where(x[0] & 0x8000, v | 0x8000, v)
+    h8 = qws.lmhead_quantize_fp8(bf16(w))
+    kw = dict(temperature=0.6, top_k=29, top_p=1.0)
+    res = _run(h8, bf16(x), [], [0.42], qws.verify_workspace(1, "cuda"), **kw)
+    want = [r for _, r in sorted(zip(order, chosen))][:29]
+    assert res["topk"][0].tolist() == want
+    assert len(set(cluster) & set(want)) >= 17
+    _check(res, [], [0.42], kw, rows)
+
+
 def test_sample_more_candidates_than_rows():
     say("sample top_k > rows")
     rows, cols = 5, 64
