@@ -302,10 +302,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   __shared__ int s_wg[kCandWg];    // candidate workgroups
   __shared__ int s_fwg[kCandWg];   // those whose lists are full
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  // the draft and the uniform, loaded while the keys are (the compiler had put u's load at its
-  // use, a memory round trip at the end of the chain)
   const int my_draft = m < M - 1 ? draft[m] : -1;
-  float um = u[m];
   const long long ntiles = (rows + 15) >> 4;
   const int tpg = (int)((ntiles + G - 1) / G);   // tiles per head workgroup (host: <= 8)
   const int k = (int)(top_k < rows ? top_k : rows);
@@ -333,7 +330,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     s_ntop = 0;
     s_nfull = 0;
   }
-  asm volatile("" : "+s"(um));   // u has arrived before the keys are ranked
   // 1. each wave's jw largest distinct upper words of its maxima (a round clears every copy)
   uint32_t kh[kPer];
 #pragma unroll
@@ -459,7 +455,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const unsigned long long reach = __ballot(lane < k && c >= top_p * total);
   const int keep = reach ? __builtin_ctzll(reach) + 1 : k;
   const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), keep - 1));
-  const unsigned long long over = __ballot(lane < keep && c > um * sk);
+  const unsigned long long over = __ballot(lane < keep && c > u[m] * sk);
   const int pick = over ? __builtin_ctzll(over) : keep - 1;
   const int token = __builtin_amdgcn_readlane(row, pick);
   if (topk_out && lane < top_k) topk_out[(size_t)m * top_k + lane] = lane < k ? row : -1;
