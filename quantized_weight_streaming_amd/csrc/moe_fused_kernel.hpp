@@ -1050,10 +1050,14 @@ __device__ __forceinline__ void select_multi(const Shape& sh, const Work& w, con
 }
 
 // ------------------------------------------------------------------------------ the kernel
-// Blocks per task group: the smallest divisor of J for which the nsr routed slots' groups fit in
-// G workgroups (1 when every task has a workgroup of its own).
-__device__ __forceinline__ int group_size(int nsr, int J, int G) {
-  for (int k = 1; k < J; ++k)
+// Blocks per task group: the smallest divisor of J, at least kmin, for which the nsr routed slots'
+// groups fit in G workgroups. A group stores one partial vector per token of its slot after summing
+// its blocks in registers, so with several tokens per slot single-block groups multiply the
+// partial-sum traffic: the same-expert window at M = 4 (9 slots, 4 tokens each) wrote 17.3 MB of
+// partial sums per layer and took 25.3 us per layer; with kmin = 2 for M > 1, 22.5 us (the other
+// windows choose 2 or more anyway; one token keeps single blocks, whose burst is the shorter).
+__device__ __forceinline__ int group_size(int nsr, int J, int G, int kmin) {
+  for (int k = kmin; k < J; ++k)
     if (J % k == 0 && nsr * (J / k) <= G) return k;
   return J;
 }
@@ -1343,7 +1347,7 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       // registers and are stored once. Each task's loads are issued during the previous one's
       // compute.
       const int s0 = kEarlyShared<M> ? ns : 0;   // first slot of the pool
-      const int nsr = un.n - s0, kg = group_size(nsr, J, G), jg = J / kg, n_gr = nsr * jg;
+      const int nsr = un.n - s0, kg = group_size(nsr, J, G, M > 1 ? 2 : 1), jg = J / kg, n_gr = nsr * jg;
       sh.jg = jg;
       int gi = b;
       if (gi < n_gr) {
