@@ -1342,8 +1342,9 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
 
     // ------------------------------------------------------------------ 4: routed tasks
     {
-      // groups of kg consecutive blocks of one slot (kg = the smallest divisor of J that leaves at
-      // most G groups): workgroup b takes groups b, b + G, ...; a group's partials add up in
+      // groups of kg consecutive blocks of one slot (kg = the smallest divisor of J, at least 2 with
+      // several tokens, that leaves at most G groups): workgroup b takes groups b, b + G, ...; a
+      // group's partials add up in
       // registers and are stored once. Each task's loads are issued during the previous one's
       // compute.
       const int s0 = kEarlyShared<M> ? ns : 0;   // first slot of the pool
