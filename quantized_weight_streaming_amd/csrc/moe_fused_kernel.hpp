@@ -66,7 +66,11 @@ constexpr int kRtCpl = 5;       // 16-byte chunks per lane of a router row: H <=
 constexpr int kDnRpl = 3;       // down rows per thread in a task: H <= 1024 * 3
 constexpr int kMaxRows = 16;    // output rows owned by one workgroup
 constexpr int kMaxGrid = 512;
-constexpr int kPollBatch = 8;   // tagged words per thread in flight while reading partials
+// Tagged partial-sum words per thread in flight while an owner reads its lines: one token's 216
+// lines fit one batch of 4 (64 line groups x 4; 8 left half the slots empty and cost 0.12 us per
+// layer, 2 or 3 take two batches, 0.2 us slower); several tokens' ~300 lines, one batch of 8.
+template <int M>
+constexpr int kPollBatch = M == 1 ? 4 : 8;
 constexpr int kLine = 16;       // 64-bit words per 128-byte line: hand-off words of one writer share no line
                                 // (the one-token logits aside)
 static_assert(kMaxRows <= kLine, "an owner's rows of one (pair, block) share one line");
@@ -1402,17 +1406,17 @@ __global__ __launch_bounds__(kThreads) void moe_layers_kernel(Layer first, const
       float acc[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-      for (int k0 = 0; k0 * kStep < n_lines; k0 += kPollBatch) {
-        int idx[kPollBatch];
-        unsigned long long v[kPollBatch];
+      for (int k0 = 0; k0 * kStep < n_lines; k0 += kPollBatch<M>) {
+        int idx[kPollBatch<M>];
+        unsigned long long v[kPollBatch<M>];
 #pragma unroll
-        for (int q = 0; q < kPollBatch; ++q) {
+        for (int q = 0; q < kPollBatch<M>; ++q) {
           const int Lq = L0 + (k0 + q) * kStep;
           idx[q] = Lq < n_lines && my_row ? Lq * H + r : -1;
         }
-        poll_tagged<kPollBatch>(w, src, idx, tag_pt, v);
+        poll_tagged<kPollBatch<M>>(w, src, idx, tag_pt, v);
 #pragma unroll
-        for (int q = 0; q < kPollBatch; ++q) {
+        for (int q = 0; q < kPollBatch<M>; ++q) {
           if (idx[q] >= 0) {
             const float x = __uint_as_float((uint32_t)v[q]);
             if constexpr (M == 1) {
