@@ -301,6 +301,18 @@ __device__ __forceinline__ void router_row_to_lds(const uint16_t* row, uint16_t*
                                        (__attribute__((address_space(3))) void*)(dst + c0 * 8), 16, 0, 0);
 }
 
+// The barrier's wait: every workgroup's tagged word, kPer words per lane of one wave. The wait
+// re-checks every slot each round, so kPer matches the grid (4 for G <= 256: 16 slots, sized for the
+// largest grid, made each layer 0.09 us slower at M = 1 and 0.23 us at M = 4).
+template <int kPer>
+__device__ __forceinline__ void poll_done(const Work& w, const unsigned long long* src, int lane, uint32_t tag) {
+  int idx[kPer];
+  unsigned long long v[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) idx[q] = lane + q * kWave < (int)gridDim.x ? (lane + q * kWave) * kLine : -1;
+  poll_tagged<kPer>(w, src, idx, tag, v);
+}
+
 // Between layers that are not chained: every workgroup publishes a tagged word once all of its
 // stores have been acknowledged, then waits for every workgroup's word. No atomics, so no
 // round trip to a counter before the wait starts. Meanwhile waves 0 .. kCopyWaves-1 copy the next
@@ -324,13 +336,10 @@ __device__ void tagged_barrier(const Work& w, uint32_t tag, int tid, int l, cons
                                          (__attribute__((address_space(3))) void*)(xs + (size_t)c * 8), 16, 0, 0);
   }
   if (tid >= kThreads - kWave) {
-    constexpr int kPer = kMaxGrid / kWave;
     const int lane = tid - (kThreads - kWave);
-    int idx[kPer];
-    unsigned long long v[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) idx[q] = lane + q * kWave < (int)gridDim.x ? (lane + q * kWave) * kLine : -1;
-    poll_tagged<kPer>(w, w.done + (size_t)(blockIdx.x % kReplicas) * kMaxGrid * kLine, idx, tag, v);
+    const unsigned long long* src = w.done + (size_t)(blockIdx.x % kReplicas) * kMaxGrid * kLine;
+    if (gridDim.x <= 4 * kWave) poll_done<4>(w, src, lane, tag);
+    else poll_done<kMaxGrid / kWave>(w, src, lane, tag);
   }
   __syncthreads();
 }
